@@ -1,0 +1,296 @@
+"""CPU oracle for the jagged HSTU encoder stack (test infrastructure only).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import this
+module. It shares no code with the HIP path and must never be called by it.
+
+What it computes is the plain definition of one DLRMv3/HSTU ranking-encoder stack,
+as described on the page "DLRMv3: MLPerf Inference generative recommendation
+benchmark" (section "Model selection"): per layer a D -> 4D projection, the
+attention core Mask(SiLU(Q K^T)) V with an absolute position bias added to Q, K
+and V, and a post-attention GEMM of 3*D*D multiply-adds per token; the user
+interaction history (UIH) is encoded once and shared by every candidate, and a
+user's UIH key/value state is reused across consecutive timestamps. Candidates
+are target-aware ("Target-Aware Multi-Head Attention" on the page about Meta's
+multi-stage sequence model): each candidate attends to the whole history and to
+itself, never to another candidate, and the history's representation never
+depends on the candidates. Jagged batches are concatenated values plus per-user
+lengths (the KeyedJaggedTensor example of the TorchRec DLRM tutorial page,
+section 2.1).
+
+Readings adopted where the pages are silent (each listed in the design notes):
+the 3*D*D GEMM consumes [U | O | U*O]; the residual is X + Z; no normalisation
+and no GEMM biases; SiLU on all four projection slices; one [max_len, 3D]
+position table per layer with column blocks V, Q, K, added after SiLU; every
+candidate sits at position m+n (the next-event slot); the scale 1/max_len is
+applied once to each attention output; the UIH mask is causal with the diagonal
+included.
+
+Arithmetic is float64 throughout. ``mode="f64"`` applies no intermediate
+rounding. ``mode="bf16"`` mirrors a bfloat16 pipeline by rounding (to nearest,
+ties to even) at exactly these points: U, V, Q, K after bias; every attention
+weight SiLU(q.k); every attention output; the gate U*O; and X + Z.
+
+Parity pins for every function here live in tests/test_oracle_pins.py (brute
+force on tiny inputs, closed forms, invariants, the page's jagged example and
+its FLOP formula).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = ["round_bf16", "silu", "jagged_offsets", "MacCounter", "OracleCache",
+           "encode", "layer_user", "attention_user", "user_positions", "count_macs"]
+
+_BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+_BF16_MIN_QUANTUM_EXP = -133          # smallest bfloat16 subnormal is 2**-133
+
+
+def round_bf16(x) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 value, ties to even.
+
+    bfloat16 keeps 8 significant bits with float32's exponent range: a value of
+    binade [2**(e-1), 2**e) is quantised to multiples of 2**(e-8), subnormals to
+    multiples of 2**-133. Results beyond the largest finite bfloat16 become
+    +-inf (IEEE overflow under round-to-nearest); signed zeros, inf and NaN pass
+    through. Rounds once from float64 (no intermediate float32 step).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    q = np.maximum(e - 8, _BF16_MIN_QUANTUM_EXP)
+    with np.errstate(invalid="ignore", over="ignore"):
+        y = np.ldexp(np.rint(np.ldexp(x, -q)), q)
+        y = np.where(np.abs(y) > _BF16_MAX, np.copysign(np.inf, x), y)
+    return y
+
+
+def silu(x) -> np.ndarray:
+    """SiLU(x) = x / (1 + exp(-x)) in float64; tends to -0 as x -> -inf (no NaN)."""
+    x = np.asarray(x, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return x / (1.0 + np.exp(-x))
+
+
+def jagged_offsets(lengths) -> np.ndarray:
+    """Offsets of a jagged batch: the exclusive running sum of the segment lengths,
+    with one more entry than there are segments (values + lengths layout)."""
+    out = [0]
+    for n in lengths:
+        if int(n) < 0:
+            raise ValueError("negative segment length")
+        out.append(out[-1] + int(n))
+    return np.asarray(out, dtype=np.int64)
+
+
+@dataclasses.dataclass
+class MacCounter:
+    """Multiply-accumulates counted while the oracle computes, by category.
+
+    gemm_uvqk: the D -> 4D projection; gemm_out: the 3D -> D output GEMM;
+    attn_qk / attn_pv: q.k and a*v over masked history keys (dh per pair and head,
+    i.e. D per pair over all heads); attn_self: a candidate's q.k and a*v with itself.
+    """
+    gemm_uvqk: int = 0
+    gemm_out: int = 0
+    attn_qk: int = 0
+    attn_pv: int = 0
+    attn_self: int = 0
+
+    def total_macs(self) -> int:
+        return self.gemm_uvqk + self.gemm_out + self.attn_qk + self.attn_pv + self.attn_self
+
+    def algorithmic_flops(self) -> int:
+        return 2 * self.total_macs()
+
+
+@dataclasses.dataclass
+class OracleCache:
+    """Per-layer, per-slot history keys and values (after bias), float64.
+
+    k, v: [L, slots, capacity, D]; rows 0..cached_len[b]-1 of slot slot_of_user[b]
+    hold the user's earlier history, in position order.
+    """
+    k: np.ndarray
+    v: np.ndarray
+    slot_of_user: np.ndarray
+    cached_len: np.ndarray
+
+    def copy(self) -> "OracleCache":
+        return OracleCache(self.k.copy(), self.v.copy(), self.slot_of_user.copy(),
+                           self.cached_len.copy())
+
+
+def user_positions(m: int, n: int, c: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Absolute positions: new history row i sits at m+i; every candidate sits at m+n."""
+    return np.arange(m, m + n, dtype=np.int64), np.full(c, m + n, dtype=np.int64)
+
+
+def attention_user(q_u, k_all, v_all, q_c, k_c, v_c, *, m: int, heads: int, inv: float,
+                   bf16: bool, counter: Optional[MacCounter] = None,
+                   uih_rows: Optional[Sequence[int]] = None, block: int = 256):
+    """Target-aware causal SiLU attention for one user.
+
+    q_u [n, D]: new history queries (row i at position m+i); k_all, v_all [m+n, D]:
+    every history key/value, row j at position j; q_c, k_c, v_c [c, D]: candidates.
+    History row i: O_i = inv * sum_{j <= m+i} SiLU(q_i.k_j) v_j.
+    Candidate r:   O_r = inv * (sum_{all j} SiLU(q_r.k_j) v_j + SiLU(q_r.k_r) v_r).
+    Per head h the columns [h*dh, (h+1)*dh) are used. ``uih_rows`` restricts the
+    history outputs to the listed rows (the result then has len(uih_rows) rows).
+    Returns (O_u, O_c).
+    """
+    n, D = q_u.shape
+    c = q_c.shape[0]
+    dh = D // heads
+    rows = np.arange(n) if uih_rows is None else np.asarray(uih_rows, dtype=np.int64)
+    R = round_bf16 if bf16 else (lambda a: a)
+    o_u = np.zeros((rows.shape[0], D))
+    o_c = np.zeros((c, D))
+    nkeys = k_all.shape[0]
+    key_pos = np.arange(nkeys)
+    for h in range(heads):
+        cols = slice(h * dh, (h + 1) * dh)
+        kh, vh = k_all[:, cols], v_all[:, cols]
+        for s in range(0, rows.shape[0], block):
+            rb = rows[s:s + block]
+            allowed = key_pos[None, :] <= (m + rb)[:, None]
+            a = np.where(allowed, silu(q_u[rb][:, cols] @ kh.T), 0.0)
+            a = R(a)
+            o_u[s:s + block, cols] = R(inv * (a @ vh))
+            if counter is not None:
+                counter.attn_qk += int(allowed.sum()) * dh
+                counter.attn_pv += int(allowed.sum()) * dh
+        for s in range(0, c, block):
+            qc = q_c[s:s + block, cols]
+            a = R(silu(qc @ kh.T))
+            a_self = R(silu(np.sum(qc * k_c[s:s + block, cols], axis=1)))
+            o_c[s:s + block, cols] = R(inv * (a @ vh + a_self[:, None] * v_c[s:s + block, cols]))
+            if counter is not None:
+                counter.attn_qk += qc.shape[0] * nkeys * dh
+                counter.attn_pv += qc.shape[0] * nkeys * dh
+                counter.attn_self += 2 * qc.shape[0] * dh
+    return o_u, o_c
+
+
+def _project(x, w1, pos_table, positions, bf16, counter):
+    """S = SiLU(X W1) split into U, V, Q, K; position bias on V, Q, K (not U)."""
+    D = x.shape[1]
+    R = round_bf16 if bf16 else (lambda a: a)
+    s = silu(x @ w1)
+    if counter is not None:
+        counter.gemm_uvqk += x.shape[0] * D * 4 * D
+    bias = pos_table[positions]
+    u = R(s[:, 0:D])
+    v = R(s[:, D:2 * D] + bias[:, 0:D])
+    q = R(s[:, 2 * D:3 * D] + bias[:, D:2 * D])
+    k = R(s[:, 3 * D:4 * D] + bias[:, 2 * D:3 * D])
+    return u, v, q, k
+
+
+def _output(x, u, o, w2, bf16, counter):
+    """X' = X + [U | O | U*O] W2 (gate and sum rounded once each in bf16 mode)."""
+    R = round_bf16 if bf16 else (lambda a: a)
+    D = x.shape[1]
+    gate = R(u * o)
+    z = np.concatenate([u, o, gate], axis=1) @ w2
+    if counter is not None:
+        counter.gemm_out += x.shape[0] * 3 * D * D
+    return R(x + z)
+
+
+def layer_user(x_u, x_c, w1, w2, pos_table, *, k_cached, v_cached, heads: int, max_len: int,
+               bf16: bool, counter: Optional[MacCounter] = None,
+               uih_rows: Optional[Sequence[int]] = None):
+    """One encoder layer for one user.
+
+    x_u [n, D] new history tokens, x_c [c, D] candidates, k_cached/v_cached [m, D]
+    the user's cached keys/values for this layer. History and candidate rows go
+    through separate products, so history results never depend on the candidates.
+    Returns (x_u', x_c', k_new, v_new); with ``uih_rows`` x_u' holds only those rows.
+    """
+    m = k_cached.shape[0]
+    n, c = x_u.shape[0], x_c.shape[0]
+    if m + n + 1 > max_len:
+        raise ValueError("history plus candidate slot exceeds the position table")
+    pos_u, pos_c = user_positions(m, n, c)
+    u_u, v_u, q_u, k_u = _project(x_u, w1, pos_table, pos_u, bf16, counter)
+    u_c, v_c, q_c, k_c = _project(x_c, w1, pos_table, pos_c, bf16, counter)
+    k_all = np.concatenate([k_cached, k_u], axis=0)
+    v_all = np.concatenate([v_cached, v_u], axis=0)
+    o_u, o_c = attention_user(q_u, k_all, v_all, q_c, k_c, v_c, m=m, heads=heads,
+                              inv=1.0 / max_len, bf16=bf16, counter=counter, uih_rows=uih_rows)
+    rows = np.arange(n) if uih_rows is None else np.asarray(uih_rows, dtype=np.int64)
+    y_u = _output(x_u[rows], u_u[rows], o_u, w2, bf16, counter)
+    y_c = _output(x_c, u_c, o_c, w2, bf16, counter)
+    return y_u, y_c, k_u, v_u
+
+
+def encode(uih, uih_offsets, cand, cand_offsets, params, *, heads: int, max_len: int,
+           mode: str, cache: Optional[OracleCache] = None,
+           counter: Optional[MacCounter] = None, users: Optional[Sequence[int]] = None):
+    """The whole layer stack over a jagged batch.
+
+    uih [Nu, D], cand [Nc, D]: tokens in jagged layout with int offsets [B+1].
+    params: per layer (w1 [D,4D], w2 [3D,D], pos [max_len,3D]) in math layout
+    (objects with .w1/.w2/.pos or 3-tuples). mode: "f64" or "bf16".
+    cache: None (no earlier history) or an OracleCache; a copy is returned with
+    every layer's new keys/values appended and cached_len advanced.
+    users: optional subset of user indices to compute (the others' rows are NaN).
+    Returns (uih_out [Nu, D], cand_out [Nc, D], new_cache).
+    """
+    if mode not in ("f64", "bf16"):
+        raise ValueError(mode)
+    bf16 = mode == "bf16"
+    uih = np.asarray(uih, dtype=np.float64)
+    cand = np.asarray(cand, dtype=np.float64)
+    D = uih.shape[1]
+    layers = [(p.w1, p.w2, p.pos) if hasattr(p, "w1") else tuple(p) for p in params]
+    layers = [tuple(np.asarray(a, dtype=np.float64) for a in lp) for lp in layers]
+    B = len(uih_offsets) - 1
+    new_cache = cache.copy() if cache is not None else None
+    uih_out = np.full_like(uih, np.nan)
+    cand_out = np.full_like(cand, np.nan)
+    for b in (range(B) if users is None else users):
+        xu = uih[uih_offsets[b]:uih_offsets[b + 1]]
+        xc = cand[cand_offsets[b]:cand_offsets[b + 1]]
+        n = xu.shape[0]
+        if new_cache is not None:
+            slot, m = int(new_cache.slot_of_user[b]), int(new_cache.cached_len[b])
+            if m + n > new_cache.k.shape[2]:
+                raise ValueError("cache capacity exceeded")
+        else:
+            slot, m = -1, 0
+        for l, (w1, w2, pos) in enumerate(layers):
+            if new_cache is not None:
+                kc, vc = new_cache.k[l, slot, :m], new_cache.v[l, slot, :m]
+            else:
+                kc, vc = np.zeros((0, D)), np.zeros((0, D))
+            xu, xc, k_new, v_new = layer_user(xu, xc, w1, w2, pos, k_cached=kc, v_cached=vc,
+                                              heads=heads, max_len=max_len, bf16=bf16,
+                                              counter=counter)
+            if new_cache is not None:
+                new_cache.k[l, slot, m:m + n] = k_new
+                new_cache.v[l, slot, m:m + n] = v_new
+        if new_cache is not None:
+            new_cache.cached_len[b] = m + n
+        uih_out[uih_offsets[b]:uih_offsets[b + 1]] = xu
+        cand_out[cand_offsets[b]:cand_offsets[b + 1]] = xc
+    return uih_out, cand_out, new_cache
+
+
+def count_macs(D: int, layers: int, n: int, c: int, m: int) -> Dict[str, int]:
+    """Multiply-accumulates of ``layers`` layers for one user with m cached, n new and
+    c candidate rows, enumerated query row by query row (history row i sees m+i+1 keys;
+    each candidate sees the m+n history keys plus itself). Gives the counter's values
+    at sizes where running the oracle itself would take too long."""
+    pairs_u = sum(m + i + 1 for i in range(n))
+    pairs_c = c * (m + n)
+    per_layer = {
+        "gemm_uvqk": (n + c) * D * 4 * D,
+        "gemm_out": (n + c) * 3 * D * D,
+        "attn_qk": (pairs_u + pairs_c) * D,
+        "attn_pv": (pairs_u + pairs_c) * D,
+        "attn_self": 2 * c * D,
+    }
+    return {k: v * layers for k, v in per_layer.items()}

@@ -1,0 +1,192 @@
+"""Seeded synthetic inputs for the jagged HSTU encoder.
+
+This module only draws numbers: lengths, token embeddings and layer parameters.
+It holds none of the encoder's arithmetic, and it is the one module that both the
+CPU oracle (``oracle/``) and the HIP path's tests and benchmark import.
+
+The DLRMv3 ranking benchmark reviewed on the page "DLRMv3: MLPerf Inference
+generative recommendation benchmark" (section "Dataset selection") asks for
+requests with thousands of history events over a huge hashed item set, replayed in
+time order. That dataset is not available here; the workloads below stand in for it:
+
+* token embeddings are drawn directly (the embedding-table lookup is upstream of
+  the encoder), N(0, 1);
+* per layer, the fused projection weight W1 [D, 4D] ~ N(0, var 1/D), the output
+  weight W2 [3D, D] ~ N(0, var 1/D) and the absolute position-bias table
+  P [max_len, 3D] ~ N(0, std 0.02);
+* UIH lengths follow each workload's distribution; the streaming workload draws a
+  cached prefix plus newly appended events per user.
+
+Values are drawn in float32 from ``numpy.random.Generator(PCG64(seed))`` in a fixed
+order (lengths; per user UIH then candidate embeddings; per layer W1, W2, P).
+For bfloat16 workloads every drawn value is then stored once as the nearest
+bfloat16 (round to nearest even), so both sides consume identical bits.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, List, Optional, Tuple
+
+import numpy as np
+
+__all__ = ["WORKLOADS", "Workload", "LayerParams", "make_workload", "make_custom",
+           "to_bf16_values", "lengths_to_offsets"]
+
+
+@dataclasses.dataclass(frozen=True)
+class WorkloadSpec:
+    name: str
+    seed: int
+    layers: int
+    dtype: str            # "f32" or "bf16"
+    users: int
+    uih_dist: Tuple       # ("uniform", lo, hi) | ("lognormal", median, sigma, lo, hi) | ("fixed", n)
+    cached: int           # cached prefix tokens per user (streaming), 0 otherwise
+    cands: int            # candidates per user
+    d_model: int
+    heads: int
+    max_len: int          # rows of the position-bias table = UIH bound + 1 candidate slot
+
+
+# The five workloads. The headline one is "d512_uih2k_c2k" (D=512, UIH ~2K, 2K candidates).
+WORKLOADS: Dict[str, WorkloadSpec] = {
+    s.name: s for s in [
+        WorkloadSpec("tiny_f32", 1, 1, "f32", 4, ("uniform", 16, 64), 0, 8, 64, 2, 65),
+        WorkloadSpec("d256_uih1k_c64", 2, 4, "bf16", 32, ("uniform", 256, 1024), 0, 64, 256, 4, 1025),
+        WorkloadSpec("d512_uih2k_c2k", 3, 8, "bf16", 16, ("lognormal", 2000, 0.5, 512, 4096), 0, 2048,
+                     512, 4, 4097),
+        WorkloadSpec("stream_3000p300_c2k", 4, 8, "bf16", 64, ("fixed", 300), 3000, 2048, 512, 4, 3301),
+        WorkloadSpec("long_uih16k_c2k", 5, 16, "bf16", 4, ("uniform", 8192, 16384), 0, 2048, 512, 8, 16385),
+    ]
+}
+
+
+@dataclasses.dataclass
+class LayerParams:
+    """One layer's parameters in mathematical layout (float32 arrays).
+
+    w1:  [D, 4D]; G = X @ w1; column blocks U, V, Q, K.
+    w2:  [3D, D]; Z = [U | O | U*O] @ w2; row blocks U, O, U*O.
+    pos: [max_len, 3D]; column blocks added to V, Q, K.
+    """
+    w1: np.ndarray
+    w2: np.ndarray
+    pos: np.ndarray
+
+
+@dataclasses.dataclass
+class Workload:
+    name: str
+    dtype: str
+    layers: int
+    d_model: int
+    heads: int
+    max_len: int
+    uih_lengths: np.ndarray      # [B] int64, new UIH tokens per user
+    cand_lengths: np.ndarray     # [B] int64
+    cached_lengths: np.ndarray   # [B] int64, prefix tokens to be cached first (streaming)
+    prefix: np.ndarray           # [sum cached, D] float32 prefix tokens (empty if none)
+    uih: np.ndarray              # [sum uih_lengths, D] float32
+    cand: np.ndarray             # [sum cand_lengths, D] float32
+    params: List[LayerParams]
+
+    @property
+    def users(self) -> int:
+        return int(self.uih_lengths.shape[0])
+
+
+def to_bf16_values(x: np.ndarray) -> np.ndarray:
+    """Storage conversion: float32 -> nearest bfloat16 (ties to even), kept as float32.
+
+    Input preparation only. NaN is not produced by the generator, so it is not handled.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return (rounded.astype(np.uint32) << 16).view(np.float32).reshape(x.shape)
+
+
+def lengths_to_offsets(lengths) -> np.ndarray:
+    """Exclusive scan of jagged lengths (values + lengths layout), as int32 [B+1]."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    out = np.zeros(lengths.shape[0] + 1, dtype=np.int64)
+    np.cumsum(lengths, out=out[1:])
+    return out.astype(np.int32)
+
+
+def _draw_lengths(rng: np.random.Generator, spec: WorkloadSpec) -> np.ndarray:
+    kind = spec.uih_dist[0]
+    if kind == "uniform":
+        lo, hi = spec.uih_dist[1], spec.uih_dist[2]
+        return rng.integers(lo, hi, size=spec.users, endpoint=True).astype(np.int64)
+    if kind == "lognormal":
+        median, sigma, lo, hi = spec.uih_dist[1:]
+        raw = rng.lognormal(mean=math.log(median), sigma=sigma, size=spec.users)
+        return np.clip(np.rint(raw), lo, hi).astype(np.int64)
+    if kind == "fixed":
+        return np.full(spec.users, spec.uih_dist[1], dtype=np.int64)
+    raise ValueError(kind)
+
+
+def _normal(rng, shape, std) -> np.ndarray:
+    return rng.standard_normal(size=shape, dtype=np.float32) * np.float32(std)
+
+
+def _finish(spec_dtype, arrays):
+    if spec_dtype == "bf16":
+        return [to_bf16_values(a) for a in arrays]
+    return [np.ascontiguousarray(a, dtype=np.float32) for a in arrays]
+
+
+def make_custom(*, seed: int, dtype: str, layers: int, d_model: int, heads: int, max_len: int,
+                uih_lengths, cand_lengths, cached_lengths=None, name: str = "custom") -> Workload:
+    """A workload with explicit lengths (tests: ragged tails, empty users, tiny shapes)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    uih_lengths = np.asarray(uih_lengths, dtype=np.int64)
+    cand_lengths = np.asarray(cand_lengths, dtype=np.int64)
+    B = uih_lengths.shape[0]
+    cached_lengths = (np.zeros(B, dtype=np.int64) if cached_lengths is None
+                      else np.asarray(cached_lengths, dtype=np.int64))
+    return _draw_rest(rng, name, dtype, layers, d_model, heads, max_len,
+                      uih_lengths, cand_lengths, cached_lengths)
+
+
+def _draw_rest(rng, name, dtype, layers, D, H, max_len, uih_lengths, cand_lengths, cached_lengths):
+    prefix_parts, uih_parts, cand_parts = [], [], []
+    for b in range(uih_lengths.shape[0]):
+        m, n, c = int(cached_lengths[b]), int(uih_lengths[b]), int(cand_lengths[b])
+        hist = _normal(rng, (m + n, D), 1.0)        # the user's whole history, oldest first
+        prefix_parts.append(hist[:m])
+        uih_parts.append(hist[m:])
+        cand_parts.append(_normal(rng, (c, D), 1.0))
+    params = []
+    for _ in range(layers):
+        w1 = _normal(rng, (D, 4 * D), 1.0 / math.sqrt(D))
+        w2 = _normal(rng, (3 * D, D), 1.0 / math.sqrt(D))
+        pos = _normal(rng, (max_len, 3 * D), 0.02)
+        w1, w2, pos = _finish(dtype, [w1, w2, pos])
+        params.append(LayerParams(w1, w2, pos))
+    cat = lambda parts: (np.concatenate(parts, axis=0) if parts else np.zeros((0, D), np.float32))
+    prefix, uih, cand = _finish(dtype, [cat(prefix_parts), cat(uih_parts), cat(cand_parts)])
+    return Workload(name=name, dtype=dtype, layers=layers, d_model=D, heads=H, max_len=max_len,
+                    uih_lengths=uih_lengths, cand_lengths=cand_lengths,
+                    cached_lengths=cached_lengths, prefix=prefix, uih=uih, cand=cand, params=params)
+
+
+def make_workload(name: str, *, users: Optional[int] = None, layers: Optional[int] = None) -> Workload:
+    """Draw one of the named workloads.
+
+    ``users``/``layers`` truncate it for quick tests. The draw order is unchanged, so the
+    first users' lengths and embeddings match the full draw, but the layer parameters
+    (drawn after all users) do not: a truncated workload is a different problem."""
+    spec = WORKLOADS[name]
+    rng = np.random.Generator(np.random.PCG64(spec.seed))
+    lengths = _draw_lengths(rng, spec)
+    B = spec.users if users is None else users
+    L = spec.layers if layers is None else layers
+    lengths = lengths[:B]
+    cands = np.full(B, spec.cands, dtype=np.int64)
+    cached = np.full(B, spec.cached, dtype=np.int64)
+    return _draw_rest(rng, spec.name, spec.dtype, L, spec.d_model, spec.heads, spec.max_len,
+                      lengths, cands, cached)
