@@ -1,0 +1,219 @@
+"""Python binding of libhstu.so, the gfx950 jagged HSTU encoder (C ABI in include/hstu.h).
+
+Argument marshalling only: PyTorch supplies device memory and the current stream,
+and every step of the encoder runs in the library's HIP kernels. There is no
+fallback: if the library is missing or fails to load, every call raises.
+
+Low-level functions carry the C names (``hstu_encode``, ``hstu_workspace_size``,
+``hstu_flops``, ``hstu_abi_version``, ``hstu_status_string``). ``Model``,
+``KVCache`` and ``encode`` wrap them for torch tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = ["HSTU_F32", "HSTU_BF16", "HstuError", "load_library", "library_path",
+           "hstu_abi_version", "hstu_status_string", "hstu_workspace_size", "hstu_flops",
+           "hstu_encode", "Model", "KVCache", "encode", "HstuDims", "HstuLayerWeights",
+           "HstuKvCache"]
+
+HSTU_F32, HSTU_BF16 = 0, 1
+HSTU_OK = 0
+_EXPORTS = ["hstu_abi_version", "hstu_status_string", "hstu_workspace_size", "hstu_flops",
+            "hstu_encode"]
+
+
+class HstuDims(ctypes.Structure):
+    _fields_ = [("layers", ctypes.c_int32), ("d_model", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("max_len", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class HstuLayerWeights(ctypes.Structure):
+    _fields_ = [("w_uvqk", ctypes.c_void_p), ("w_out", ctypes.c_void_p), ("pos_bias", ctypes.c_void_p)]
+
+
+class HstuKvCache(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("slots", ctypes.c_int32),
+                ("capacity", ctypes.c_int32), ("slot_of_user", ctypes.POINTER(ctypes.c_int32)),
+                ("cached_len", ctypes.POINTER(ctypes.c_int32))]
+
+
+class HstuError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({hstu_status_string(status)})")
+
+
+def library_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhstu.so")
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libhstu.so (built in-tree by ``__graft_entry__.build()``). Raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build the HIP library first (__graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER
+    i32p = P(ctypes.c_int32)
+    lib.hstu_abi_version.restype = ctypes.c_int32
+    lib.hstu_abi_version.argtypes = []
+    lib.hstu_status_string.restype = ctypes.c_char_p
+    lib.hstu_status_string.argtypes = [ctypes.c_int32]
+    lib.hstu_workspace_size.restype = ctypes.c_int32
+    lib.hstu_workspace_size.argtypes = [P(HstuDims), ctypes.c_int32, i32p, i32p, P(ctypes.c_size_t)]
+    lib.hstu_flops.restype = ctypes.c_int32
+    lib.hstu_flops.argtypes = [P(HstuDims), ctypes.c_int32, i32p, i32p, i32p, P(ctypes.c_uint64),
+                               P(ctypes.c_uint64)]
+    lib.hstu_encode.restype = ctypes.c_int32
+    lib.hstu_encode.argtypes = [P(HstuDims), ctypes.c_int32, i32p, i32p, ctypes.c_void_p, ctypes.c_void_p,
+                                P(HstuLayerWeights), P(HstuKvCache), ctypes.c_void_p, ctypes.c_void_p,
+                                ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    _lib = lib
+    return lib
+
+
+def _i32(a) -> Tuple[np.ndarray, ctypes.POINTER(ctypes.c_int32)]:
+    if a is None:
+        return None, None
+    arr = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _dims(layers, d_model, heads, max_len, dtype) -> HstuDims:
+    return HstuDims(layers, d_model, heads, max_len, dtype)
+
+
+def hstu_abi_version() -> int:
+    return int(load_library().hstu_abi_version())
+
+
+def hstu_status_string(status: int) -> str:
+    return load_library().hstu_status_string(int(status)).decode()
+
+
+def hstu_workspace_size(dims: HstuDims, B: int, uih_offsets, cand_offsets) -> Tuple[int, int]:
+    """Returns (status, bytes)."""
+    _, uo = _i32(uih_offsets)
+    _, co = _i32(cand_offsets)
+    out = ctypes.c_size_t(0)
+    st = load_library().hstu_workspace_size(ctypes.byref(dims), B, uo, co, ctypes.byref(out))
+    return int(st), int(out.value)
+
+
+def hstu_flops(dims: HstuDims, B: int, uih_offsets, cand_offsets, cached_len=None) -> Tuple[int, int, int]:
+    """Returns (status, algorithmic_flops, formula_flops)."""
+    _, uo = _i32(uih_offsets)
+    _, co = _i32(cand_offsets)
+    _, cl = _i32(cached_len)
+    alg, form = ctypes.c_uint64(0), ctypes.c_uint64(0)
+    st = load_library().hstu_flops(ctypes.byref(dims), B, uo, co, cl, ctypes.byref(alg), ctypes.byref(form))
+    return int(st), int(alg.value), int(form.value)
+
+
+def hstu_encode(dims: HstuDims, B: int, uih_offsets, cand_offsets, uih_ptr: int, cand_ptr: int,
+                weights: Sequence[HstuLayerWeights], kv: Optional[HstuKvCache], uih_out_ptr: int,
+                cand_out_ptr: int, workspace_ptr: int, workspace_bytes: int, stream: int) -> int:
+    """Raw call with integer device pointers. Returns the status."""
+    _, uo = _i32(uih_offsets)
+    _, co = _i32(cand_offsets)
+    warr = (HstuLayerWeights * max(len(weights), 1))(*weights)
+    return int(load_library().hstu_encode(ctypes.byref(dims), B, uo, co, uih_ptr, cand_ptr, warr,
+                                          ctypes.byref(kv) if kv is not None else None,
+                                          uih_out_ptr, cand_out_ptr, workspace_ptr, workspace_bytes, stream))
+
+
+# ---------------------------------------------------------------------------- torch helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+class Model:
+    """Device-resident parameters of an encoder stack in the ABI's layout.
+
+    ``params``: per layer objects with ``w1`` [D,4D], ``w2`` [3D,D], ``pos`` [max_len,3D]
+    (math layout, float32 numpy arrays); they are stored transposed as [out][in].
+    """
+
+    def __init__(self, params, *, d_model: int, heads: int, max_len: int, dtype: str, device="cuda"):
+        torch = _torch()
+        self.d_model, self.heads, self.max_len = d_model, heads, max_len
+        self.dtype_code = HSTU_BF16 if dtype == "bf16" else HSTU_F32
+        self.torch_dtype = torch.bfloat16 if dtype == "bf16" else torch.float32
+        self.layers: List[Tuple] = []
+        for p in params:
+            w1 = torch.from_numpy(np.ascontiguousarray(p.w1.T)).to(device=device, dtype=self.torch_dtype)
+            w2 = torch.from_numpy(np.ascontiguousarray(p.w2.T)).to(device=device, dtype=self.torch_dtype)
+            pos = torch.from_numpy(np.ascontiguousarray(p.pos)).to(device=device, dtype=self.torch_dtype)
+            self.layers.append((w1.contiguous(), w2.contiguous(), pos.contiguous()))
+        self.weights = [HstuLayerWeights(a.data_ptr(), b.data_ptr(), c.data_ptr()) for a, b, c in self.layers]
+
+    def dims(self, layers: Optional[int] = None) -> HstuDims:
+        return _dims(len(self.layers) if layers is None else layers, self.d_model, self.heads,
+                     self.max_len, self.dtype_code)
+
+
+class KVCache:
+    """Caller-owned streaming cache: k, v [layers][slots][capacity][D] on the device plus
+    host int32 ``cached_len`` and ``slot_of_user`` (per user of the next call)."""
+
+    def __init__(self, model: Model, slots: int, capacity: int, device="cuda"):
+        torch = _torch()
+        L, D = len(model.layers), model.d_model
+        self.k = torch.zeros((L, slots, capacity, D), dtype=model.torch_dtype, device=device)
+        self.v = torch.zeros((L, slots, capacity, D), dtype=model.torch_dtype, device=device)
+        self.slots, self.capacity = slots, capacity
+        self.slot_of_user = np.arange(slots, dtype=np.int32)
+        self.cached_len = np.zeros(slots, dtype=np.int32)
+
+    def struct(self) -> HstuKvCache:
+        self.slot_of_user = np.ascontiguousarray(self.slot_of_user, dtype=np.int32)
+        self.cached_len = np.ascontiguousarray(self.cached_len, dtype=np.int32)
+        return HstuKvCache(self.k.data_ptr(), self.v.data_ptr(), self.slots, self.capacity,
+                           self.slot_of_user.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                           self.cached_len.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+
+
+def workspace_bytes(model: Model, uih_offsets, cand_offsets) -> int:
+    B = len(uih_offsets) - 1
+    st, nbytes = hstu_workspace_size(model.dims(), B, uih_offsets, cand_offsets)
+    if st != HSTU_OK:
+        raise HstuError(st, "hstu_workspace_size")
+    return nbytes
+
+
+def encode(model: Model, uih, uih_offsets, cand, cand_offsets, *, cache: Optional[KVCache] = None,
+           out: Optional[Tuple] = None, workspace=None, stream=None):
+    """Run hstu_encode on the current (or given) stream; returns (uih_out, cand_out).
+
+    uih/cand: device tensors [rows, D] in the model's dtype; offsets: host int sequences.
+    The cache's ``cached_len`` advances on success.
+    """
+    torch = _torch()
+    B = len(uih_offsets) - 1
+    if out is None:
+        out = (torch.empty_like(uih), torch.empty_like(cand))
+    nbytes = workspace_bytes(model, uih_offsets, cand_offsets)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=uih.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(uih.device).cuda_stream
+    kv = cache.struct() if cache is not None else None
+    st = hstu_encode(model.dims(), B, uih_offsets, cand_offsets, uih.data_ptr(), cand.data_ptr(),
+                     model.weights, kv, out[0].data_ptr(), out[1].data_ptr(), workspace.data_ptr(),
+                     workspace.numel(), stream)
+    if st != HSTU_OK:
+        raise HstuError(st, "hstu_encode")
+    return out

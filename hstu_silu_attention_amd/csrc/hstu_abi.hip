@@ -1,0 +1,331 @@
+// Host side of the C ABI declared in include/hstu.h: argument validation, the
+// jagged work planner, the pinned staging ring and the per-layer launch sequence.
+//
+// Validation is complete before anything is enqueued, so every error except
+// HSTU_ERR_HIP leaves the device and every host array untouched.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <mutex>
+#include <numeric>
+#include <unordered_map>
+#include <vector>
+
+#include "../../include/hstu.h"
+#include "hstu_internal.h"
+
+namespace {
+
+using hstu::UserRec;
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+hstu_status check_dims(const hstu_dims* d) {
+  if (!d) return HSTU_ERR_NULL;
+  if (d->layers < 1 || d->d_model <= 0 || d->heads <= 0 || d->max_len < 1) return HSTU_ERR_SHAPE;
+  if (d->d_model % d->heads) return HSTU_ERR_SHAPE;
+  const int dh = d->d_model / d->heads;
+  if (d->dtype == HSTU_F32) {
+    if (d->d_model % 64 || (dh != 32 && dh != 64 && dh != 128)) return HSTU_ERR_SHAPE;
+  } else if (d->dtype == HSTU_BF16) {
+    if (d->d_model % 128 || (dh != 64 && dh != 128)) return HSTU_ERR_SHAPE;
+  } else {
+    return HSTU_ERR_SHAPE;
+  }
+  return HSTU_OK;
+}
+
+// Offsets are the exclusive running sum of per-user lengths: start at 0, never decrease.
+hstu_status check_offsets(int32_t B, const int32_t* uo, const int32_t* co) {
+  if (B < 0) return HSTU_ERR_SHAPE;
+  if (B == 0) return HSTU_OK;
+  if (!uo || !co) return HSTU_ERR_NULL;
+  if (uo[0] != 0 || co[0] != 0) return HSTU_ERR_OFFSETS;
+  for (int32_t b = 0; b < B; ++b)
+    if (uo[b + 1] < uo[b] || co[b + 1] < co[b]) return HSTU_ERR_OFFSETS;
+  if ((int64_t)uo[B] + (int64_t)co[B] > INT32_MAX) return HSTU_ERR_SHAPE;
+  return HSTU_OK;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Layout {
+  int32_t Nu = 0, Nc = 0, T = 0;
+  int64_t ntiles = 0;
+  size_t users = 0, tiles = 0, rows = 0, uvqk = 0, o = 0, x = 0, total = 0;
+  size_t staged = 0;  // bytes copied from the host: users table + tile list
+};
+
+Layout make_layout(const hstu_dims* d, int32_t B, const int32_t* uo, const int32_t* co) {
+  Layout L;
+  if (B > 0) {
+    L.Nu = uo[B];
+    L.Nc = co[B];
+  }
+  L.T = L.Nu + L.Nc;
+  const int bm = hstu::attn_block_rows(d->dtype);
+  for (int32_t b = 0; b < B; ++b)
+    L.ntiles += d->heads * (cdiv(uo[b + 1] - uo[b], bm) + cdiv(co[b + 1] - co[b], bm));
+  const size_t es = d->dtype == HSTU_F32 ? 4 : 2;
+  const size_t D = (size_t)d->d_model, T = (size_t)L.T;
+  size_t off = 0;
+  L.users = off; off += align_up((size_t)B * sizeof(UserRec));
+  L.tiles = off; off += align_up((size_t)L.ntiles * 16);
+  L.staged = off;
+  L.rows = off; off += align_up(T * 8);
+  L.uvqk = off; off += align_up(T * 4 * D * es);
+  L.o = off; off += align_up(T * D * es);
+  L.x = off; off += d->layers > 1 ? align_up(T * D * es) : 0;
+  L.total = L.T == 0 ? 0 : off;
+  return L;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// ---------------------------------------------------------------- pinned staging ring
+// The plan (users table + tile list) is written into pinned host memory and copied
+// asynchronously into the workspace. A ring slot is reused only after the copy that
+// last read it has completed (its event), so a call never waits for the device
+// unless more than kRing calls are in flight on the device.
+constexpr int kRing = 4;
+struct StageSlot {
+  void* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t ev = nullptr;
+  bool pending = false;
+};
+struct DeviceStage {
+  StageSlot slot[kRing];
+  int next = 0;
+};
+std::mutex g_stage_mu;
+std::unordered_map<int, DeviceStage> g_stage;
+
+hstu_status stage_and_copy(const void* src, size_t bytes, void* dst, hipStream_t stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return HSTU_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_stage_mu);
+  DeviceStage& ds = g_stage[dev];
+  StageSlot& s = ds.slot[ds.next];
+  ds.next = (ds.next + 1) % kRing;
+  if (s.pending) {
+    if (hipEventSynchronize(s.ev) != hipSuccess) return HSTU_ERR_HIP;
+    s.pending = false;
+  }
+  if (s.cap < bytes) {
+    if (s.host && hipHostFree(s.host) != hipSuccess) return HSTU_ERR_HIP;
+    s.host = nullptr;
+    s.cap = 0;
+    size_t cap = std::max<size_t>(bytes, 64 * 1024);
+    if (hipHostMalloc(&s.host, cap, hipHostMallocDefault) != hipSuccess) return HSTU_ERR_HIP;
+    s.cap = cap;
+  }
+  if (!s.ev && hipEventCreateWithFlags(&s.ev, hipEventDisableTiming) != hipSuccess) return HSTU_ERR_HIP;
+  std::memcpy(s.host, src, bytes);
+  if (hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, stream) != hipSuccess)
+    return HSTU_ERR_HIP;
+  if (hipEventRecord(s.ev, stream) != hipSuccess) return HSTU_ERR_HIP;
+  s.pending = true;
+  return HSTU_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t hstu_abi_version(void) { return HSTU_ABI_VERSION; }
+
+const char* hstu_status_string(hstu_status s) {
+  switch (s) {
+    case HSTU_OK: return "ok";
+    case HSTU_ERR_NULL: return "a required pointer is NULL";
+    case HSTU_ERR_SHAPE: return "unsupported dimensions, dtype or batch size";
+    case HSTU_ERR_OFFSETS: return "offsets must start at 0 and never decrease";
+    case HSTU_ERR_CAPACITY: return "history exceeds max_len or cache capacity, or a bad cache slot";
+    case HSTU_ERR_WORKSPACE: return "workspace missing or smaller than hstu_workspace_size()";
+    case HSTU_ERR_HIP: return "a HIP runtime call failed";
+    case HSTU_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+    default: return "unknown status";
+  }
+}
+
+hstu_status hstu_workspace_size(const hstu_dims* d, int32_t B, const int32_t* uih_offsets,
+                                const int32_t* cand_offsets, size_t* bytes) {
+  hstu_status st = check_dims(d);
+  if (st != HSTU_OK) return st;
+  if (!bytes) return HSTU_ERR_NULL;
+  st = check_offsets(B, uih_offsets, cand_offsets);
+  if (st != HSTU_OK) return st;
+  *bytes = make_layout(d, B, uih_offsets, cand_offsets).total;
+  return HSTU_OK;
+}
+
+hstu_status hstu_flops(const hstu_dims* d, int32_t B, const int32_t* uih_offsets,
+                       const int32_t* cand_offsets, const int32_t* cached_len,
+                       uint64_t* algorithmic_flops, uint64_t* formula_flops) {
+  hstu_status st = check_dims(d);
+  if (st != HSTU_OK) return st;
+  st = check_offsets(B, uih_offsets, cand_offsets);
+  if (st != HSTU_OK) return st;
+  const uint64_t D = (uint64_t)d->d_model, L = (uint64_t)d->layers;
+  uint64_t alg = 0, form = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    const uint64_t n = (uint64_t)(uih_offsets[b + 1] - uih_offsets[b]);
+    const uint64_t c = (uint64_t)(cand_offsets[b + 1] - cand_offsets[b]);
+    int32_t mm = cached_len ? cached_len[b] : 0;
+    if (mm < 0) return HSTU_ERR_CAPACITY;
+    const uint64_t m = (uint64_t)mm;
+    // masked (query, key) pairs: history row i sees m+i+1 keys, a candidate m+n keys + itself
+    const uint64_t pairs = n * m + n * (n + 1) / 2 + c * (m + n + 1);
+    alg += L * (14 * (n + c) * D * D + 4 * D * pairs);
+    const uint64_t N = m + n;
+    form += 2 * L * (N * N * D / 2 + N * D * D * 4 + N * D * D * 3);
+  }
+  if (algorithmic_flops) *algorithmic_flops = alg;
+  if (formula_flops) *formula_flops = form;
+  return HSTU_OK;
+}
+
+hstu_status hstu_encode(const hstu_dims* d, int32_t B, const int32_t* uih_offsets,
+                        const int32_t* cand_offsets, const void* uih, const void* cand,
+                        const hstu_layer_weights* w, hstu_kv_cache* kv, void* uih_out,
+                        void* cand_out, void* workspace, size_t workspace_bytes, void* stream) {
+  // ------------------------------------------------------------ validation (host only)
+  hstu_status st = check_dims(d);
+  if (st != HSTU_OK) return st;
+  st = check_offsets(B, uih_offsets, cand_offsets);
+  if (st != HSTU_OK) return st;
+  if (!w) return HSTU_ERR_NULL;
+  const Layout lay = make_layout(d, B, uih_offsets, cand_offsets);
+  if (lay.T == 0) return HSTU_OK;  // nothing to encode; no history appended
+  const int32_t L = d->layers, D = d->d_model;
+  for (int32_t l = 0; l < L; ++l) {
+    if (!w[l].w_uvqk || !w[l].w_out || !w[l].pos_bias) return HSTU_ERR_NULL;
+    if (!aligned16(w[l].w_uvqk) || !aligned16(w[l].w_out) || !aligned16(w[l].pos_bias))
+      return HSTU_ERR_ALIGN;
+  }
+  if ((lay.Nu > 0 && (!uih || !uih_out)) || (lay.Nc > 0 && (!cand || !cand_out))) return HSTU_ERR_NULL;
+  if ((lay.Nu > 0 && (!aligned16(uih) || !aligned16(uih_out))) ||
+      (lay.Nc > 0 && (!aligned16(cand) || !aligned16(cand_out))))
+    return HSTU_ERR_ALIGN;
+  if (kv) {
+    if (!kv->k || !kv->v || !kv->slot_of_user || !kv->cached_len) return HSTU_ERR_NULL;
+    if (!aligned16(kv->k) || !aligned16(kv->v)) return HSTU_ERR_ALIGN;
+    if (kv->slots <= 0 || kv->capacity <= 0) return HSTU_ERR_CAPACITY;
+  }
+  std::vector<char> slot_used(kv ? (size_t)kv->slots : 0, 0);
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t n = uih_offsets[b + 1] - uih_offsets[b];
+    int64_t m = 0;
+    if (kv) {
+      m = kv->cached_len[b];
+      const int32_t slot = kv->slot_of_user[b];
+      if (m < 0 || slot < 0 || slot >= kv->slots || slot_used[slot]) return HSTU_ERR_CAPACITY;
+      slot_used[slot] = 1;
+      if (m + n > kv->capacity) return HSTU_ERR_CAPACITY;
+    }
+    if (m + n + 1 > d->max_len) return HSTU_ERR_CAPACITY;
+  }
+  if (!workspace || workspace_bytes < lay.total) return HSTU_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0) return HSTU_ERR_ALIGN;
+
+  // ------------------------------------------------------------ plan (host)
+  const int bm = hstu::attn_block_rows(d->dtype);
+  std::vector<char> staged(lay.staged, 0);
+  UserRec* users = reinterpret_cast<UserRec*>(staged.data() + lay.users);
+  for (int32_t b = 0; b < B; ++b) {
+    UserRec& u = users[b];
+    u.uoff = uih_offsets[b];
+    u.n = uih_offsets[b + 1] - uih_offsets[b];
+    u.coff = cand_offsets[b];
+    u.c = cand_offsets[b + 1] - cand_offsets[b];
+    u.m = kv ? kv->cached_len[b] : 0;
+    u.key_row = kv ? kv->slot_of_user[b] * kv->capacity : u.uoff;
+    u.pad0 = u.pad1 = 0;
+  }
+  // Attention work items, most keys first, so long items start early and short
+  // ones fill the tail of the launch. The order never changes any result: each
+  // item writes its own rows, with a fixed key order inside.
+  struct Item { int32_t user, hk, q0, nq; int64_t keys; };
+  std::vector<Item> items;
+  items.reserve((size_t)lay.ntiles);
+  for (int32_t b = 0; b < B; ++b) {
+    const UserRec& u = users[b];
+    for (int32_t h = 0; h < d->heads; ++h) {
+      for (int32_t q0 = 0; q0 < u.n; q0 += bm)
+        items.push_back({b, h << 1, q0, std::min(bm, u.n - q0), (int64_t)u.m + q0 + std::min(bm, u.n - q0)});
+      for (int32_t q0 = 0; q0 < u.c; q0 += bm)
+        items.push_back({b, (h << 1) | 1, q0, std::min(bm, u.c - q0), (int64_t)u.m + u.n + 1});
+    }
+  }
+  std::stable_sort(items.begin(), items.end(),
+                   [](const Item& a, const Item& b) { return a.keys > b.keys; });
+  int32_t* tiles = reinterpret_cast<int32_t*>(staged.data() + lay.tiles);
+  for (size_t i = 0; i < items.size(); ++i) {
+    tiles[4 * i + 0] = items[i].user;
+    tiles[4 * i + 1] = items[i].hk;
+    tiles[4 * i + 2] = items[i].q0;
+    tiles[4 * i + 3] = items[i].nq;
+  }
+
+  // ------------------------------------------------------------ enqueue
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  st = stage_and_copy(staged.data(), lay.staged, ws, s);
+  if (st != HSTU_OK) return st;
+  const UserRec* d_users = reinterpret_cast<const UserRec*>(ws + lay.users);
+  const int4* d_tiles = reinterpret_cast<const int4*>(ws + lay.tiles);
+  int2* d_rows = reinterpret_cast<int2*>(ws + lay.rows);
+  const size_t es = d->dtype == HSTU_F32 ? 4 : 2;
+  char* uvqk = ws + lay.uvqk;
+  char* obuf = ws + lay.o;
+  char* xbuf = ws + lay.x;
+  const size_t nu_bytes = (size_t)lay.Nu * D * es;
+
+  hstu::PlanArgs pa{d_users, B, lay.Nu, lay.T, d_rows};
+  if (hstu::launch_plan(pa, s) != hipSuccess) return HSTU_ERR_HIP;
+
+  const int dh = D / d->heads;
+  const size_t layer_cache = kv ? (size_t)kv->slots * kv->capacity * D * es : 0;
+  for (int32_t l = 0; l < L; ++l) {
+    const void* x_lo = l == 0 ? uih : xbuf;
+    const void* x_hi = l == 0 ? cand : (const void*)(xbuf + nu_bytes);
+    void* y_lo = l == L - 1 ? uih_out : (void*)xbuf;
+    void* y_hi = l == L - 1 ? cand_out : (void*)(xbuf + nu_bytes);
+    void* ck = kv ? (void*)((char*)kv->k + l * layer_cache) : nullptr;
+    void* cv = kv ? (void*)((char*)kv->v + l * layer_cache) : nullptr;
+
+    hstu::UvqkArgs ua{x_lo, x_hi, lay.Nu, lay.T, D, w[l].w_uvqk, w[l].pos_bias, d_rows, d_users,
+                      uvqk, ck, cv};
+    if (hstu::launch_uvqk(d->dtype, ua, s) != hipSuccess) return HSTU_ERR_HIP;
+
+    hstu::AttnArgs aa{};
+    aa.tiles = d_tiles;
+    aa.users = d_users;
+    aa.Nu = lay.Nu;
+    aa.D = D;
+    aa.inv = 1.0f / (float)d->max_len;
+    aa.uvqk = uvqk;
+    if (kv) {
+      aa.kbase = ck;
+      aa.vbase = cv;
+      aa.ld = D;
+    } else {
+      aa.kbase = uvqk + 3 * (size_t)D * es;
+      aa.vbase = uvqk + 1 * (size_t)D * es;
+      aa.ld = 4 * (int64_t)D;
+    }
+    aa.o = obuf;
+    if (hstu::launch_attn(d->dtype, dh, aa, (int)lay.ntiles, s) != hipSuccess) return HSTU_ERR_HIP;
+
+    hstu::OutArgs oa{uvqk, obuf, w[l].w_out, x_lo, x_hi, y_lo, y_hi, lay.Nu, lay.T, D};
+    if (hstu::launch_out(d->dtype, oa, s) != hipSuccess) return HSTU_ERR_HIP;
+  }
+  if (kv)
+    for (int32_t b = 0; b < B; ++b) kv->cached_len[b] += uih_offsets[b + 1] - uih_offsets[b];
+  return HSTU_OK;
+}
+
+}  // extern "C"

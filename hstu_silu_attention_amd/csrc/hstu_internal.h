@@ -1,0 +1,74 @@
+// Internal interface between the host planner (hstu_abi.hip) and the gfx950
+// kernels. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hstu {
+
+// One user of the batch, as the kernels see it (32 bytes).
+//  uoff/n:  new history rows uoff..uoff+n-1 of the packed row space
+//  coff/c:  candidate rows Nu+coff..Nu+coff+c-1 of the packed row space
+//  m:       cached history length (positions 0..m-1 live in the cache)
+//  key_row: row of key 0 in the key/value source (cache: slot*capacity;
+//           no cache: uoff, i.e. the user's first history row of the uvqk buffer)
+struct UserRec {
+  int32_t uoff, n, coff, c, m, key_row, pad0, pad1;
+};
+
+// Attention work item: 16 bytes = {user, (head << 1) | is_candidate_tile, q0, nq}.
+// q0 is the tile's first query within the user's history (or candidate) rows,
+// nq <= the kernel's query-block size.
+
+struct PlanArgs {
+  const UserRec* users;
+  int32_t B, Nu, T;
+  int2* row_info;        // [T] {user, position}
+};
+
+struct UvqkArgs {
+  const void* x_lo;      // rows [0, Nu)
+  const void* x_hi;      // rows [Nu, T)
+  int32_t Nu, T, D;
+  const void* w;         // [4D][D]
+  const void* pos;       // [max_len][3D]
+  const int2* row_info;
+  const UserRec* users;
+  void* uvqk;            // [T][4D] out
+  void* cache_k;         // this layer's [slots][cap][D] or nullptr
+  void* cache_v;
+};
+
+struct AttnArgs {
+  const int4* tiles;
+  const UserRec* users;
+  int32_t Nu, D;
+  float inv;             // 1 / max_len
+  const void* uvqk;      // [T][4D]: Q, and the candidates' own K, V
+  const void* kbase;     // key row r of user b is kbase + (key_row_b + r) * ld
+  const void* vbase;
+  int64_t ld;
+  void* o;               // [T][D] out
+};
+
+struct OutArgs {
+  const void* uvqk;      // [T][4D]; U = columns [0, D)
+  const void* o;         // [T][D]
+  const void* w;         // [D][3D]
+  const void* x_lo;      // residual rows [0, Nu)
+  const void* x_hi;      // residual rows [Nu, T)
+  void* y_lo;            // output rows [0, Nu)
+  void* y_hi;            // output rows [Nu, T)
+  int32_t Nu, T, D;
+};
+
+// Query rows per attention work item for a dtype.
+int attn_block_rows(int dtype);
+
+hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+hipError_t launch_uvqk(int dtype, const UvqkArgs& a, hipStream_t s);
+hipError_t launch_attn(int dtype, int dh, const AttnArgs& a, int ntiles, hipStream_t s);
+hipError_t launch_out(int dtype, const OutArgs& a, hipStream_t s);
+
+}  // namespace hstu

@@ -1,0 +1,201 @@
+// float32 kernels (no intermediate rounding). These serve float32 models: plain
+// LDS-tiled VALU arithmetic with float32 accumulation.
+#include <hip/hip_runtime.h>
+
+#include "hstu_internal.h"
+
+namespace hstu {
+namespace {
+
+__device__ __forceinline__ float silu(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.4426950408889634f));
+}
+
+// C[M][N] = A[M][K] * W[N][K]^T on 64 x 64 tiles, K step 16, 4 x 4 outputs per thread.
+constexpr int FT = 64, FK = 16;
+
+template <typename ALoad, typename Epi>
+__device__ __forceinline__ void gemm_f32(const ALoad& aload, const float* __restrict__ w, int K, int M,
+                                         int ncol, const Epi& epi) {
+  __shared__ float sa[FK][FT + 1];
+  __shared__ float sb[FK][FT + 1];
+  const int tile = blockIdx.x;
+  const int row0 = (tile / ncol) * FT, col0 = (tile % ncol) * FT;
+  const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += FK) {
+    __syncthreads();
+    for (int id = tid; id < FT * FK; id += 256) {
+      const int r = id / FK, k = id % FK;
+      sa[k][r] = row0 + r < M ? aload(row0 + r, k0 + k) : 0.0f;
+      sb[k][r] = w[(size_t)(col0 + r) * K + k0 + k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < FK; ++k) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        av[i] = sa[k][ty * 4 + i];
+        bv[i] = sb[k][tx * 4 + i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] += av[i] * bv[j];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = row0 + ty * 4 + i;
+    if (row >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) epi(row, col0 + tx * 4 + j, acc[i][j]);
+  }
+}
+
+struct XLoadF {
+  const float* lo;
+  const float* hi;
+  int Nu, D;
+  __device__ __forceinline__ float operator()(int row, int k) const {
+    return row < Nu ? lo[(size_t)row * D + k] : hi[(size_t)(row - Nu) * D + k];
+  }
+};
+
+struct GateLoadF {
+  const float* uvqk;
+  const float* o;
+  int D;
+  __device__ __forceinline__ float operator()(int row, int k) const {
+    const float* urow = uvqk + (size_t)row * 4 * D;
+    const float* orow = o + (size_t)row * D;
+    if (k < D) return urow[k];
+    if (k < 2 * D) return orow[k - D];
+    return urow[k - 2 * D] * orow[k - 2 * D];
+  }
+};
+
+__global__ __launch_bounds__(256) void uvqk_f32_kernel(UvqkArgs a) {
+  const int D = a.D;
+  const float* pos = (const float*)a.pos;
+  float* out = (float*)a.uvqk;
+  auto epi = [&](int row, int col, float g) {
+    const int2 ri = a.row_info[row];
+    const int slice = col / D, cc = col - slice * D;
+    float v = silu(g);
+    if (slice > 0) v += pos[(size_t)ri.y * 3 * D + (slice - 1) * D + cc];
+    out[(size_t)row * 4 * D + col] = v;
+    if (a.cache_k != nullptr && row < a.Nu && (slice == 1 || slice == 3)) {
+      float* dst = (float*)(slice == 1 ? a.cache_v : a.cache_k);
+      dst[((size_t)a.users[ri.x].key_row + ri.y) * D + cc] = v;
+    }
+  };
+  gemm_f32(XLoadF{(const float*)a.x_lo, (const float*)a.x_hi, a.Nu, D}, (const float*)a.w, D, a.T,
+           4 * D / FT, epi);
+}
+
+__global__ __launch_bounds__(256) void out_f32_kernel(OutArgs a) {
+  const int D = a.D;
+  auto epi = [&](int row, int col, float z) {
+    if (row < a.Nu)
+      ((float*)a.y_lo)[(size_t)row * D + col] = ((const float*)a.x_lo)[(size_t)row * D + col] + z;
+    else
+      ((float*)a.y_hi)[(size_t)(row - a.Nu) * D + col] =
+          ((const float*)a.x_hi)[(size_t)(row - a.Nu) * D + col] + z;
+  };
+  gemm_f32(GateLoadF{(const float*)a.uvqk, (const float*)a.o, D}, (const float*)a.w, 3 * D, a.T,
+           D / FT, epi);
+}
+
+// One work item per workgroup of 64 threads; one thread per query row; key blocks of
+// 32 staged in LDS.
+constexpr int FBM = 64, FKB = 32;
+
+template <int DH>
+__global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
+  __shared__ float sk[FKB][DH];
+  __shared__ float sv[FKB][DH];
+  const int4 t = a.tiles[blockIdx.x];
+  const UserRec u = a.users[t.x];
+  const int head = t.y >> 1, q0 = t.z, nq = t.w;
+  const bool cand = (t.y & 1) != 0;
+  const int tid = threadIdx.x;
+  const int D = a.D;
+  const bool qok = tid < nq;
+  const int qi = q0 + tid;
+  const size_t row = cand ? (size_t)a.Nu + u.coff + qi : (size_t)u.uoff + qi;
+  const float* uvqk = (const float*)a.uvqk;
+  float q[DH], acc[DH];
+#pragma unroll
+  for (int e = 0; e < DH; ++e) {
+    q[e] = qok ? uvqk[row * 4 * D + 2 * D + head * DH + e] : 0.0f;
+    acc[e] = 0.0f;
+  }
+  const int key_end = cand ? u.m + u.n : u.m + q0 + nq;
+  const int qpos = u.m + qi;
+  const float* kp = (const float*)a.kbase + (size_t)u.key_row * a.ld + head * DH;
+  const float* vp = (const float*)a.vbase + (size_t)u.key_row * a.ld + head * DH;
+  for (int k0 = 0; k0 < key_end; k0 += FKB) {
+    __syncthreads();
+    for (int id = tid; id < FKB * DH; id += 64) {
+      const int key = id / DH, e = id % DH;
+      const bool in = k0 + key < key_end;
+      sk[key][e] = in ? kp[(size_t)(k0 + key) * a.ld + e] : 0.0f;
+      sv[key][e] = in ? vp[(size_t)(k0 + key) * a.ld + e] : 0.0f;
+    }
+    __syncthreads();
+    const int kn = min(FKB, key_end - k0);
+    for (int j = 0; j < kn; ++j) {
+      const int key = k0 + j;
+      if (!cand && key > qpos) break;
+      float s = 0.0f;
+#pragma unroll
+      for (int e = 0; e < DH; ++e) s += q[e] * sk[j][e];
+      const float w = silu(s);
+#pragma unroll
+      for (int e = 0; e < DH; ++e) acc[e] += w * sv[j][e];
+    }
+  }
+  if (!qok) return;
+  if (cand) {
+    const float* krow = uvqk + row * 4 * D + 3 * D + head * DH;
+    const float* vrow = uvqk + row * 4 * D + 1 * D + head * DH;
+    float s = 0.0f;
+#pragma unroll
+    for (int e = 0; e < DH; ++e) s += q[e] * krow[e];
+    const float w = silu(s);
+#pragma unroll
+    for (int e = 0; e < DH; ++e) acc[e] += w * vrow[e];
+  }
+  float* orow = (float*)a.o + row * D + head * DH;
+#pragma unroll
+  for (int e = 0; e < DH; ++e) orow[e] = a.inv * acc[e];
+}
+
+}  // namespace
+
+hipError_t launch_uvqk_f32(const UvqkArgs& a, hipStream_t s) {
+  uvqk_f32_kernel<<<((a.T + FT - 1) / FT) * (4 * a.D / FT), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_out_f32(const OutArgs& a, hipStream_t s) {
+  out_f32_kernel<<<((a.T + FT - 1) / FT) * (a.D / FT), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_f32(int dh, const AttnArgs& a, int ntiles, hipStream_t s) {
+  if (ntiles <= 0) return hipSuccess;
+  switch (dh) {
+    case 32: attn_f32_kernel<32><<<ntiles, 64, 0, s>>>(a); break;
+    case 64: attn_f32_kernel<64><<<ntiles, 64, 0, s>>>(a); break;
+    case 128: attn_f32_kernel<128><<<ntiles, 64, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+int attn_block_rows_f32() { return FBM; }
+
+}  // namespace hstu

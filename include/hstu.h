@@ -1,0 +1,168 @@
+/*
+ * hstu.h - C ABI of the MI355X (gfx950) jagged HSTU ranking encoder.
+ *
+ * What it computes. One DLRMv3/HSTU-style ranking-encoder stack over a jagged
+ * batch of users, as described on the page "DLRMv3: MLPerf Inference generative
+ * recommendation benchmark" (section "Model selection"): per layer a fused D->4D
+ * projection, attention Mask(SiLU(Q K^T)) V with an absolute position bias added
+ * to Q, K and V, and a post-attention GEMM of 3*D*D multiply-adds per token. The
+ * user interaction history (UIH) is encoded once per request and shared by every
+ * candidate; a user's history keys/values persist across consecutive timestamps
+ * (same section). Candidates are target-aware (the multi-stage sequence model
+ * page, "Target-Aware Multi-Head Attention"): they attend to the whole history
+ * and to themselves, never to other candidates, and history rows never see
+ * candidates, so the history's representation does not depend on the candidate
+ * set. Jagged batches are concatenated rows plus offsets, the exclusive running
+ * sum of per-user lengths (TorchRec DLRM tutorial page, section 2.1).
+ *
+ * Per layer l, for user b with m cached, n new history rows and c candidates:
+ *   S = SiLU(X W1_l) = [U | V | Q | K]           (each D wide)
+ *   V += P_l[pos, 0:D]; Q += P_l[pos, D:2D]; K += P_l[pos, 2D:3D]
+ *        new history row i has pos = m + i; every candidate has pos = m + n
+ *   history row i:  O_i = (1/max_len) * sum_{key j <= m+i} SiLU(q_i . k_j) v_j
+ *   candidate r:    O_r = (1/max_len) * (sum_{all m+n history keys j} SiLU(q_r . k_j) v_j
+ *                                        + SiLU(q_r . k_r) v_r)
+ *        (per head h: the columns [h*dh, (h+1)*dh), dh = D / heads)
+ *   X_{l+1} = X_l + [U | O | U*O] W2_l
+ * The new history rows' K, V (after bias) are appended to the cache.
+ *
+ * bfloat16 mode: storage is bfloat16, accumulation float32; results are rounded
+ * to bfloat16 (nearest, ties to even) at U,V,Q,K; at each attention weight
+ * SiLU(q.k); at each attention output; at the gate U*O; and at X + Z.
+ * float32 mode: float32 storage and arithmetic throughout.
+ *
+ * Conventions for every entry point:
+ *  - Host pointers are read during the call only. Device pointers must stay valid
+ *    until the work enqueued on `stream` has completed.
+ *  - Nothing is allocated on the device by the library; scratch memory is the
+ *    caller's workspace. The library keeps a small pinned host staging ring per
+ *    device (allocated on first use, grown when a larger plan is needed) from which
+ *    the per-call work plan is copied into the workspace.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null
+ *    stream). There is no device synchronisation inside a call.
+ *  - Every argument is validated on the host before anything is enqueued. On a
+ *    validation error nothing is launched and no host array is modified.
+ *  - Calls may run concurrently from several host threads if each uses its own
+ *    workspace, outputs and cache slots.
+ *  - Inputs, outputs, workspace and cache must not overlap.
+ */
+#ifndef HSTU_H_
+#define HSTU_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HSTU_ABI_VERSION 1
+
+/* Element type of every device tensor of a call. */
+enum hstu_dtype { HSTU_F32 = 0, HSTU_BF16 = 1 };
+
+/* Status codes. No exception or abort ever crosses the ABI. */
+enum hstu_status_code {
+  HSTU_OK = 0,
+  HSTU_ERR_NULL = 1,       /* a required pointer is NULL                                  */
+  HSTU_ERR_SHAPE = 2,      /* unsupported dims/dtype (see hstu_dims), B < 0                */
+  HSTU_ERR_OFFSETS = 3,    /* offsets do not start at 0 or decrease                        */
+  HSTU_ERR_CAPACITY = 4,   /* m+n >= max_len, cache capacity < m+n, bad or repeated slot,   */
+                           /* or cached_len < 0                                             */
+  HSTU_ERR_WORKSPACE = 5,  /* workspace NULL or smaller than hstu_workspace_size()          */
+  HSTU_ERR_HIP = 6,        /* a HIP runtime call failed; outputs and cache are undefined    */
+  HSTU_ERR_ALIGN = 7       /* a device pointer is not 16-byte aligned                       */
+};
+typedef int32_t hstu_status;
+
+/* Model dimensions, fixed for a model.
+ *  layers  >= 1
+ *  d_model  D; heads H with dh = D / H.
+ *           float32:  D % 64 == 0 and dh in {32, 64, 128}
+ *           bfloat16: D % 128 == 0 and dh in {64, 128}
+ *  max_len  rows of each position-bias table; every user needs m + n + 1 <= max_len
+ *           (history positions 0..m+n-1 plus the candidate slot m+n). The attention
+ *           scale is 1/max_len.
+ *  dtype    enum hstu_dtype. */
+typedef struct hstu_dims {
+  int32_t layers;
+  int32_t d_model;
+  int32_t heads;
+  int32_t max_len;
+  int32_t dtype;
+} hstu_dims;
+
+/* One layer's parameters: device pointers, row-major, in the call's dtype.
+ *  w_uvqk   [4D][D]: output feature j of the projection in row j (the transpose of
+ *           the math-layout W1 [D][4D]); row blocks U, V, Q, K.
+ *  w_out    [D][3D]: output feature j of the output GEMM in row j (the transpose of
+ *           W2 [3D][D]); column blocks U, O, U*O.
+ *  pos_bias [max_len][3D]: row p is the bias of position p; column blocks V, Q, K. */
+typedef struct hstu_layer_weights {
+  const void* w_uvqk;
+  const void* w_out;
+  const void* pos_bias;
+} hstu_layer_weights;
+
+/* Streaming key/value cache (caller-owned).
+ *  k, v          device, each [layers][slots][capacity][D] in the call's dtype. Rows
+ *                0..cached_len[b]-1 of slot slot_of_user[b] hold user b's earlier
+ *                history keys / values (after position bias), in position order.
+ *  slot_of_user  host [B]; distinct slots in [0, slots).
+ *  cached_len    host [B], in/out: m_b on entry; m_b + n_b after a successful call.
+ * The call reads rows 0..m_b-1 and writes rows m_b..m_b+n_b-1 of each layer.
+ * Candidates are never appended. */
+typedef struct hstu_kv_cache {
+  void* k;
+  void* v;
+  int32_t slots;
+  int32_t capacity;
+  const int32_t* slot_of_user;
+  int32_t* cached_len;
+} hstu_kv_cache;
+
+/* HSTU_ABI_VERSION of the loaded library. */
+int32_t hstu_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* hstu_status_string(hstu_status s);
+
+/* Bytes of device workspace hstu_encode needs for this batch (host-only; launches
+ * nothing). uih_offsets / cand_offsets: host int32 [B+1], starting at 0,
+ * non-decreasing; user b owns history rows uih_offsets[b]..uih_offsets[b+1]-1 and
+ * candidate rows cand_offsets[b]..cand_offsets[b+1]-1. */
+hstu_status hstu_workspace_size(const hstu_dims* d, int32_t B, const int32_t* uih_offsets,
+                                 const int32_t* cand_offsets, size_t* bytes);
+
+/* Work of one hstu_encode call (host-only integer arithmetic).
+ *  algorithmic_flops: 2 x the multiply-adds the method needs over all layers: both
+ *    GEMMs for every new history row and candidate, q.k and a*v for every masked pair
+ *    (history row i of user b sees m_b+i+1 keys; a candidate sees m_b+n_b keys plus
+ *    itself). Per layer and user: 14*(n+c)*D^2 + 4*D*(n*m + n(n+1)/2 + c*(m+n+1)).
+ *  formula_flops: the benchmark page's expression
+ *    2*layers*(N*N*D/2 + N*D*D*4 + N*D*D*3) with N = m+n, summed over users.
+ * cached_len may be NULL (all m = 0). Either output pointer may be NULL. */
+hstu_status hstu_flops(const hstu_dims* d, int32_t B, const int32_t* uih_offsets,
+                       const int32_t* cand_offsets, const int32_t* cached_len,
+                       uint64_t* algorithmic_flops, uint64_t* formula_flops);
+
+/* Encode one jagged batch through all layers.
+ *  uih        device [uih_offsets[B]][D]   new history tokens of every user
+ *  cand       device [cand_offsets[B]][D]  candidate tokens
+ *  w          host array of d->layers entries (device pointers inside)
+ *  kv         NULL (no earlier history: m_b = 0, nothing appended) or a cache
+ *  uih_out    device [uih_offsets[B]][D]   final-layer rows of the new history tokens
+ *  cand_out   device [cand_offsets[B]][D]  final-layer rows of the candidates
+ *  workspace  device, >= hstu_workspace_size() bytes, 256-byte aligned
+ * Users with n_b = 0 and/or c_b = 0, and B = 0, are valid. Device pointers must be
+ * 16-byte aligned. On HSTU_OK, kv->cached_len[b] has been advanced by n_b. */
+hstu_status hstu_encode(const hstu_dims* d, int32_t B, const int32_t* uih_offsets,
+                        const int32_t* cand_offsets, const void* uih, const void* cand,
+                        const hstu_layer_weights* w, hstu_kv_cache* kv, void* uih_out,
+                        void* cand_out, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSTU_H_ */

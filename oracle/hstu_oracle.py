@@ -129,21 +129,25 @@ def user_positions(m: int, n: int, c: int) -> Tuple[np.ndarray, np.ndarray]:
 
 def attention_user(q_u, k_all, v_all, q_c, k_c, v_c, *, m: int, heads: int, inv: float,
                    bf16: bool, counter: Optional[MacCounter] = None,
-                   uih_rows: Optional[Sequence[int]] = None, block: int = 256):
+                   uih_rows: Optional[Sequence[int]] = None,
+                   cand_rows: Optional[Sequence[int]] = None, block: int = 256):
     """Target-aware causal SiLU attention for one user.
 
     q_u [n, D]: new history queries (row i at position m+i); k_all, v_all [m+n, D]:
     every history key/value, row j at position j; q_c, k_c, v_c [c, D]: candidates.
     History row i: O_i = inv * sum_{j <= m+i} SiLU(q_i.k_j) v_j.
     Candidate r:   O_r = inv * (sum_{all j} SiLU(q_r.k_j) v_j + SiLU(q_r.k_r) v_r).
-    Per head h the columns [h*dh, (h+1)*dh) are used. ``uih_rows`` restricts the
-    history outputs to the listed rows (the result then has len(uih_rows) rows).
+    Per head h the columns [h*dh, (h+1)*dh) are used. ``uih_rows`` / ``cand_rows``
+    restrict the outputs to the listed rows (the results then have that many rows).
     Returns (O_u, O_c).
     """
     n, D = q_u.shape
-    c = q_c.shape[0]
     dh = D // heads
     rows = np.arange(n) if uih_rows is None else np.asarray(uih_rows, dtype=np.int64)
+    if cand_rows is not None:
+        sel = np.asarray(cand_rows, dtype=np.int64)
+        q_c, k_c, v_c = q_c[sel], k_c[sel], v_c[sel]
+    c = q_c.shape[0]
     R = round_bf16 if bf16 else (lambda a: a)
     o_u = np.zeros((rows.shape[0], D))
     o_c = np.zeros((c, D))
@@ -201,13 +205,15 @@ def _output(x, u, o, w2, bf16, counter):
 
 def layer_user(x_u, x_c, w1, w2, pos_table, *, k_cached, v_cached, heads: int, max_len: int,
                bf16: bool, counter: Optional[MacCounter] = None,
-               uih_rows: Optional[Sequence[int]] = None):
+               uih_rows: Optional[Sequence[int]] = None,
+               cand_rows: Optional[Sequence[int]] = None):
     """One encoder layer for one user.
 
     x_u [n, D] new history tokens, x_c [c, D] candidates, k_cached/v_cached [m, D]
     the user's cached keys/values for this layer. History and candidate rows go
     through separate products, so history results never depend on the candidates.
-    Returns (x_u', x_c', k_new, v_new); with ``uih_rows`` x_u' holds only those rows.
+    Returns (x_u', x_c', k_new, v_new); with ``uih_rows`` / ``cand_rows`` x_u' / x_c'
+    hold only those rows (every history row is still projected: all are keys).
     """
     m = k_cached.shape[0]
     n, c = x_u.shape[0], x_c.shape[0]
@@ -215,6 +221,9 @@ def layer_user(x_u, x_c, w1, w2, pos_table, *, k_cached, v_cached, heads: int, m
         raise ValueError("history plus candidate slot exceeds the position table")
     pos_u, pos_c = user_positions(m, n, c)
     u_u, v_u, q_u, k_u = _project(x_u, w1, pos_table, pos_u, bf16, counter)
+    if cand_rows is not None:
+        x_c = x_c[np.asarray(cand_rows, dtype=np.int64)]
+        pos_c = pos_c[:x_c.shape[0]]
     u_c, v_c, q_c, k_c = _project(x_c, w1, pos_table, pos_c, bf16, counter)
     k_all = np.concatenate([k_cached, k_u], axis=0)
     v_all = np.concatenate([v_cached, v_u], axis=0)

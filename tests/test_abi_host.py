@@ -1,0 +1,208 @@
+"""Host-side tests of the C ABI: the library loads and exports what include/hstu.h declares,
+validation rejects bad arguments before anything touches a GPU, and the host FLOP counter
+equals the oracle's live counter. Nothing here launches a kernel."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import hstu_silu_attention_amd as hsa
+import oracle
+from oracle.hstu_oracle import count_macs
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hstu.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_OFFSETS, ERR_CAPACITY, ERR_WORKSPACE, ERR_HIP, ERR_ALIGN = range(8)
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:hstu_status|int32_t|const char\*)\s+(hstu_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = hsa.load_library()
+    names = header_functions()
+    assert set(names) == {"hstu_abi_version", "hstu_status_string", "hstu_workspace_size", "hstu_flops",
+                          "hstu_encode"} | set(names)
+    for name in names:
+        assert hasattr(lib, name), name
+    version = int(re.search(r"#define HSTU_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert hsa.hstu_abi_version() == version
+
+
+def test_status_strings():
+    seen = set()
+    for s in range(8):
+        msg = hsa.hstu_status_string(s)
+        assert msg and msg not in seen
+        seen.add(msg)
+    assert hsa.hstu_status_string(99) == "unknown status"
+
+
+def dims(L=2, D=256, H=4, max_len=64, dtype=hsa.HSTU_BF16):
+    return hsa.HstuDims(L, D, H, max_len, dtype)
+
+
+@pytest.mark.parametrize("d,want", [
+    (dims(), OK),
+    (dims(D=256, H=8), ERR_SHAPE),               # dh = 32 not supported in bf16
+    (dims(D=192, H=3), ERR_SHAPE),               # D % 128
+    (dims(D=256, H=3), ERR_SHAPE),               # D % H
+    (dims(dtype=2), ERR_SHAPE),
+    (dims(L=0), ERR_SHAPE),
+    (dims(max_len=0), ERR_SHAPE),
+    (dims(D=64, H=2, dtype=hsa.HSTU_F32), OK),   # fp32, dh = 32
+    (dims(D=96, H=3, dtype=hsa.HSTU_F32), ERR_SHAPE),
+    (dims(D=512, H=2, dtype=hsa.HSTU_F32), ERR_SHAPE),   # dh = 256
+])
+def test_workspace_size_dims(d, want):
+    st, _ = hsa.hstu_workspace_size(d, 1, [0, 5], [0, 3])
+    assert st == want
+
+
+def test_workspace_size_offsets_and_growth():
+    d = dims()
+    assert hsa.hstu_workspace_size(d, 2, [1, 5, 6], [0, 0, 0])[0] == ERR_OFFSETS
+    assert hsa.hstu_workspace_size(d, 2, [0, 5, 4], [0, 0, 0])[0] == ERR_OFFSETS
+    assert hsa.hstu_workspace_size(d, 2, [0, 5, 6], [0, 2, 1])[0] == ERR_OFFSETS
+    assert hsa.hstu_workspace_size(d, -1, None, None)[0] == ERR_SHAPE
+    assert hsa.hstu_workspace_size(d, 0, None, None) == (OK, 0)
+    assert hsa.hstu_workspace_size(d, 2, [0, 0, 0], [0, 0, 0]) == (OK, 0)
+    _, small = hsa.hstu_workspace_size(d, 2, [0, 5, 6], [0, 2, 3])
+    _, big = hsa.hstu_workspace_size(d, 2, [0, 500, 600], [0, 2, 3])
+    assert 0 < small < big
+    # at least the [T][4D] projection, [T][D] attention output and [T][D] layer buffer
+    T = 603
+    assert big >= T * 6 * 256 * 2
+
+
+def test_workspace_size_page_offsets_example():
+    """The jagged example's offsets (10 users, one of them empty) are a valid batch."""
+    lengths = [1, 1, 1, 1, 1, 2, 3, 2, 2, 0]
+    offs = oracle.jagged_offsets(lengths).tolist()
+    st, nbytes = hsa.hstu_workspace_size(dims(), 10, offs, offs)
+    assert st == OK and nbytes > 0
+
+
+# ------------------------------------------------------------------------------ FLOP counter
+
+@pytest.mark.parametrize("uih,cand,cached", [([10, 17], [0, 0], None), ([5, 0, 3], [3, 4, 0], [6, 2, 0])])
+def test_flops_equal_oracle_counter(uih, cand, cached):
+    D, H, L = 64, 2, 2
+    wl = workloads.make_custom(seed=61, dtype="f32", layers=L, d_model=D, heads=H, max_len=64,
+                               uih_lengths=uih, cand_lengths=cand, cached_lengths=cached)
+    cache = None
+    if cached is not None:
+        cap = 16
+        cache = oracle.OracleCache(np.zeros((L, len(uih), cap, D)), np.zeros((L, len(uih), cap, D)),
+                                   np.arange(len(uih)), np.array(cached))
+    cnt = oracle.MacCounter()
+    oracle.encode(wl.uih, workloads.lengths_to_offsets(uih), wl.cand, workloads.lengths_to_offsets(cand),
+                  wl.params, heads=H, max_len=64, mode="f64", cache=cache, counter=cnt)
+    st, alg, form = hsa.hstu_flops(hsa.HstuDims(L, D, H, 64, hsa.HSTU_F32), len(uih),
+                                   workloads.lengths_to_offsets(uih), workloads.lengths_to_offsets(cand),
+                                   cached)
+    assert st == OK
+    assert alg == cnt.algorithmic_flops()
+    ms = cached or [0] * len(uih)
+    assert form == sum(2 * L * ((m + n) ** 2 * D // 2 + (m + n) * D * D * 7) for n, m in zip(uih, ms))
+
+
+@pytest.mark.parametrize("name", ["d256_uih1k_c64", "d512_uih2k_c2k", "stream_3000p300_c2k", "long_uih16k_c2k"])
+def test_flops_of_workloads_equal_enumeration(name):
+    spec = workloads.WORKLOADS[name]
+    rng = np.random.default_rng(0)
+    B = spec.users
+    uih = rng.integers(1, 2000, B)
+    cand = np.full(B, spec.cands)
+    cached = np.full(B, spec.cached)
+    st, alg, _ = hsa.hstu_flops(hsa.HstuDims(spec.layers, spec.d_model, spec.heads, spec.max_len,
+                                             hsa.HSTU_BF16), B, workloads.lengths_to_offsets(uih),
+                                workloads.lengths_to_offsets(cand), cached)
+    want = sum(2 * sum(count_macs(spec.d_model, spec.layers, int(n), int(c), int(m)).values())
+               for n, c, m in zip(uih, cand, cached))
+    assert st == OK and alg == want
+
+
+# ------------------------------------------------------------------------------ encode validation
+
+class FakeArgs:
+    """Arguments whose device pointers are never dereferenced: every case below must be rejected
+    on the host before any HIP call (this container has no GPU)."""
+
+    def __init__(self, L=2, D=256, H=4, max_len=64, uih=(5, 3), cand=(2, 0)):
+        self.d = dims(L, D, H, max_len)
+        self.B = len(uih)
+        self.uo = workloads.lengths_to_offsets(uih)
+        self.co = workloads.lengths_to_offsets(cand)
+        self.w = [hsa.HstuLayerWeights(0x10000, 0x20000, 0x30000) for _ in range(L)]
+        self.ptrs = dict(uih=0x40000, cand=0x50000, uih_out=0x60000, cand_out=0x70000, ws=0x100000)
+        st, self.ws_bytes = hsa.hstu_workspace_size(self.d, self.B, self.uo, self.co)
+        assert st == OK
+
+    def call(self, kv=None, ws_bytes=None, **over):
+        p = dict(self.ptrs, **over)
+        return hsa.hstu_encode(self.d, self.B, self.uo, self.co, p["uih"], p["cand"], self.w, kv,
+                               p["uih_out"], p["cand_out"], p["ws"],
+                               self.ws_bytes if ws_bytes is None else ws_bytes, 0)
+
+
+def fake_cache(cached, slots=4, capacity=32, slot_of_user=None):
+    sl = np.ascontiguousarray(slot_of_user if slot_of_user is not None else np.arange(len(cached)),
+                              dtype=np.int32)
+    cl = np.ascontiguousarray(cached, dtype=np.int32)
+    kv = hsa.HstuKvCache(0x200000, 0x300000, slots, capacity,
+                         sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                         cl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+    return kv, sl, cl
+
+
+def test_encode_rejects_before_launch():
+    a = FakeArgs()
+    assert a.call(ws_bytes=a.ws_bytes - 1) == ERR_WORKSPACE
+    assert a.call(ws=0) == ERR_WORKSPACE
+    assert a.call(ws=0x100010) == ERR_ALIGN            # workspace must be 256-byte aligned
+    assert a.call(uih=0) == ERR_NULL
+    assert a.call(cand_out=0) == ERR_NULL
+    assert a.call(uih=0x40008) == ERR_ALIGN
+    a.w[1] = hsa.HstuLayerWeights(0x10000, 0, 0x30000)
+    assert a.call() == ERR_NULL
+    a.w[1] = hsa.HstuLayerWeights(0x10000, 0x20004, 0x30000)
+    assert a.call() == ERR_ALIGN
+
+
+def test_encode_capacity_and_slots_leave_cached_len_unchanged():
+    a = FakeArgs(max_len=64, uih=(5, 3), cand=(2, 0))
+    # m + n + 1 must fit the position table: 58 + 5 + 1 = 64 fits, 59 does not
+    kv, sl, cl = fake_cache([59, 0])
+    assert a.call(kv=kv) == ERR_CAPACITY and cl.tolist() == [59, 0]
+    kv, sl, cl = fake_cache([20, 30], capacity=32)          # 30 + 3 > capacity 32
+    assert a.call(kv=kv) == ERR_CAPACITY and cl.tolist() == [20, 30]
+    kv, sl, cl = fake_cache([1, 1], slot_of_user=[2, 2])    # one slot for two users
+    assert a.call(kv=kv) == ERR_CAPACITY and cl.tolist() == [1, 1]
+    kv, sl, cl = fake_cache([1, 1], slots=2, slot_of_user=[0, 2])
+    assert a.call(kv=kv) == ERR_CAPACITY
+    kv, sl, cl = fake_cache([-1, 1])
+    assert a.call(kv=kv) == ERR_CAPACITY
+    kv, sl, cl = fake_cache([0, 0])
+    kv.k = 0
+    assert a.call(kv=kv) == ERR_NULL
+    # without a cache, n + 1 must fit max_len
+    b = FakeArgs(max_len=6, uih=(5, 6), cand=(1, 1))
+    assert b.call() == ERR_CAPACITY
+
+
+def test_encode_empty_batches_are_ok_without_device_work():
+    d = dims()
+    assert hsa.hstu_encode(d, 0, None, None, 0, 0, [hsa.HstuLayerWeights(1, 1, 1)] * 2, None,
+                           0, 0, 0, 0, 0) == OK
+    a = FakeArgs(uih=(0, 0), cand=(0, 0))
+    kv, sl, cl = fake_cache([3, 4])
+    assert a.call(kv=kv, ws=0, ws_bytes=0) == OK and cl.tolist() == [3, 4]
+    a = FakeArgs()
+    assert hsa.hstu_encode(a.d, a.B, [0, 5, 4], a.co, 1, 1, a.w, None, 1, 1, 1, 1, 0) == ERR_OFFSETS
