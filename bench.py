@@ -1,0 +1,203 @@
+"""Throughput benchmark of the jagged HSTU encoder on one MI355X.
+
+One step = one hstu_encode call over the whole batch through every layer (row
+statistics, uvqk projection, target-aware SiLU attention, gated output GEMM), on
+seeded synthetic inputs already resident in HBM. The default workload is
+"d512_uih2k_c2k": 16 users, UIH lengths lognormal (median 2000, sigma 0.5, clipped
+to [512, 4096]), 2048 candidates per user, D=512, 4 heads, 8 layers, bfloat16.
+
+Prints one JSON line: algorithmic TFLOP/s of the whole job (``value``), users/s, the
+fraction of the bf16 MFMA peak, per-kernel device times (HIP events recorded by the
+library on the launch stream), the roofline of the dominant kernel and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import hstu_silu_attention_amd as hsa  # noqa: E402
+import workloads  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = {
+    "attention": "hstu_silu_attention_amd/csrc/kernels_bf16.hip",
+    "uvqk": "hstu_silu_attention_amd/csrc/kernels_bf16.hip",
+    "out": "hstu_silu_attention_amd/csrc/kernels_bf16.hip",
+}
+
+
+def kernel_flops_per_launch(wl) -> dict:
+    """Algorithmic flops of one launch (one layer) of each kernel, from the lengths."""
+    D = wl.d_model
+    n = wl.uih_lengths.astype(np.int64)
+    c = wl.cand_lengths.astype(np.int64)
+    m = np.zeros_like(n) if wl.cached_lengths is None else wl.cached_lengths.astype(np.int64)
+    T = int((n + c).sum())
+    pairs = int((n * m + n * (n + 1) // 2 + c * (m + n + 1)).sum())
+    return {"uvqk": 2 * T * D * 4 * D, "attention": 4 * D * pairs, "out": 2 * T * 3 * D * D,
+            "norm": 0, "plan": 0}
+
+
+def source_hash(path: str) -> str:
+    with open(os.path.join(ROOT, path), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
+    on the kernel source as it is now (its hash matches); otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, max_users: int = 1):
+    """The CPU oracle (as it stands) on a bounded sample: the median-length user of the
+    same workload through every layer in bf16-mirror mode; scaled to TFLOP/s by the
+    sample's algorithmic flops."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    order = np.argsort(wl.uih_lengths)
+    b = int(order[len(order) // 2])
+    uo = workloads.lengths_to_offsets(wl.uih_lengths)
+    co = workloads.lengths_to_offsets(wl.cand_lengths)
+    t0 = time.perf_counter()
+    oracle.encode(wl.uih, uo, wl.cand, co, wl.params, heads=wl.heads, max_len=wl.max_len,
+                  mode="bf16" if wl.dtype == "bf16" else "f64", users=[b])
+    dt = time.perf_counter() - t0
+    n, c = int(wl.uih_lengths[b]), int(wl.cand_lengths[b])
+    D, L = wl.d_model, wl.layers
+    flops = L * (14 * (n + c) * D * D + 4 * D * (n * (n + 1) // 2 + c * (n + 1)))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"user {b} of {wl.users} (UIH {n}, {c} candidates), all {L} layers, "
+                      f"float64 with bf16-mirror rounding; {dt:.1f} s; "
+                      f"{1.0 / dt:.4f} users/s on this host"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="d512_uih2k_c2k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); users are "
+              f"independent, so N GPUs would each run this one-GPU workload on their own users.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    hsa.load_library()
+    dev = torch.device("cuda:0")
+    wl = workloads.make_workload(args.workload)
+    if wl.dtype != "bf16" or wl.cached_lengths.any():
+        print("bench.py times the bf16 workloads without a cached prefix", file=sys.stderr)
+        sys.exit(1)
+    model = hsa.Model(wl.params, d_model=wl.d_model, heads=wl.heads, max_len=wl.max_len,
+                      dtype=wl.dtype, device=dev)
+    uih = torch.from_numpy(wl.uih).to(device=dev, dtype=torch.bfloat16)
+    cand = torch.from_numpy(wl.cand).to(device=dev, dtype=torch.bfloat16)
+    uo = workloads.lengths_to_offsets(wl.uih_lengths)
+    co = workloads.lengths_to_offsets(wl.cand_lengths)
+    out = (torch.empty_like(uih), torch.empty_like(cand))
+    ws = torch.empty(hsa.workspace_bytes(model, uo, co), dtype=torch.uint8, device=dev)
+    st, alg_flops, formula_flops = hsa.hstu_flops(model.dims(), wl.users, uo, co, None)
+    assert st == 0
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def step():
+        hsa.encode(model, uih, uo, cand, co, out=out, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    hsa.hstu_timing_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    hsa.hstu_timing_enable(False)
+    st, ktimes = hsa.hstu_timing_read()
+    assert st == 0
+    finite = bool(torch.isfinite(out[0].float()).all().item() and torch.isfinite(out[1].float()).all().item())
+
+    sec = (t1 - t0) / args.steps
+    tflops = alg_flops / sec / 1e12
+    per_launch = kernel_flops_per_launch(wl)
+    kernels = {k: {"avg_ms": (ms / n if n else 0.0), "launches": n, "share": ms / max(sum(v[0] for v in ktimes.values()), 1e-12)}
+               for k, (ms, n) in ktimes.items()}
+    dominant = max(("uvqk", "attention", "out"), key=lambda k: ktimes[k][0])
+    avg_s = kernels[dominant]["avg_ms"] / 1e3
+    achieved = per_launch[dominant] / avg_s / 1e12
+    for k in ("uvqk", "attention", "out"):
+        a_ms = kernels[k]["avg_ms"]
+        kernels[k]["tflops"] = per_launch[k] / (a_ms / 1e3) / 1e12 if a_ms else 0.0
+    traffic = read_traffic(dominant, args.workload)
+    result = {
+        "metric": "HSTU encoder TFLOP/s (% bf16 MFMA peak) + users/s, D=512 UIH~2K, 2K cands",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded: lognormal UIH lengths, N(0,1) tokens, N(0,1/D) weights, "
+                "N(0,0.02) position bias)",
+        "config": {"workload": args.workload, "users": wl.users, "layers": wl.layers,
+                   "d_model": wl.d_model, "heads": wl.heads, "cands_per_user": int(wl.cand_lengths[0]),
+                   "uih_mean": float(wl.uih_lengths.mean()), "rows": int(wl.uih_lengths.sum() + wl.cand_lengths.sum())},
+        "users_per_s": round(wl.users / sec, 2),
+        "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "formula_tflops": round(formula_flops / sec / 1e12, 3),
+        "algorithmic_tflop_per_step": alg_flops / 1e12,
+        "outputs_finite": finite,
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in kernels.items()},
+        "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl)
+        result["cpu_baseline"]["value"] = round(result["cpu_baseline"]["value"], 6)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -18,13 +18,12 @@ import numpy as np
 
 __all__ = ["HSTU_F32", "HSTU_BF16", "HstuError", "load_library", "library_path",
            "hstu_abi_version", "hstu_status_string", "hstu_workspace_size", "hstu_flops",
-           "hstu_encode", "Model", "KVCache", "encode", "HstuDims", "HstuLayerWeights",
+           "hstu_encode", "hstu_timing_enable", "hstu_timing_read", "KERNEL_KINDS", "Model", "KVCache", "encode", "HstuDims", "HstuLayerWeights",
            "HstuKvCache"]
 
 HSTU_F32, HSTU_BF16 = 0, 1
 HSTU_OK = 0
-_EXPORTS = ["hstu_abi_version", "hstu_status_string", "hstu_workspace_size", "hstu_flops",
-            "hstu_encode"]
+KERNEL_KINDS = ("plan", "uvqk", "attention", "out", "norm")
 
 
 class HstuDims(ctypes.Structure):
@@ -75,6 +74,10 @@ def load_library() -> ctypes.CDLL:
     lib.hstu_flops.restype = ctypes.c_int32
     lib.hstu_flops.argtypes = [P(HstuDims), ctypes.c_int32, i32p, i32p, i32p, P(ctypes.c_uint64),
                                P(ctypes.c_uint64)]
+    lib.hstu_timing_enable.restype = ctypes.c_int32
+    lib.hstu_timing_enable.argtypes = [ctypes.c_int32]
+    lib.hstu_timing_read.restype = ctypes.c_int32
+    lib.hstu_timing_read.argtypes = [P(ctypes.c_double), P(ctypes.c_int64), ctypes.c_int32]
     lib.hstu_encode.restype = ctypes.c_int32
     lib.hstu_encode.argtypes = [P(HstuDims), ctypes.c_int32, i32p, i32p, ctypes.c_void_p, ctypes.c_void_p,
                                 P(HstuLayerWeights), P(HstuKvCache), ctypes.c_void_p, ctypes.c_void_p,
@@ -131,6 +134,19 @@ def hstu_encode(dims: HstuDims, B: int, uih_offsets, cand_offsets, uih_ptr: int,
     return int(load_library().hstu_encode(ctypes.byref(dims), B, uo, co, uih_ptr, cand_ptr, warr,
                                           ctypes.byref(kv) if kv is not None else None,
                                           uih_out_ptr, cand_out_ptr, workspace_ptr, workspace_bytes, stream))
+
+
+def hstu_timing_enable(enable: bool) -> int:
+    return int(load_library().hstu_timing_enable(1 if enable else 0))
+
+
+def hstu_timing_read():
+    """Returns (status, {kind: (total_ms, launches)}) for the kinds in KERNEL_KINDS."""
+    n = len(KERNEL_KINDS)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    st = int(load_library().hstu_timing_read(ms, cnt, n))
+    return st, {k: (float(ms[i]), int(cnt[i])) for i, k in enumerate(KERNEL_KINDS)}
 
 
 # ---------------------------------------------------------------------------- torch helpers

@@ -54,7 +54,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 struct Layout {
   int32_t Nu = 0, Nc = 0, T = 0;
   int64_t ntiles = 0;
-  size_t users = 0, tiles = 0, rows = 0, uvqk = 0, o = 0, x = 0, total = 0;
+  size_t users = 0, tiles = 0, rows = 0, stats = 0, uvqk = 0, o = 0, x = 0, total = 0;
   size_t staged = 0;  // bytes copied from the host: users table + tile list
 };
 
@@ -75,6 +75,7 @@ Layout make_layout(const hstu_dims* d, int32_t B, const int32_t* uo, const int32
   L.tiles = off; off += align_up((size_t)L.ntiles * 16);
   L.staged = off;
   L.rows = off; off += align_up(T * 8);
+  L.stats = off; off += align_up(T * 8);
   L.uvqk = off; off += align_up(T * 4 * D * es);
   L.o = off; off += align_up(T * D * es);
   L.x = off; off += d->layers > 1 ? align_up(T * D * es) : 0;
@@ -131,9 +132,95 @@ hstu_status stage_and_copy(const void* src, size_t bytes, void* dst, hipStream_t
   return HSTU_OK;
 }
 
+// ---------------------------------------------------------------- per-kernel timing
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  struct Rec { int kind; hipEvent_t a, b; };
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> pool;
+  double ms[HSTU_KERNEL_KINDS] = {};
+  int64_t n[HSTU_KERNEL_KINDS] = {};
+};
+Timing g_timing;
+
+hipEvent_t timing_event() {
+  if (!g_timing.pool.empty()) {
+    hipEvent_t e = g_timing.pool.back();
+    g_timing.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Launch through `f`, bracketed by events on `s` while timing is on.
+template <typename F>
+hipError_t timed_launch(int kind, hipStream_t s, F&& f) {
+  std::unique_lock<std::mutex> lock(g_timing.mu);
+  if (!g_timing.on) {
+    lock.unlock();
+    return f();
+  }
+  hipEvent_t a = timing_event(), b = timing_event();
+  if (!a || !b) return hipErrorOutOfMemory;
+  hipError_t e = hipEventRecord(a, s);
+  if (e != hipSuccess) return e;
+  e = f();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(b, s);
+  if (e != hipSuccess) return e;
+  g_timing.recs.push_back({kind, a, b});
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
+
+hstu_status hstu_timing_enable(int32_t enable) {
+  std::lock_guard<std::mutex> lock(g_timing.mu);
+  if (enable) {
+    for (auto& r : g_timing.recs) {
+      if (hipEventSynchronize(r.b) != hipSuccess) return HSTU_ERR_HIP;
+      g_timing.pool.push_back(r.a);
+      g_timing.pool.push_back(r.b);
+    }
+    g_timing.recs.clear();
+    for (int k = 0; k < HSTU_KERNEL_KINDS; ++k) {
+      g_timing.ms[k] = 0.0;
+      g_timing.n[k] = 0;
+    }
+  }
+  g_timing.on = enable != 0;
+  return HSTU_OK;
+}
+
+hstu_status hstu_timing_read(double* total_ms, int64_t* launches, int32_t kinds) {
+  if (!total_ms || !launches) return HSTU_ERR_NULL;
+  if (kinds < 0) return HSTU_ERR_SHAPE;
+  std::lock_guard<std::mutex> lock(g_timing.mu);
+  for (auto& r : g_timing.recs) {
+    if (hipEventSynchronize(r.b) != hipSuccess) return HSTU_ERR_HIP;
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return HSTU_ERR_HIP;
+    g_timing.ms[r.kind] += ms;
+    g_timing.n[r.kind] += 1;
+    g_timing.pool.push_back(r.a);
+    g_timing.pool.push_back(r.b);
+  }
+  g_timing.recs.clear();
+  for (int k = 0; k < kinds; ++k) {
+    total_ms[k] = k < HSTU_KERNEL_KINDS ? g_timing.ms[k] : 0.0;
+    launches[k] = k < HSTU_KERNEL_KINDS ? g_timing.n[k] : 0;
+  }
+  for (int k = 0; k < HSTU_KERNEL_KINDS; ++k) {
+    g_timing.ms[k] = 0.0;
+    g_timing.n[k] = 0;
+  }
+  return HSTU_OK;
+}
 
 int32_t hstu_abi_version(void) { return HSTU_ABI_VERSION; }
 
@@ -278,6 +365,7 @@ hstu_status hstu_encode(const hstu_dims* d, int32_t B, const int32_t* uih_offset
   const UserRec* d_users = reinterpret_cast<const UserRec*>(ws + lay.users);
   const int4* d_tiles = reinterpret_cast<const int4*>(ws + lay.tiles);
   int2* d_rows = reinterpret_cast<int2*>(ws + lay.rows);
+  float2* d_stats = reinterpret_cast<float2*>(ws + lay.stats);
   const size_t es = d->dtype == HSTU_F32 ? 4 : 2;
   char* uvqk = ws + lay.uvqk;
   char* obuf = ws + lay.o;
@@ -285,7 +373,8 @@ hstu_status hstu_encode(const hstu_dims* d, int32_t B, const int32_t* uih_offset
   const size_t nu_bytes = (size_t)lay.Nu * D * es;
 
   hstu::PlanArgs pa{d_users, B, lay.Nu, lay.T, d_rows};
-  if (hstu::launch_plan(pa, s) != hipSuccess) return HSTU_ERR_HIP;
+  if (timed_launch(HSTU_KERNEL_PLAN, s, [&] { return hstu::launch_plan(pa, s); }) != hipSuccess)
+    return HSTU_ERR_HIP;
 
   const int dh = D / d->heads;
   const size_t layer_cache = kv ? (size_t)kv->slots * kv->capacity * D * es : 0;
@@ -297,9 +386,13 @@ hstu_status hstu_encode(const hstu_dims* d, int32_t B, const int32_t* uih_offset
     void* ck = kv ? (void*)((char*)kv->k + l * layer_cache) : nullptr;
     void* cv = kv ? (void*)((char*)kv->v + l * layer_cache) : nullptr;
 
-    hstu::UvqkArgs ua{x_lo, x_hi, lay.Nu, lay.T, D, w[l].w_uvqk, w[l].pos_bias, d_rows, d_users,
+    hstu::StatsArgs sa{x_lo, x_hi, lay.Nu, lay.T, D, d_stats};
+    if (timed_launch(HSTU_KERNEL_NORM, s, [&] { return hstu::launch_stats(d->dtype, sa, s); }) != hipSuccess)
+      return HSTU_ERR_HIP;
+    hstu::UvqkArgs ua{x_lo, x_hi, lay.Nu, lay.T, D, d_stats, w[l].w_uvqk, w[l].pos_bias, d_rows, d_users,
                       uvqk, ck, cv};
-    if (hstu::launch_uvqk(d->dtype, ua, s) != hipSuccess) return HSTU_ERR_HIP;
+    if (timed_launch(HSTU_KERNEL_UVQK, s, [&] { return hstu::launch_uvqk(d->dtype, ua, s); }) != hipSuccess)
+      return HSTU_ERR_HIP;
 
     hstu::AttnArgs aa{};
     aa.tiles = d_tiles;
@@ -318,10 +411,13 @@ hstu_status hstu_encode(const hstu_dims* d, int32_t B, const int32_t* uih_offset
       aa.ld = 4 * (int64_t)D;
     }
     aa.o = obuf;
-    if (hstu::launch_attn(d->dtype, dh, aa, (int)lay.ntiles, s) != hipSuccess) return HSTU_ERR_HIP;
+    if (timed_launch(HSTU_KERNEL_ATTENTION, s,
+                     [&] { return hstu::launch_attn(d->dtype, dh, aa, (int)lay.ntiles, s); }) != hipSuccess)
+      return HSTU_ERR_HIP;
 
     hstu::OutArgs oa{uvqk, obuf, w[l].w_out, x_lo, x_hi, y_lo, y_hi, lay.Nu, lay.T, D};
-    if (hstu::launch_out(d->dtype, oa, s) != hipSuccess) return HSTU_ERR_HIP;
+    if (timed_launch(HSTU_KERNEL_OUT, s, [&] { return hstu::launch_out(d->dtype, oa, s); }) != hipSuccess)
+      return HSTU_ERR_HIP;
   }
   if (kv)
     for (int32_t b = 0; b < B; ++b) kv->cached_len[b] += uih_offsets[b + 1] - uih_offsets[b];

@@ -27,10 +27,21 @@ struct PlanArgs {
   int2* row_info;        // [T] {user, position}
 };
 
+// Per-row statistics of a layer input for its normalisation: {mean, 1/sqrt(var + eps)}.
+struct StatsArgs {
+  const void* x_lo;      // rows [0, Nu)
+  const void* x_hi;      // rows [Nu, T)
+  int32_t Nu, T, D;
+  float2* stats;         // [T] out
+};
+
+constexpr float kNormEps = 1e-6f;
+
 struct UvqkArgs {
   const void* x_lo;      // rows [0, Nu)
   const void* x_hi;      // rows [Nu, T)
   int32_t Nu, T, D;
+  const float2* stats;   // [T] {mean, rstd} of each input row
   const void* w;         // [4D][D]
   const void* pos;       // [max_len][3D]
   const int2* row_info;
@@ -67,6 +78,7 @@ struct OutArgs {
 int attn_block_rows(int dtype);
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+hipError_t launch_stats(int dtype, const StatsArgs& a, hipStream_t s);
 hipError_t launch_uvqk(int dtype, const UvqkArgs& a, hipStream_t s);
 hipError_t launch_attn(int dtype, int dh, const AttnArgs& a, int ntiles, hipStream_t s);
 hipError_t launch_out(int dtype, const OutArgs& a, hipStream_t s);

@@ -2,7 +2,7 @@
 // float32 accumulation, 64-wide wavefronts, LDS-staged tiles.
 //
 // Rounding to bfloat16 (hardware round-to-nearest-even conversion) happens exactly
-// at: U, V, Q, K after the position bias; each attention weight SiLU(q.k); each
+// at: the normalised layer input; U, V, Q, K after the position bias; each attention weight SiLU(q.k); each
 // attention output; the gate U*O; and X + Z.
 //
 // MFMA operand layout used throughout (32x32x16, wave64): for D = A*B + C with A
@@ -107,15 +107,24 @@ __device__ __forceinline__ void gemm_core(const ALoad& aload, const u16* __restr
   }
 }
 
-// A rows of the projection: the layer input, history rows then candidate rows.
+// A rows of the projection: the normalised layer input bf16((x - mean) * rstd),
+// history rows then candidate rows.
 struct XLoad {
   const u16* lo;
   const u16* hi;
+  const float2* stats;
   int Nu, T, D;
   __device__ __forceinline__ uint4 operator()(int row, int k) const {
     if (row >= T) return make_uint4(0, 0, 0, 0);
     const u16* p = row < Nu ? lo + (size_t)row * D : hi + (size_t)(row - Nu) * D;
-    return *reinterpret_cast<const uint4*>(p + k);
+    const uint4 v = *reinterpret_cast<const uint4*>(p + k);
+    const float2 st = stats[row];
+    uint4 r;
+    r.x = pack2((bf2f_lo(v.x) - st.x) * st.y, (bf2f_hi(v.x) - st.x) * st.y);
+    r.y = pack2((bf2f_lo(v.y) - st.x) * st.y, (bf2f_hi(v.y) - st.x) * st.y);
+    r.z = pack2((bf2f_lo(v.z) - st.x) * st.y, (bf2f_hi(v.z) - st.x) * st.y);
+    r.w = pack2((bf2f_lo(v.w) - st.x) * st.y, (bf2f_hi(v.w) - st.x) * st.y);
+    return r;
   }
 };
 
@@ -147,7 +156,7 @@ __global__ __launch_bounds__(256) void uvqk_kernel(UvqkArgs a) {
   const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
   const int row0 = (tile / ncol) * GM, col0 = (tile % ncol) * GN;
   f32x16 acc[2][2];
-  XLoad ld{(const u16*)a.x_lo, (const u16*)a.x_hi, a.Nu, a.T, D};
+  XLoad ld{(const u16*)a.x_lo, (const u16*)a.x_hi, a.stats, a.Nu, a.T, D};
   gemm_core(ld, (const u16*)a.w, D, row0, col0, acc, sm);
 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;

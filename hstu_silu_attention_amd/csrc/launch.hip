@@ -37,7 +37,48 @@ __global__ __launch_bounds__(256) void plan_rows_kernel(PlanArgs a) {
   a.row_info[r] = make_int2(lo, hist ? u.m + (key - u.uoff) : u.m + u.n);
 }
 
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+__device__ __forceinline__ float load_f(const float* p) { return *p; }
+__device__ __forceinline__ float load_f(const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
+
+// One wave per row: two passes over the row (mean, then the mean squared deviation),
+// each reduced across the wave in a fixed butterfly order, so a row's statistics
+// depend on that row alone.
+template <typename T>
+__global__ __launch_bounds__(256) void row_stats_kernel(StatsArgs a) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= a.T) return;
+  const int D = a.D;
+  const T* x = row < a.Nu ? (const T*)a.x_lo + (size_t)row * D : (const T*)a.x_hi + (size_t)(row - a.Nu) * D;
+  float s = 0.0f;
+  for (int k = lane; k < D; k += 64) s += load_f(x + k);
+  const float mean = wave_sum(s) / (float)D;
+  float q = 0.0f;
+  for (int k = lane; k < D; k += 64) {
+    const float d = load_f(x + k) - mean;
+    q += d * d;
+  }
+  const float var = wave_sum(q) / (float)D;
+  if (lane == 0) a.stats[row] = make_float2(mean, 1.0f / sqrtf(var + kNormEps));
+}
+
 }  // namespace
+
+hipError_t launch_stats(int dtype, const StatsArgs& a, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  const int blocks = (a.T + 3) / 4;
+  if (dtype == HSTU_F32)
+    row_stats_kernel<float><<<blocks, 256, 0, s>>>(a);
+  else
+    row_stats_kernel<uint16_t><<<blocks, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
 
 int attn_block_rows(int dtype) { return dtype == HSTU_F32 ? attn_block_rows_f32() : attn_block_rows_bf16(); }
 

@@ -16,7 +16,8 @@
  * sum of per-user lengths (TorchRec DLRM tutorial page, section 2.1).
  *
  * Per layer l, for user b with m cached, n new history rows and c candidates:
- *   S = SiLU(X W1_l) = [U | V | Q | K]           (each D wide)
+ *   Xn = (X - mean(X)) / sqrt(var(X) + 1e-6)     (per row over its D features)
+ *   S = SiLU(Xn W1_l) = [U | V | Q | K]          (each D wide)
  *   V += P_l[pos, 0:D]; Q += P_l[pos, D:2D]; K += P_l[pos, 2D:3D]
  *        new history row i has pos = m + i; every candidate has pos = m + n
  *   history row i:  O_i = (1/max_len) * sum_{key j <= m+i} SiLU(q_i . k_j) v_j
@@ -27,7 +28,7 @@
  * The new history rows' K, V (after bias) are appended to the cache.
  *
  * bfloat16 mode: storage is bfloat16, accumulation float32; results are rounded
- * to bfloat16 (nearest, ties to even) at U,V,Q,K; at each attention weight
+ * to bfloat16 (nearest, ties to even) at Xn; at U,V,Q,K; at each attention weight
  * SiLU(q.k); at each attention output; at the gate U*O; and at X + Z.
  * float32 mode: float32 storage and arithmetic throughout.
  *
@@ -160,6 +161,25 @@ hstu_status hstu_encode(const hstu_dims* d, int32_t B, const int32_t* uih_offset
                         const int32_t* cand_offsets, const void* uih, const void* cand,
                         const hstu_layer_weights* w, hstu_kv_cache* kv, void* uih_out,
                         void* cand_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Measurement aid: device time of each kernel that hstu_encode launches, taken with
+ * HIP events recorded on the caller's stream immediately before and after every
+ * launch while timing is enabled (calls on one device at a time).
+ *  hstu_timing_enable(1) discards earlier records and starts recording;
+ *  hstu_timing_enable(0) stops recording (records are kept).
+ *  hstu_timing_read waits for the recorded events, then writes, per kernel kind k <
+ *  kinds (enum hstu_kernel_kind), the summed milliseconds total_ms[k] and the number
+ *  of launches[k] recorded since enabling; it consumes the records. */
+enum hstu_kernel_kind {
+  HSTU_KERNEL_PLAN = 0,       /* jagged row planner                      */
+  HSTU_KERNEL_UVQK = 1,       /* projection GEMM + SiLU + bias + append  */
+  HSTU_KERNEL_ATTENTION = 2,  /* target-aware causal SiLU attention      */
+  HSTU_KERNEL_OUT = 3,        /* gated output GEMM + residual            */
+  HSTU_KERNEL_NORM = 4,       /* per-row statistics of the layer input   */
+  HSTU_KERNEL_KINDS = 5
+};
+hstu_status hstu_timing_enable(int32_t enable);
+hstu_status hstu_timing_read(double* total_ms, int64_t* launches, int32_t kinds);
 
 #ifdef __cplusplus
 }

@@ -4,7 +4,8 @@ Re-derives every output element of the layer stack with plain Python floats and
 explicit index loops, straight from the definition (the attention core
 Mask(SiLU(Q K^T)) V with absolute position bias on Q, K, V, from the DLRMv3
 benchmark review's "Model selection" section; the target-aware candidate mask;
-the D -> 4D projection and the 3D -> D output GEMM). It shares nothing with
+the per-row input normalisation, the D -> 4D projection and the 3D -> D output
+GEMM). It shares nothing with
 ``hstu_oracle`` (no NumPy arithmetic, its own bfloat16 rounding and SiLU), so the
 two pin each other: a dropped term, a wrong sign, a wrong index or a transposed
 operand in either one shows up as a mismatch.
@@ -15,6 +16,7 @@ import math
 from typing import List, Optional, Sequence
 
 _BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+_EPS = 1e-6
 
 
 def bf16_round(x: float) -> float:
@@ -69,10 +71,13 @@ def encode_brute(uih, uih_offsets, cand, cand_offsets, params, *, heads: int, ma
             posn = [m + i for i in range(n)] + [m + n] * c
             U, V, Q, K = _mat(n + c, D), _mat(n + c, D), _mat(n + c, D), _mat(n + c, D)
             for r in range(n + c):
+                mean = sum(xs[r]) / D
+                var = sum((t - mean) * (t - mean) for t in xs[r]) / D
+                xn = [rnd((t - mean) / math.sqrt(var + _EPS)) for t in xs[r]]
                 for j in range(4 * D):
                     g = 0.0
                     for k in range(D):
-                        g += xs[r][k] * w1[k][j]
+                        g += xn[k] * w1[k][j]
                     s = silu_scalar(g)
                     blk, col = divmod(j, D)
                     if blk == 0:

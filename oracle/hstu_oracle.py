@@ -18,8 +18,11 @@ lengths (the KeyedJaggedTensor example of the TorchRec DLRM tutorial page,
 section 2.1).
 
 Readings adopted where the pages are silent (each listed in the design notes):
-the 3*D*D GEMM consumes [U | O | U*O]; the residual is X + Z; no normalisation
-and no GEMM biases; SiLU on all four projection slices; one [max_len, 3D]
+the 3*D*D GEMM consumes [U | O | U*O]; the residual is X + Z; each layer
+normalises its input rows (zero mean, unit variance over D, eps 1e-6, no learned
+scale or shift) before the projection, which keeps the stacked blocks stable (the
+multi-stage page stresses stacking blocks with stable attention distributions;
+without it the configured 8- and 16-layer stacks overflow); no GEMM biases; SiLU on all four projection slices; one [max_len, 3D]
 position table per layer with column blocks V, Q, K, added after SiLU; every
 candidate sits at position m+n (the next-event slot); the scale 1/max_len is
 applied once to each attention output; the UIH mask is causal with the diagonal
@@ -27,8 +30,9 @@ included.
 
 Arithmetic is float64 throughout. ``mode="f64"`` applies no intermediate
 rounding. ``mode="bf16"`` mirrors a bfloat16 pipeline by rounding (to nearest,
-ties to even) at exactly these points: U, V, Q, K after bias; every attention
-weight SiLU(q.k); every attention output; the gate U*O; and X + Z.
+ties to even) at exactly these points: the normalised layer input; U, V, Q, K
+after bias; every attention weight SiLU(q.k); every attention output; the gate
+U*O; and X + Z.
 
 Parity pins for every function here live in tests/test_oracle_pins.py (brute
 force on tiny inputs, closed forms, invariants, the page's jagged example and
@@ -41,11 +45,12 @@ from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 
-__all__ = ["round_bf16", "silu", "jagged_offsets", "MacCounter", "OracleCache",
+__all__ = ["round_bf16", "silu", "normalize_rows", "NORM_EPS", "jagged_offsets", "MacCounter", "OracleCache",
            "encode", "layer_user", "attention_user", "user_positions", "count_macs"]
 
 _BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
 _BF16_MIN_QUANTUM_EXP = -133          # smallest bfloat16 subnormal is 2**-133
+NORM_EPS = 1e-6
 
 
 def round_bf16(x) -> np.ndarray:
@@ -71,6 +76,15 @@ def silu(x) -> np.ndarray:
     x = np.asarray(x, dtype=np.float64)
     with np.errstate(over="ignore"):
         return x / (1.0 + np.exp(-x))
+
+
+def normalize_rows(x) -> np.ndarray:
+    """Each row minus its mean, divided by sqrt(its variance + NORM_EPS) (population
+    variance over the row's D features); no learned scale or shift."""
+    x = np.asarray(x, dtype=np.float64)
+    mu = x.mean(axis=1, keepdims=True)
+    var = np.mean((x - mu) ** 2, axis=1, keepdims=True)
+    return (x - mu) / np.sqrt(var + NORM_EPS)
 
 
 def jagged_offsets(lengths) -> np.ndarray:
@@ -178,10 +192,10 @@ def attention_user(q_u, k_all, v_all, q_c, k_c, v_c, *, m: int, heads: int, inv:
 
 
 def _project(x, w1, pos_table, positions, bf16, counter):
-    """S = SiLU(X W1) split into U, V, Q, K; position bias on V, Q, K (not U)."""
+    """S = SiLU(norm(X) W1) split into U, V, Q, K; position bias on V, Q, K (not U)."""
     D = x.shape[1]
     R = round_bf16 if bf16 else (lambda a: a)
-    s = silu(x @ w1)
+    s = silu(R(normalize_rows(x)) @ w1)
     if counter is not None:
         counter.gemm_uvqk += x.shape[0] * D * 4 * D
     bias = pos_table[positions]

@@ -1,0 +1,127 @@
+"""GPU parity at the workloads' full sizes.
+
+The GPU always runs the whole batch in one hstu_encode call, as the benchmark does;
+the oracle recomputes what it can finish in seconds: whole users (users are
+independent, so a user's rows depend on that user alone), or, for the 16-layer long
+histories, single layers on sampled rows, fed with the GPU's own layer input."""
+import numpy as np
+import pytest
+
+import hstu_silu_attention_amd as hsa
+import oracle
+import workloads
+from gpu_util import (BF16_TOL, gpu_encode, make_model, normwise_per_user, oracle_encode, say,
+                      select_users, to_dev, to_np, torch_cuda)
+
+pytestmark = pytest.mark.gpu
+
+
+def compare_users(wl, gu, gc, users, cache=None, sub=None):
+    ru, rc, _ = oracle_encode(wl, "bf16", users=users)
+    worst = 0.0
+    for b in users:
+        eu = normwise_per_user(select_users(gu, wl.uih_lengths, [b]), select_users(ru, wl.uih_lengths, [b]),
+                               [wl.uih_lengths[b]])
+        ec = normwise_per_user(select_users(gc, wl.cand_lengths, [b]), select_users(rc, wl.cand_lengths, [b]),
+                               [wl.cand_lengths[b]])
+        say(f"  user {b} (UIH {wl.uih_lengths[b]}, {wl.cand_lengths[b]} cand): uih {eu:.3e} cand {ec:.3e}")
+        worst = max(worst, eu, ec)
+    assert worst <= BF16_TOL
+
+
+def test_headline_workload_sampled_users():
+    """D=512, UIH ~2K (lognormal), 2048 candidates, 8 layers, 16 users: the benchmark's inputs
+    and launch; the shortest and the median-length user are recomputed by the oracle."""
+    wl = workloads.make_workload("d512_uih2k_c2k")
+    gu, gc = gpu_encode(wl)
+    assert np.all(np.isfinite(gu)) and np.all(np.isfinite(gc))
+    order = np.argsort(wl.uih_lengths)
+    compare_users(wl, gu, gc, [int(order[0]), int(order[len(order) // 2])])
+
+
+def test_d256_workload_all_users():
+    """D=256, 4 layers, 32 users, UIH uniform [256, 1024], 64 candidates: every user checked."""
+    wl = workloads.make_workload("d256_uih1k_c64")
+    gu, gc = gpu_encode(wl)
+    ru, rc, _ = oracle_encode(wl, "bf16")
+    eu = normwise_per_user(gu, ru, wl.uih_lengths)
+    ec = normwise_per_user(gc, rc, wl.cand_lengths)
+    say(f"  d256 all users: uih {eu:.3e} cand {ec:.3e}")
+    assert eu <= BF16_TOL and ec <= BF16_TOL
+
+
+def test_streaming_workload_sampled_user():
+    """64 users, each with a 3000-event cached prefix (filled by hstu_encode with no
+    candidates), then 300 new events + 2048 candidates against the cache. One user is
+    recomputed by the oracle, prefix fill included, on a one-user batch."""
+    torch = torch_cuda()
+    wl = workloads.make_workload("stream_3000p300_c2k")
+    B, L, D = wl.users, wl.layers, wl.d_model
+    model = make_model(torch, wl)
+    cap = 3300
+    cache = hsa.KVCache(model, slots=B, capacity=cap)
+    cache.cached_len = np.zeros(B, dtype=np.int32)
+    empty = np.zeros((0, D), np.float32)
+    gpu_encode(wl, model=model, uih=wl.prefix, cand=empty, uih_lengths=wl.cached_lengths,
+               cand_lengths=np.zeros(B, np.int64), cache=cache)
+    assert cache.cached_len.tolist() == [3000] * B
+    gu, gc = gpu_encode(wl, model=model, cache=cache)
+    assert cache.cached_len.tolist() == [3300] * B
+    b = 37
+    n, c, m = int(wl.uih_lengths[b]), int(wl.cand_lengths[b]), int(wl.cached_lengths[b])
+    pre = wl.prefix[b * m:(b + 1) * m]
+    ocache = oracle.OracleCache(np.zeros((L, 1, cap, D)), np.zeros((L, 1, cap, D)), np.array([0]),
+                                np.array([0]))
+    _, _, ocache = oracle.encode(pre, [0, m], empty, [0, 0], wl.params, heads=wl.heads, max_len=wl.max_len,
+                                 mode="bf16", cache=ocache)
+    ru, rc, ocache = oracle.encode(wl.uih[b * n:(b + 1) * n], [0, n], wl.cand[b * c:(b + 1) * c], [0, c],
+                                   wl.params, heads=wl.heads, max_len=wl.max_len, mode="bf16", cache=ocache)
+    eu = normwise_per_user(gu[b * n:(b + 1) * n], ru, [n])
+    ec = normwise_per_user(gc[b * c:(b + 1) * c], rc, [c])
+    gk = to_np(cache.k[:, b])
+    ek = max(float(np.max(np.abs(gk[l, :m + n] - ocache.k[l, 0, :m + n])) / np.max(np.abs(ocache.k[l, 0, :m + n])))
+             for l in range(L))
+    say(f"  streaming user {b}: uih {eu:.3e} cand {ec:.3e} cached K {ek:.3e}")
+    assert eu <= BF16_TOL and ec <= BF16_TOL and ek <= BF16_TOL
+
+
+def test_long_workload_layerwise_sampled_rows():
+    """16 layers, 4 users with UIH 8K-16K, 2048 candidates, 8 heads (dh 64). The full call
+    equals the chain of 16 one-layer calls bit for bit; layers 0, 7 and 15 are then checked
+    row by row against the oracle on sampled history and candidate rows of every user, fed
+    with the GPU's own input to that layer."""
+    torch = torch_cuda()
+    wl = workloads.make_workload("long_uih16k_c2k")
+    D = wl.d_model
+    full_u, full_c = gpu_encode(wl, keep_device=True)
+    full_u, full_c = to_np(full_u), to_np(full_c)
+    xs = [(to_dev(torch, wl.uih, "bf16"), to_dev(torch, wl.cand, "bf16"))]
+    for l in range(wl.layers):
+        m1 = hsa.Model([wl.params[l]], d_model=D, heads=wl.heads, max_len=wl.max_len, dtype="bf16")
+        xs.append(gpu_encode(wl, model=m1, uih=xs[-1][0], cand=xs[-1][1], keep_device=True))
+        del m1
+    assert np.array_equal(to_np(xs[-1][0]), full_u) and np.array_equal(to_np(xs[-1][1]), full_c)
+    uo = workloads.lengths_to_offsets(wl.uih_lengths)
+    co = workloads.lengths_to_offsets(wl.cand_lengths)
+    rng = np.random.default_rng(5)
+    worst = 0.0
+    for l in (0, 7, 15):
+        p = wl.params[l]
+        w1, w2, pos = (a.astype(np.float64) for a in (p.w1, p.w2, p.pos))
+        xin_u, xin_c = to_np(xs[l][0]), to_np(xs[l][1])
+        xo_u, xo_c = to_np(xs[l + 1][0]), to_np(xs[l + 1][1])
+        for b in range(wl.users):
+            n, c = int(wl.uih_lengths[b]), int(wl.cand_lengths[b])
+            rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, n - 2, n - 1], rng.integers(0, n, 24)]))
+            crows = np.unique(np.concatenate([[0, c - 1], rng.integers(0, c, 14)]))
+            yu, yc, _, _ = oracle.layer_user(xin_u[uo[b]:uo[b + 1]], xin_c[co[b]:co[b + 1]], w1, w2, pos,
+                                             k_cached=np.zeros((0, D)), v_cached=np.zeros((0, D)),
+                                             heads=wl.heads, max_len=wl.max_len, bf16=True,
+                                             uih_rows=rows, cand_rows=crows)
+            gu_rows = xo_u[uo[b] + rows]
+            gc_rows = xo_c[co[b] + crows]
+            eu = float(np.max(np.abs(gu_rows - yu)) / np.max(np.abs(yu)))
+            ec = float(np.max(np.abs(gc_rows - yc)) / np.max(np.abs(yc)))
+            worst = max(worst, eu, ec)
+        say(f"  long: layer {l} worst sampled normwise error so far {worst:.3e}")
+    assert worst <= BF16_TOL

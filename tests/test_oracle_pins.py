@@ -137,6 +137,25 @@ def test_silu_closed_forms():
     assert abs(float(oracle.silu(1.0)) - 1.0 / (1.0 + math.exp(-1.0))) < 1e-16
 
 
+# --------------------------------------------------------------------------- input normalisation
+
+def test_normalize_rows_closed_forms():
+    """Pin (closed form): a row (1, 3) has mean 2 and variance 1, so it maps to
+    (-1, 1)/sqrt(1 + eps); every row ends with mean 0 and variance 1/(1 + eps/var); the map is
+    invariant to a positive scale and a shift of the row."""
+    eps = oracle.NORM_EPS
+    assert np.allclose(oracle.normalize_rows(np.array([[1.0, 3.0]])),
+                       np.array([[-1.0, 1.0]]) / math.sqrt(1 + eps), rtol=1e-15)
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((50, 64)) * 3.0 + 1.5
+    y = oracle.normalize_rows(x)
+    var = x.var(axis=1)
+    assert np.max(np.abs(y.mean(axis=1))) < 1e-14
+    assert np.allclose(y.var(axis=1), var / (var + eps), rtol=1e-13)
+    assert np.allclose(oracle.normalize_rows(7.0 * x - 4.0), oracle.normalize_rows(x), atol=1e-6)
+    assert oracle.normalize_rows(np.zeros((0, 8))).shape == (0, 8)
+
+
 # --------------------------------------------------------------------------- brute force
 
 @pytest.mark.parametrize("mode", ["f64", "bf16"])
@@ -253,7 +272,8 @@ def test_zero_query_gives_zero_attention(mode):
                                        k_cached=np.zeros((0, D)), v_cached=np.zeros((0, D)),
                                        heads=2, max_len=40, bf16=bf16)
     # attention outputs directly
-    s = oracle.silu(xu[:7] @ w1)
+    xn = oracle.normalize_rows(xu[:7])
+    s = oracle.silu((oracle.round_bf16(xn) if bf16 else xn) @ w1)
     q = s[:, 2 * D:3 * D] + pos[:7, D:2 * D]
     assert np.all(q == 0)
     kk = s[:, 3 * D:] + pos[:7, 2 * D:]
