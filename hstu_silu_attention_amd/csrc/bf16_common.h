@@ -1,0 +1,50 @@
+// Device helpers shared by the bfloat16 kernels (gfx950).
+//
+// MFMA operand layout used throughout (v_mfma_f32_32x32x16_bf16, wave64): for
+// D = A*B + C with A 32 x 16, B 16 x 32, lane l supplies A[l%32][8*(l/32) .. +8] and
+// B[8*(l/32) .. +8][l%32]; it receives D[8*i + 4*(l/32) + j][l%32] in accumulator
+// element 4*i + j.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hstu {
+
+typedef uint16_t u16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float bf2f(u16 x) { return __uint_as_float((uint32_t)x << 16); }
+__device__ __forceinline__ float bf2f_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf2f_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+// Two floats -> two bfloat16 (hardware round to nearest even), packed low first.
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float round_bf(float a) { return (float)(__bf16)a; }
+
+// SiLU(x) = x / (1 + 2^(-x*log2(e))) with the hardware exp2 and reciprocal. For
+// x -> -inf the exponential overflows to +inf and the result is -0; no NaN arises.
+__device__ __forceinline__ float silu(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.4426950408889634f));
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Workgroup -> tile order that keeps neighbouring tiles on one XCD. Workgroups are
+// dealt to the 8 XCDs round-robin; giving each XCD a contiguous run of tiles keeps
+// tiles that share operand blocks inside one XCD's L2.
+__device__ __forceinline__ int xcd_swizzle(int wg, int nwg) {
+  const int per = nwg / 8, rem = nwg % 8;
+  const int xcd = wg % 8, local = wg / 8;
+  return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+}
+
+}  // namespace hstu

@@ -12,7 +12,7 @@
 #include <unordered_map>
 #include <vector>
 
-#include "../../include/hstu.h"
+#include "hstu.h"
 #include "hstu_internal.h"
 
 namespace {
@@ -54,7 +54,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 struct Layout {
   int32_t Nu = 0, Nc = 0, T = 0;
   int64_t ntiles = 0;
-  size_t users = 0, tiles = 0, rows = 0, stats = 0, uvqk = 0, o = 0, x = 0, total = 0;
+  size_t users = 0, tiles = 0, rows = 0, xn = 0, uvqk = 0, o = 0, x = 0, total = 0;
   size_t staged = 0;  // bytes copied from the host: users table + tile list
 };
 
@@ -70,14 +70,16 @@ Layout make_layout(const hstu_dims* d, int32_t B, const int32_t* uo, const int32
     L.ntiles += d->heads * (cdiv(uo[b + 1] - uo[b], bm) + cdiv(co[b + 1] - co[b], bm));
   const size_t es = d->dtype == HSTU_F32 ? 4 : 2;
   const size_t D = (size_t)d->d_model, T = (size_t)L.T;
+  // GEMM operands (xn, uvqk, o) are padded to whole 256-row tiles.
+  const size_t Tp = (size_t)cdiv(L.T, hstu::kRowPad) * hstu::kRowPad;
   size_t off = 0;
   L.users = off; off += align_up((size_t)B * sizeof(UserRec));
   L.tiles = off; off += align_up((size_t)L.ntiles * 16);
   L.staged = off;
   L.rows = off; off += align_up(T * 8);
-  L.stats = off; off += align_up(T * 8);
-  L.uvqk = off; off += align_up(T * 4 * D * es);
-  L.o = off; off += align_up(T * D * es);
+  L.xn = off; off += align_up(Tp * D * es);
+  L.uvqk = off; off += align_up(Tp * 4 * D * es);
+  L.o = off; off += align_up(Tp * D * es);
   L.x = off; off += d->layers > 1 ? align_up(T * D * es) : 0;
   L.total = L.T == 0 ? 0 : off;
   return L;
@@ -365,7 +367,7 @@ hstu_status hstu_encode(const hstu_dims* d, int32_t B, const int32_t* uih_offset
   const UserRec* d_users = reinterpret_cast<const UserRec*>(ws + lay.users);
   const int4* d_tiles = reinterpret_cast<const int4*>(ws + lay.tiles);
   int2* d_rows = reinterpret_cast<int2*>(ws + lay.rows);
-  float2* d_stats = reinterpret_cast<float2*>(ws + lay.stats);
+  char* xn = ws + lay.xn;
   const size_t es = d->dtype == HSTU_F32 ? 4 : 2;
   char* uvqk = ws + lay.uvqk;
   char* obuf = ws + lay.o;
@@ -386,10 +388,10 @@ hstu_status hstu_encode(const hstu_dims* d, int32_t B, const int32_t* uih_offset
     void* ck = kv ? (void*)((char*)kv->k + l * layer_cache) : nullptr;
     void* cv = kv ? (void*)((char*)kv->v + l * layer_cache) : nullptr;
 
-    hstu::StatsArgs sa{x_lo, x_hi, lay.Nu, lay.T, D, d_stats};
-    if (timed_launch(HSTU_KERNEL_NORM, s, [&] { return hstu::launch_stats(d->dtype, sa, s); }) != hipSuccess)
+    hstu::NormArgs na{x_lo, x_hi, lay.Nu, lay.T, D, xn};
+    if (timed_launch(HSTU_KERNEL_NORM, s, [&] { return hstu::launch_norm(d->dtype, na, s); }) != hipSuccess)
       return HSTU_ERR_HIP;
-    hstu::UvqkArgs ua{x_lo, x_hi, lay.Nu, lay.T, D, d_stats, w[l].w_uvqk, w[l].pos_bias, d_rows, d_users,
+    hstu::UvqkArgs ua{xn, lay.Nu, lay.T, D, w[l].w_uvqk, w[l].pos_bias, d_rows, d_users,
                       uvqk, ck, cv};
     if (timed_launch(HSTU_KERNEL_UVQK, s, [&] { return hstu::launch_uvqk(d->dtype, ua, s); }) != hipSuccess)
       return HSTU_ERR_HIP;

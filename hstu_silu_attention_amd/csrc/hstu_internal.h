@@ -27,26 +27,28 @@ struct PlanArgs {
   int2* row_info;        // [T] {user, position}
 };
 
-// Per-row statistics of a layer input for its normalisation: {mean, 1/sqrt(var + eps)}.
-struct StatsArgs {
+// Row-padded buffers: the GEMM operands in the workspace have a multiple of kRowPad
+// rows; rows T.. are never written and only ever feed discarded output rows.
+constexpr int kRowPad = 256;
+
+// Normalised layer input Xn = (X - mean) / sqrt(var + eps), per row over D.
+struct NormArgs {
   const void* x_lo;      // rows [0, Nu)
   const void* x_hi;      // rows [Nu, T)
   int32_t Nu, T, D;
-  float2* stats;         // [T] out
+  void* xn;              // [T_pad][D] out
 };
 
 constexpr float kNormEps = 1e-6f;
 
 struct UvqkArgs {
-  const void* x_lo;      // rows [0, Nu)
-  const void* x_hi;      // rows [Nu, T)
+  const void* xn;        // [T_pad][D] normalised input rows
   int32_t Nu, T, D;
-  const float2* stats;   // [T] {mean, rstd} of each input row
   const void* w;         // [4D][D]
   const void* pos;       // [max_len][3D]
   const int2* row_info;
   const UserRec* users;
-  void* uvqk;            // [T][4D] out
+  void* uvqk;            // [T_pad][4D] out (rows < T written)
   void* cache_k;         // this layer's [slots][cap][D] or nullptr
   void* cache_v;
 };
@@ -60,12 +62,12 @@ struct AttnArgs {
   const void* kbase;     // key row r of user b is kbase + (key_row_b + r) * ld
   const void* vbase;
   int64_t ld;
-  void* o;               // [T][D] out
+  void* o;               // [T_pad][D] out (rows < T written)
 };
 
 struct OutArgs {
-  const void* uvqk;      // [T][4D]; U = columns [0, D)
-  const void* o;         // [T][D]
+  const void* uvqk;      // [T_pad][4D]; U = columns [0, D)
+  const void* o;         // [T_pad][D]
   const void* w;         // [D][3D]
   const void* x_lo;      // residual rows [0, Nu)
   const void* x_hi;      // residual rows [Nu, T)
@@ -78,7 +80,7 @@ struct OutArgs {
 int attn_block_rows(int dtype);
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
-hipError_t launch_stats(int dtype, const StatsArgs& a, hipStream_t s);
+hipError_t launch_norm(int dtype, const NormArgs& a, hipStream_t s);
 hipError_t launch_uvqk(int dtype, const UvqkArgs& a, hipStream_t s);
 hipError_t launch_attn(int dtype, int dh, const AttnArgs& a, int ntiles, hipStream_t s);
 hipError_t launch_out(int dtype, const OutArgs& a, hipStream_t s);

@@ -54,17 +54,11 @@ __device__ __forceinline__ void gemm_f32(const ALoad& aload, const float* __rest
   }
 }
 
-// The normalised layer input (x - mean) * rstd.
+// The normalised layer input, as stored.
 struct XLoadF {
-  const float* lo;
-  const float* hi;
-  const float2* stats;
-  int Nu, D;
-  __device__ __forceinline__ float operator()(int row, int k) const {
-    const float x = row < Nu ? lo[(size_t)row * D + k] : hi[(size_t)(row - Nu) * D + k];
-    const float2 st = stats[row];
-    return (x - st.x) * st.y;
-  }
+  const float* xn;
+  int D;
+  __device__ __forceinline__ float operator()(int row, int k) const { return xn[(size_t)row * D + k]; }
 };
 
 struct GateLoadF {
@@ -95,7 +89,7 @@ __global__ __launch_bounds__(256) void uvqk_f32_kernel(UvqkArgs a) {
       dst[((size_t)a.users[ri.x].key_row + ri.y) * D + cc] = v;
     }
   };
-  gemm_f32(XLoadF{(const float*)a.x_lo, (const float*)a.x_hi, a.stats, a.Nu, D}, (const float*)a.w, D, a.T,
+  gemm_f32(XLoadF{(const float*)a.xn, D}, (const float*)a.w, D, a.T,
            4 * D / FT, epi);
 }
 

@@ -1,7 +1,8 @@
 // The jagged row planner kernel and the per-dtype launch dispatch.
 #include <hip/hip_runtime.h>
 
-#include "../../include/hstu.h"
+#include "hstu.h"
+#include "bf16_common.h"
 #include "hstu_internal.h"
 
 namespace hstu {
@@ -43,40 +44,71 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ float load_f(const float* p) { return *p; }
-__device__ __forceinline__ float load_f(const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
+// 16-byte chunk <-> floats: 4 float32 or 8 bfloat16 values.
+__device__ __forceinline__ void load_chunk(const float* p, float* v) {
+  const float4 q = *reinterpret_cast<const float4*>(p);
+  v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+}
+__device__ __forceinline__ void load_chunk(const u16* p, float* v) {
+  const uint4 q = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[2 * e] = bf2f_lo(w[e]);
+    v[2 * e + 1] = bf2f_hi(w[e]);
+  }
+}
+__device__ __forceinline__ void store_chunk(float* p, const float* v) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void store_chunk(u16* p, const float* v) {
+  *reinterpret_cast<uint4*>(p) = make_uint4(pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7]));
+}
 
-// One wave per row: two passes over the row (mean, then the mean squared deviation),
-// each reduced across the wave in a fixed butterfly order, so a row's statistics
-// depend on that row alone.
+// One wave per row: the mean, then the mean squared deviation, each reduced across
+// the wave in a fixed butterfly order (a row's result depends on that row alone),
+// then the normalised row (x - mean) / sqrt(var + eps), rounded to the storage type.
 template <typename T>
-__global__ __launch_bounds__(256) void row_stats_kernel(StatsArgs a) {
+__global__ __launch_bounds__(256) void norm_kernel(NormArgs a) {
+  constexpr int VEC = 16 / sizeof(T);
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= a.T) return;
-  const int D = a.D;
+  const int D = a.D, nchunk = D / VEC;
   const T* x = row < a.Nu ? (const T*)a.x_lo + (size_t)row * D : (const T*)a.x_hi + (size_t)(row - a.Nu) * D;
+  T* y = (T*)a.xn + (size_t)row * D;
+  float v[VEC];
   float s = 0.0f;
-  for (int k = lane; k < D; k += 64) s += load_f(x + k);
+  for (int c = lane; c < nchunk; c += 64) {
+    load_chunk(x + c * VEC, v);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) s += v[e];
+  }
   const float mean = wave_sum(s) / (float)D;
   float q = 0.0f;
-  for (int k = lane; k < D; k += 64) {
-    const float d = load_f(x + k) - mean;
-    q += d * d;
+  for (int c = lane; c < nchunk; c += 64) {
+    load_chunk(x + c * VEC, v);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) q += (v[e] - mean) * (v[e] - mean);
   }
-  const float var = wave_sum(q) / (float)D;
-  if (lane == 0) a.stats[row] = make_float2(mean, 1.0f / sqrtf(var + kNormEps));
+  const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)D + kNormEps);
+  for (int c = lane; c < nchunk; c += 64) {
+    load_chunk(x + c * VEC, v);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) v[e] = (v[e] - mean) * rstd;
+    store_chunk(y + c * VEC, v);
+  }
 }
 
 }  // namespace
 
-hipError_t launch_stats(int dtype, const StatsArgs& a, hipStream_t s) {
+hipError_t launch_norm(int dtype, const NormArgs& a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
   const int blocks = (a.T + 3) / 4;
   if (dtype == HSTU_F32)
-    row_stats_kernel<float><<<blocks, 256, 0, s>>>(a);
+    norm_kernel<float><<<blocks, 256, 0, s>>>(a);
   else
-    row_stats_kernel<uint16_t><<<blocks, 256, 0, s>>>(a);
+    norm_kernel<u16><<<blocks, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -175,7 +175,7 @@ enum hstu_kernel_kind {
   HSTU_KERNEL_UVQK = 1,       /* projection GEMM + SiLU + bias + append  */
   HSTU_KERNEL_ATTENTION = 2,  /* target-aware causal SiLU attention      */
   HSTU_KERNEL_OUT = 3,        /* gated output GEMM + residual            */
-  HSTU_KERNEL_NORM = 4,       /* per-row statistics of the layer input   */
+  HSTU_KERNEL_NORM = 4,       /* per-row normalisation of the layer input */
   HSTU_KERNEL_KINDS = 5
 };
 hstu_status hstu_timing_enable(int32_t enable);
