@@ -8,22 +8,41 @@
 namespace hstu {
 namespace {
 
-// ------------------------------------------------------------------ attention
-// One work item = (user, head, up to 128 query rows of one kind). Four waves own
-// 32 query rows each; key blocks of 64 are staged in LDS (K row-major, V
-// transposed). Per 32-key half: S^T = K Q^T (queries along lanes), mask + SiLU +
-// bf16, then O^T += V^T A^T with the key order permuted identically on both operands.
-// No softmax: partial sums over key blocks simply add; the 1/max_len scale is
-// applied once to the float32 accumulator.
-constexpr int ABM = 128, AKB = 64;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// One work item = (user, head, up to 128 query rows of one kind): four waves of 32
+// query rows. Keys advance 64 at a time through two LDS stages; K and V are both
+// staged row-major with 16-byte loads (keys past the user's last one are zero).
+//
+// Per 32-key half a wave computes S^T = K Q^T (queries along lanes), turns it into
+// bf16 weights a = SiLU(s) (masked only in blocks that cross the causal diagonal or
+// the last key), then O^T += V^T A^T. The V^T operand comes from the row-major V
+// stage by the LDS transpose read: in each 16-lane group, lanes 4r..4r+3 address
+// 16 consecutive columns of key row r and lane i receives column i of those four
+// rows. The key order inside the PV contraction is permuted to match the layout in
+// which S^T's accumulators hold the weights; both operands use the same order.
+//
+// K rows are 8 elements longer than dh (16-byte reads of 8 consecutive rows hit
+// distinct banks); V rows 16 longer (the 4 rows of one transpose read do).
+template <int DH>
+struct AttnTile {
+  static constexpr int BM = 128, KB = 64;
+  static constexpr int LDK = DH + 8, LDV = DH + 16;
+  static constexpr int KSZ = KB * LDK, STAGE = KB * (LDK + LDV);
+  static constexpr int CPR = DH / 8;             // 16-byte chunks per key row
+  static constexpr int CPT = KB * CPR / 256;     // chunks per thread per matrix
+};
 
 template <int DH>
-__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
-  constexpr int KLD = DH + 8, VLD = AKB + 8;
-  __shared__ __attribute__((aligned(16))) u16 sK[AKB * KLD];
-  __shared__ __attribute__((aligned(16))) u16 sVt[DH * VLD];
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_kernel(AttnArgs a) {
+  using C = AttnTile<DH>;
+  __shared__ __attribute__((aligned(16))) u16 smem[2 * C::STAGE];
 
-  const int4 t = a.tiles[blockIdx.x];
+  const int2 bin = a.bins[blockIdx.x % kXcds];
+  if ((int)(blockIdx.x / kXcds) >= bin.y) return;
+  const int4 t = a.tiles[bin.x + blockIdx.x / kXcds];
   const UserRec u = a.users[t.x];
   const int head = t.y >> 1, q0 = t.z, nq = t.w;
   const bool cand = (t.y & 1) != 0;
@@ -32,7 +51,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const size_t ld4 = 4 * (size_t)D;
   const int qloc = wv * 32 + l32;
   const bool qok = qloc < nq;
-  const int qi = q0 + qloc;
+  const int qi = q0 + (qok ? qloc : 0);
   const size_t row = cand ? (size_t)a.Nu + u.coff + qi : (size_t)u.uoff + qi;
   const u16* uvqk = (const u16*)a.uvqk;
 
@@ -44,66 +63,104 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 
   const int key_end = cand ? u.m + u.n : u.m + q0 + nq;  // keys [0, key_end)
   const int qpos = u.m + qi;                             // history row: keys <= qpos
+  // This wave's query positions (history items): the block loop skips key blocks
+  // past its last query and drops the mask for blocks before its first one.
+  const bool wave_live = wv * 32 < nq;
+  const int wq_first = u.m + q0 + wv * 32;
+  const int wq_last = u.m + q0 + min(nq, wv * 32 + 32) - 1;
+
   f32x16 oacc[DH / 32];
 #pragma unroll
   for (int mb = 0; mb < DH / 32; ++mb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[mb][e] = 0.0f;
 
+  // staging: thread t moves chunk t + 256*i (i < CPT): key row c / CPR, column (c % CPR) * 8
   const u16* kp = (const u16*)a.kbase + (size_t)u.key_row * a.ld + head * DH;
   const u16* vp = (const u16*)a.vbase + (size_t)u.key_row * a.ld + head * DH;
-
-  for (int k0 = 0; k0 < key_end; k0 += AKB) {
-    __syncthreads();
-    for (int id = tid; id < AKB * DH / 8; id += 256) {
-      const int key = id / (DH / 8), c8 = (id % (DH / 8)) * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (k0 + key < key_end) v = *reinterpret_cast<const uint4*>(kp + (size_t)(k0 + key) * a.ld + c8);
-      *reinterpret_cast<uint4*>(&sK[key * KLD + c8]) = v;
-    }
-    for (int id = tid; id < AKB * DH / 8; id += 256) {
-      const int key = id % AKB, c8 = (id / AKB) * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (k0 + key < key_end) v = *reinterpret_cast<const uint4*>(vp + (size_t)(k0 + key) * a.ld + c8);
-      const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
+  uint4 rk[C::CPT], rv[C::CPT];
+  auto fetch = [&](int k0) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sVt[(c8 + 2 * e) * VLD + key] = (u16)(wds[e] & 0xffffu);
-        sVt[(c8 + 2 * e + 1) * VLD + key] = (u16)(wds[e] >> 16);
-      }
+    for (int i = 0; i < C::CPT; ++i) {
+      const int c = tid + 256 * i, key = k0 + c / C::CPR, col = (c % C::CPR) * 8;
+      const bool in = key < key_end;
+      rk[i] = in ? *reinterpret_cast<const uint4*>(kp + (size_t)key * a.ld + col) : make_uint4(0, 0, 0, 0);
+      rv[i] = in ? *reinterpret_cast<const uint4*>(vp + (size_t)key * a.ld + col) : make_uint4(0, 0, 0, 0);
     }
-    __syncthreads();
+  };
+  auto store = [&](int stage) {
+    u16* sk = smem + stage * C::STAGE;
+    u16* sv = sk + C::KSZ;
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const int c = tid + 256 * i, r = c / C::CPR, col = (c % C::CPR) * 8;
+      *reinterpret_cast<uint4*>(sk + r * C::LDK + col) = rk[i];
+      *reinterpret_cast<uint4*>(sv + r * C::LDV + col) = rv[i];
+    }
+  };
+
+  // transpose-read lane constants: group g = lane / 16 reads key rows 4*(g/2) + r
+  // (r = (lane % 16) / 4) at columns 16*(g%2) + 4*(lane % 4)
+  const int tr_row = 4 * hi + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  const int nblk = (key_end + C::KB - 1) / C::KB;
+  if (nblk > 0) {
+    fetch(0);
+    store(0);
+  }
+  __syncthreads();
+  for (int kb = 0; kb < nblk; ++kb) {
+    const int k0 = kb * C::KB;
+    // the last block re-fetches itself into the idle stage (unconditional steps keep
+    // the prefetch registers free of loop-carried state)
+    fetch(kb + 1 < nblk ? k0 + C::KB : k0);
+    const u16* sk = smem + (kb & 1) * C::STAGE;
+    const u16* sv = sk + C::KSZ;
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
-      f32x16 s;
+      const int kbase = k0 + kh * 32;
+      const bool live = cand ? kbase < key_end : (wave_live && kbase <= wq_last);
+      if (live) {
+        const bool full = cand ? (kbase + 32 <= key_end) : (kbase + 31 <= wq_first);
+        f32x16 s;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[e] = 0.0f;
+        for (int e = 0; e < 16; ++e) s[e] = 0.0f;
 #pragma unroll
-      for (int kk = 0; kk < DH / 16; ++kk) {
-        const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4*>(&sK[(kh * 32 + l32) * KLD + kk * 16 + hi * 8]));
-        s = mfma32(kf, qf[kk], s);
-      }
-      // s[4*i + j] = q(row l32) . k(key k0 + kh*32 + 8*i + 4*hi + j)
-      bf16x8 af[2];
+        for (int kk = 0; kk < DH / 16; ++kk) {
+          const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4*>(sk + (kh * 32 + l32) * C::LDK + kk * 16 + hi * 8));
+          s = mfma32(kf, qf[kk], s);
+        }
+        // s[4*i + j] = q(row l32) . k(key kbase + 8*i + 4*hi + j)
+        bf16x8 af[2];
+        if (full) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = k0 + kh * 32 + (e >> 2) * 8 + hi * 4 + (e & 3);
-        const bool ok = key < key_end && (cand || key <= qpos);
-        af[e >> 3][e & 7] = (__bf16)(ok ? silu(s[e]) : 0.0f);
-      }
-      // B operand chunk c, element e <-> key kh*32 + (2c + e/4)*8 + 4*hi + e%4; the
-      // V^T operand reads the same keys for its dh row.
+          for (int e = 0; e < 16; ++e) af[e >> 3][e & 7] = (__bf16)silu(s[e]);
+        } else {
 #pragma unroll
-      for (int mb = 0; mb < DH / 32; ++mb) {
-        const u16* vrow = &sVt[(mb * 32 + l32) * VLD + kh * 32 + hi * 4];
+          for (int e = 0; e < 16; ++e) {
+            const int key = kbase + (e >> 2) * 8 + hi * 4 + (e & 3);
+            const bool ok = cand ? key < key_end : key <= qpos;
+            af[e >> 3][e & 7] = (__bf16)(ok ? silu(s[e]) : 0.0f);
+          }
+        }
+        // weight chunk c, element e <-> key kbase + 16c + 8*(e/4) + 4*hi + e%4: the
+        // transpose reads fetch V rows kbase + 16c + 4*hi + r and the same + 8
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          const uint2 p0 = *reinterpret_cast<const uint2*>(vrow + (2 * c) * 8);
-          const uint2 p1 = *reinterpret_cast<const uint2*>(vrow + (2 * c + 1) * 8);
-          oacc[mb] = mfma32(as_bf16x8(make_uint4(p0.x, p0.y, p1.x, p1.y)), af[c], oacc[mb]);
+          const u16* vrow = sv + (kh * 32 + 16 * c + tr_row) * C::LDV + tr_col;
+#pragma unroll
+          for (int mb = 0; mb < DH / 32; ++mb) {
+            const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vrow + mb * 32));
+            const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vrow + 8 * C::LDV + mb * 32));
+            const bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+            oacc[mb] = mfma32(vf, af[c], oacc[mb]);
+          }
         }
       }
     }
+    store((kb + 1) & 1);
+    __syncthreads();
   }
 
   if (cand) {
@@ -153,17 +210,17 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 
 }  // namespace
 
-hipError_t launch_attn_bf16(int dh, const AttnArgs& a, int ntiles, hipStream_t s) {
-  if (ntiles <= 0) return hipSuccess;
+hipError_t launch_attn_bf16(int dh, const AttnArgs& a, int grid, hipStream_t s) {
+  if (grid <= 0) return hipSuccess;
   if (dh == 64)
-    attn_kernel<64><<<ntiles, 256, 0, s>>>(a);
+    attn_kernel<64><<<grid, 256, 0, s>>>(a);
   else if (dh == 128)
-    attn_kernel<128><<<ntiles, 256, 0, s>>>(a);
+    attn_kernel<128><<<grid, 256, 0, s>>>(a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
-int attn_block_rows_bf16() { return ABM; }
+int attn_block_rows_bf16() { return AttnTile<128>::BM; }
 
 }  // namespace hstu

@@ -54,8 +54,8 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 struct Layout {
   int32_t Nu = 0, Nc = 0, T = 0;
   int64_t ntiles = 0;
-  size_t users = 0, tiles = 0, rows = 0, xn = 0, uvqk = 0, o = 0, x = 0, total = 0;
-  size_t staged = 0;  // bytes copied from the host: users table + tile list
+  size_t users = 0, bins = 0, tiles = 0, rows = 0, xn = 0, uvqk = 0, o = 0, x = 0, total = 0;
+  size_t staged = 0;  // bytes copied from the host: users table + XCD bins + tile list
 };
 
 Layout make_layout(const hstu_dims* d, int32_t B, const int32_t* uo, const int32_t* co) {
@@ -74,6 +74,7 @@ Layout make_layout(const hstu_dims* d, int32_t B, const int32_t* uo, const int32
   const size_t Tp = (size_t)cdiv(L.T, hstu::kRowPad) * hstu::kRowPad;
   size_t off = 0;
   L.users = off; off += align_up((size_t)B * sizeof(UserRec));
+  L.bins = off; off += align_up((size_t)hstu::kXcds * 8);
   L.tiles = off; off += align_up((size_t)L.ntiles * 16);
   L.staged = off;
   L.rows = off; off += align_up(T * 8);
@@ -334,30 +335,58 @@ hstu_status hstu_encode(const hstu_dims* d, int32_t B, const int32_t* uih_offset
     u.key_row = kv ? kv->slot_of_user[b] * kv->capacity : u.uoff;
     u.pad0 = u.pad1 = 0;
   }
-  // Attention work items, most keys first, so long items start early and short
-  // ones fill the tail of the launch. The order never changes any result: each
-  // item writes its own rows, with a fixed key order inside.
-  struct Item { int32_t user, hk, q0, nq; int64_t keys; };
-  std::vector<Item> items;
-  items.reserve((size_t)lay.ntiles);
+  // Attention work items, grouped per (user, head). Each group goes whole to one of
+  // the kXcds bins (one bin per XCD), so a user's keys and values are read into one
+  // L2 only; groups are placed largest first on the least loaded bin, and inside a
+  // bin the groups keep that order with their items most keys first. The order never
+  // changes any result: each item writes its own rows, with a fixed key order inside.
+  struct Item { int32_t user, hk, q0, nq; int64_t cost; };
+  struct Group { std::vector<Item> items; int64_t cost = 0; };
+  std::vector<Group> groups;
+  groups.reserve((size_t)B * d->heads);
   for (int32_t b = 0; b < B; ++b) {
     const UserRec& u = users[b];
     for (int32_t h = 0; h < d->heads; ++h) {
-      for (int32_t q0 = 0; q0 < u.n; q0 += bm)
-        items.push_back({b, h << 1, q0, std::min(bm, u.n - q0), (int64_t)u.m + q0 + std::min(bm, u.n - q0)});
+      Group g;
+      // cost ~ key blocks swept, plus a fixed per-item overhead
+      for (int32_t q0 = 0; q0 < u.n; q0 += bm) {
+        const int32_t nq = std::min(bm, u.n - q0);
+        g.items.push_back({b, h << 1, q0, nq, cdiv((int64_t)u.m + q0 + nq, 64) + 2});
+      }
       for (int32_t q0 = 0; q0 < u.c; q0 += bm)
-        items.push_back({b, (h << 1) | 1, q0, std::min(bm, u.c - q0), (int64_t)u.m + u.n + 1});
+        g.items.push_back({b, (h << 1) | 1, q0, std::min(bm, u.c - q0), cdiv((int64_t)u.m + u.n, 64) + 2});
+      if (g.items.empty()) continue;
+      std::stable_sort(g.items.begin(), g.items.end(),
+                       [](const Item& x, const Item& y) { return x.cost > y.cost; });
+      for (const Item& it : g.items) g.cost += it.cost;
+      groups.push_back(std::move(g));
     }
   }
-  std::stable_sort(items.begin(), items.end(),
-                   [](const Item& a, const Item& b) { return a.keys > b.keys; });
-  int32_t* tiles = reinterpret_cast<int32_t*>(staged.data() + lay.tiles);
-  for (size_t i = 0; i < items.size(); ++i) {
-    tiles[4 * i + 0] = items[i].user;
-    tiles[4 * i + 1] = items[i].hk;
-    tiles[4 * i + 2] = items[i].q0;
-    tiles[4 * i + 3] = items[i].nq;
+  std::stable_sort(groups.begin(), groups.end(),
+                   [](const Group& x, const Group& y) { return x.cost > y.cost; });
+  std::vector<std::vector<const Item*>> bin_items(hstu::kXcds);
+  int64_t bin_cost[hstu::kXcds] = {};
+  for (const Group& g : groups) {
+    const int x = (int)(std::min_element(bin_cost, bin_cost + hstu::kXcds) - bin_cost);
+    bin_cost[x] += g.cost;
+    for (const Item& it : g.items) bin_items[x].push_back(&it);
   }
+  int32_t* bins = reinterpret_cast<int32_t*>(staged.data() + lay.bins);
+  int32_t* tiles = reinterpret_cast<int32_t*>(staged.data() + lay.tiles);
+  int32_t next = 0, longest = 0;
+  for (int x = 0; x < hstu::kXcds; ++x) {
+    bins[2 * x] = next;
+    bins[2 * x + 1] = (int32_t)bin_items[x].size();
+    longest = std::max(longest, (int32_t)bin_items[x].size());
+    for (const Item* it : bin_items[x]) {
+      tiles[4 * next + 0] = it->user;
+      tiles[4 * next + 1] = it->hk;
+      tiles[4 * next + 2] = it->q0;
+      tiles[4 * next + 3] = it->nq;
+      ++next;
+    }
+  }
+  const int attn_grid = hstu::kXcds * longest;
 
   // ------------------------------------------------------------ enqueue
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -366,6 +395,7 @@ hstu_status hstu_encode(const hstu_dims* d, int32_t B, const int32_t* uih_offset
   if (st != HSTU_OK) return st;
   const UserRec* d_users = reinterpret_cast<const UserRec*>(ws + lay.users);
   const int4* d_tiles = reinterpret_cast<const int4*>(ws + lay.tiles);
+  const int2* d_bins = reinterpret_cast<const int2*>(ws + lay.bins);
   int2* d_rows = reinterpret_cast<int2*>(ws + lay.rows);
   char* xn = ws + lay.xn;
   const size_t es = d->dtype == HSTU_F32 ? 4 : 2;
@@ -398,6 +428,7 @@ hstu_status hstu_encode(const hstu_dims* d, int32_t B, const int32_t* uih_offset
 
     hstu::AttnArgs aa{};
     aa.tiles = d_tiles;
+    aa.bins = d_bins;
     aa.users = d_users;
     aa.Nu = lay.Nu;
     aa.D = D;
@@ -414,7 +445,7 @@ hstu_status hstu_encode(const hstu_dims* d, int32_t B, const int32_t* uih_offset
     }
     aa.o = obuf;
     if (timed_launch(HSTU_KERNEL_ATTENTION, s,
-                     [&] { return hstu::launch_attn(d->dtype, dh, aa, (int)lay.ntiles, s); }) != hipSuccess)
+                     [&] { return hstu::launch_attn(d->dtype, dh, aa, attn_grid, s); }) != hipSuccess)
       return HSTU_ERR_HIP;
 
     hstu::OutArgs oa{uvqk, obuf, w[l].w_out, x_lo, x_hi, y_lo, y_hi, lay.Nu, lay.T, D};

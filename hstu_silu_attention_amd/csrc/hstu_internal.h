@@ -20,6 +20,12 @@ struct UserRec {
 // Attention work item: 16 bytes = {user, (head << 1) | is_candidate_tile, q0, nq}.
 // q0 is the tile's first query within the user's history (or candidate) rows,
 // nq <= the kernel's query-block size.
+//
+// The work items are grouped into kXcds bins, one per XCD: workgroups are dealt to
+// the XCDs round-robin, so workgroup w runs on XCD w % kXcds and takes item
+// bins[w % kXcds].x + w / kXcds when w / kXcds < bins[w % kXcds].y. All items of one
+// (user, head) share a bin, so that user's keys and values stay in one L2.
+constexpr int kXcds = 8;
 
 struct PlanArgs {
   const UserRec* users;
@@ -55,6 +61,7 @@ struct UvqkArgs {
 
 struct AttnArgs {
   const int4* tiles;
+  const int2* bins;      // [kXcds] {first item, item count}
   const UserRec* users;
   int32_t Nu, D;
   float inv;             // 1 / max_len
@@ -82,7 +89,8 @@ int attn_block_rows(int dtype);
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_norm(int dtype, const NormArgs& a, hipStream_t s);
 hipError_t launch_uvqk(int dtype, const UvqkArgs& a, hipStream_t s);
-hipError_t launch_attn(int dtype, int dh, const AttnArgs& a, int ntiles, hipStream_t s);
+// grid = kXcds * (longest bin)
+hipError_t launch_attn(int dtype, int dh, const AttnArgs& a, int grid, hipStream_t s);
 hipError_t launch_out(int dtype, const OutArgs& a, hipStream_t s);
 
 }  // namespace hstu

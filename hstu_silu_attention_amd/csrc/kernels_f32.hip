@@ -114,7 +114,9 @@ template <int DH>
 __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   __shared__ float sk[FKB][DH];
   __shared__ float sv[FKB][DH];
-  const int4 t = a.tiles[blockIdx.x];
+  const int2 bin = a.bins[blockIdx.x % kXcds];
+  if ((int)(blockIdx.x / kXcds) >= bin.y) return;
+  const int4 t = a.tiles[bin.x + blockIdx.x / kXcds];
   const UserRec u = a.users[t.x];
   const int head = t.y >> 1, q0 = t.z, nq = t.w;
   const bool cand = (t.y & 1) != 0;
@@ -183,12 +185,12 @@ hipError_t launch_out_f32(const OutArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_attn_f32(int dh, const AttnArgs& a, int ntiles, hipStream_t s) {
-  if (ntiles <= 0) return hipSuccess;
+hipError_t launch_attn_f32(int dh, const AttnArgs& a, int grid, hipStream_t s) {
+  if (grid <= 0) return hipSuccess;
   switch (dh) {
-    case 32: attn_f32_kernel<32><<<ntiles, 64, 0, s>>>(a); break;
-    case 64: attn_f32_kernel<64><<<ntiles, 64, 0, s>>>(a); break;
-    case 128: attn_f32_kernel<128><<<ntiles, 64, 0, s>>>(a); break;
+    case 32: attn_f32_kernel<32><<<grid, 64, 0, s>>>(a); break;
+    case 64: attn_f32_kernel<64><<<grid, 64, 0, s>>>(a); break;
+    case 128: attn_f32_kernel<128><<<grid, 64, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -9,11 +9,11 @@ namespace hstu {
 
 hipError_t launch_uvqk_bf16(const UvqkArgs& a, hipStream_t s);
 hipError_t launch_out_bf16(const OutArgs& a, hipStream_t s);
-hipError_t launch_attn_bf16(int dh, const AttnArgs& a, int ntiles, hipStream_t s);
+hipError_t launch_attn_bf16(int dh, const AttnArgs& a, int grid, hipStream_t s);
 int attn_block_rows_bf16();
 hipError_t launch_uvqk_f32(const UvqkArgs& a, hipStream_t s);
 hipError_t launch_out_f32(const OutArgs& a, hipStream_t s);
-hipError_t launch_attn_f32(int dh, const AttnArgs& a, int ntiles, hipStream_t s);
+hipError_t launch_attn_f32(int dh, const AttnArgs& a, int grid, hipStream_t s);
 int attn_block_rows_f32();
 
 namespace {
@@ -125,8 +125,8 @@ hipError_t launch_uvqk(int dtype, const UvqkArgs& a, hipStream_t s) {
   return dtype == HSTU_F32 ? launch_uvqk_f32(a, s) : launch_uvqk_bf16(a, s);
 }
 
-hipError_t launch_attn(int dtype, int dh, const AttnArgs& a, int ntiles, hipStream_t s) {
-  return dtype == HSTU_F32 ? launch_attn_f32(dh, a, ntiles, s) : launch_attn_bf16(dh, a, ntiles, s);
+hipError_t launch_attn(int dtype, int dh, const AttnArgs& a, int grid, hipStream_t s) {
+  return dtype == HSTU_F32 ? launch_attn_f32(dh, a, grid, s) : launch_attn_bf16(dh, a, grid, s);
 }
 
 hipError_t launch_out(int dtype, const OutArgs& a, hipStream_t s) {
