@@ -48,18 +48,17 @@ void attn_kernel(AttnArgs a) {
   const bool cand = (t.y & 1) != 0;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l32 = lane & 31, hi = lane >> 5;
   const int D = a.D;
-  const size_t ld4 = 4 * (size_t)D;
+  const size_t ld3 = 3 * (size_t)D;
   const int qloc = wv * 32 + l32;
   const bool qok = qloc < nq;
   const int qi = q0 + (qok ? qloc : 0);
   const size_t row = cand ? (size_t)a.Nu + u.coff + qi : (size_t)u.uoff + qi;
-  const u16* uvqk = (const u16*)a.uvqk;
+  const u16* vqk = (const u16*)a.vqk + row * ld3 + head * DH;   // V | Q | K of this row and head
 
   bf16x8 qf[DH / 16];
 #pragma unroll
   for (int kk = 0; kk < DH / 16; ++kk)
-    qf[kk] = as_bf16x8(qok ? *reinterpret_cast<const uint4*>(uvqk + row * ld4 + 2 * D + head * DH + kk * 16 + hi * 8)
-                           : make_uint4(0, 0, 0, 0));
+    qf[kk] = as_bf16x8(qok ? *reinterpret_cast<const uint4*>(vqk + D + kk * 16 + hi * 8) : make_uint4(0, 0, 0, 0));
 
   const int key_end = cand ? u.m + u.n : u.m + q0 + nq;  // keys [0, key_end)
   const int qpos = u.m + qi;                             // history row: keys <= qpos
@@ -165,8 +164,8 @@ void attn_kernel(AttnArgs a) {
 
   if (cand) {
     // the candidate's own key and value: a_self = bf16(SiLU(q . k_self))
-    const u16* krow = uvqk + row * ld4 + 3 * D + head * DH;
-    const u16* vrow = uvqk + row * ld4 + 1 * D + head * DH;
+    const u16* krow = vqk + 2 * D;
+    const u16* vrow = vqk;
     float part = 0.0f;
     if (qok) {
 #pragma unroll
@@ -196,14 +195,25 @@ void attn_kernel(AttnArgs a) {
     }
   }
   if (qok) {
-    u16* orow = (u16*)a.o + row * D + head * DH;
+    // O = bf16(inv * acc) into columns [D, 2D) of the output GEMM's operand row, and the
+    // gate bf16(U * O), from this row's U (columns [0, D)), into columns [2D, 3D)
+    u16* arow = (u16*)a.aout + row * ld3 + head * DH;
+    uint2 uv[DH / 32][4];
+#pragma unroll
+    for (int mb = 0; mb < DH / 32; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) uv[mb][i] = *reinterpret_cast<const uint2*>(arow + mb * 32 + i * 8 + hi * 4);
 #pragma unroll
     for (int mb = 0; mb < DH / 32; ++mb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint2 pk = make_uint2(pack2(a.inv * oacc[mb][4 * i + 0], a.inv * oacc[mb][4 * i + 1]),
-                                    pack2(a.inv * oacc[mb][4 * i + 2], a.inv * oacc[mb][4 * i + 3]));
-        *reinterpret_cast<uint2*>(orow + mb * 32 + i * 8 + hi * 4) = pk;
+        const float o0 = round_bf(a.inv * oacc[mb][4 * i + 0]), o1 = round_bf(a.inv * oacc[mb][4 * i + 1]);
+        const float o2 = round_bf(a.inv * oacc[mb][4 * i + 2]), o3 = round_bf(a.inv * oacc[mb][4 * i + 3]);
+        const int c = mb * 32 + i * 8 + hi * 4;
+        *reinterpret_cast<uint2*>(arow + D + c) = make_uint2(pack2(o0, o1), pack2(o2, o3));
+        const uint2 g = make_uint2(pack2(bf2f_lo(uv[mb][i].x) * o0, bf2f_hi(uv[mb][i].x) * o1),
+                                   pack2(bf2f_lo(uv[mb][i].y) * o2, bf2f_hi(uv[mb][i].y) * o3));
+        *reinterpret_cast<uint2*>(arow + 2 * D + c) = g;
       }
   }
 }

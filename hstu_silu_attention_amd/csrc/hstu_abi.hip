@@ -54,7 +54,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 struct Layout {
   int32_t Nu = 0, Nc = 0, T = 0;
   int64_t ntiles = 0;
-  size_t users = 0, bins = 0, tiles = 0, rows = 0, xn = 0, uvqk = 0, o = 0, x = 0, total = 0;
+  size_t users = 0, bins = 0, tiles = 0, rows = 0, xn = 0, vqk = 0, aout = 0, x = 0, total = 0;
   size_t staged = 0;  // bytes copied from the host: users table + XCD bins + tile list
 };
 
@@ -70,7 +70,7 @@ Layout make_layout(const hstu_dims* d, int32_t B, const int32_t* uo, const int32
     L.ntiles += d->heads * (cdiv(uo[b + 1] - uo[b], bm) + cdiv(co[b + 1] - co[b], bm));
   const size_t es = d->dtype == HSTU_F32 ? 4 : 2;
   const size_t D = (size_t)d->d_model, T = (size_t)L.T;
-  // GEMM operands (xn, uvqk, o) are padded to whole 256-row tiles.
+  // GEMM operands (xn, vqk, aout) are padded to whole 256-row tiles.
   const size_t Tp = (size_t)cdiv(L.T, hstu::kRowPad) * hstu::kRowPad;
   size_t off = 0;
   L.users = off; off += align_up((size_t)B * sizeof(UserRec));
@@ -79,8 +79,8 @@ Layout make_layout(const hstu_dims* d, int32_t B, const int32_t* uo, const int32
   L.staged = off;
   L.rows = off; off += align_up(T * 8);
   L.xn = off; off += align_up(Tp * D * es);
-  L.uvqk = off; off += align_up(Tp * 4 * D * es);
-  L.o = off; off += align_up(Tp * D * es);
+  L.vqk = off; off += align_up(Tp * 3 * D * es);
+  L.aout = off; off += align_up(Tp * 3 * D * es);
   L.x = off; off += d->layers > 1 ? align_up(T * D * es) : 0;
   L.total = L.T == 0 ? 0 : off;
   return L;
@@ -399,8 +399,8 @@ hstu_status hstu_encode(const hstu_dims* d, int32_t B, const int32_t* uih_offset
   int2* d_rows = reinterpret_cast<int2*>(ws + lay.rows);
   char* xn = ws + lay.xn;
   const size_t es = d->dtype == HSTU_F32 ? 4 : 2;
-  char* uvqk = ws + lay.uvqk;
-  char* obuf = ws + lay.o;
+  char* vqk = ws + lay.vqk;
+  char* aout = ws + lay.aout;
   char* xbuf = ws + lay.x;
   const size_t nu_bytes = (size_t)lay.Nu * D * es;
 
@@ -422,7 +422,7 @@ hstu_status hstu_encode(const hstu_dims* d, int32_t B, const int32_t* uih_offset
     if (timed_launch(HSTU_KERNEL_NORM, s, [&] { return hstu::launch_norm(d->dtype, na, s); }) != hipSuccess)
       return HSTU_ERR_HIP;
     hstu::UvqkArgs ua{xn, lay.Nu, lay.T, D, w[l].w_uvqk, w[l].pos_bias, d_rows, d_users,
-                      uvqk, ck, cv};
+                      vqk, aout, ck, cv};
     if (timed_launch(HSTU_KERNEL_UVQK, s, [&] { return hstu::launch_uvqk(d->dtype, ua, s); }) != hipSuccess)
       return HSTU_ERR_HIP;
 
@@ -433,22 +433,22 @@ hstu_status hstu_encode(const hstu_dims* d, int32_t B, const int32_t* uih_offset
     aa.Nu = lay.Nu;
     aa.D = D;
     aa.inv = 1.0f / (float)d->max_len;
-    aa.uvqk = uvqk;
+    aa.vqk = vqk;
     if (kv) {
       aa.kbase = ck;
       aa.vbase = cv;
       aa.ld = D;
     } else {
-      aa.kbase = uvqk + 3 * (size_t)D * es;
-      aa.vbase = uvqk + 1 * (size_t)D * es;
-      aa.ld = 4 * (int64_t)D;
+      aa.kbase = vqk + 2 * (size_t)D * es;
+      aa.vbase = vqk;
+      aa.ld = 3 * (int64_t)D;
     }
-    aa.o = obuf;
+    aa.aout = aout;
     if (timed_launch(HSTU_KERNEL_ATTENTION, s,
                      [&] { return hstu::launch_attn(d->dtype, dh, aa, attn_grid, s); }) != hipSuccess)
       return HSTU_ERR_HIP;
 
-    hstu::OutArgs oa{uvqk, obuf, w[l].w_out, x_lo, x_hi, y_lo, y_hi, lay.Nu, lay.T, D};
+    hstu::OutArgs oa{aout, w[l].w_out, x_lo, x_hi, y_lo, y_hi, lay.Nu, lay.T, D};
     if (timed_launch(HSTU_KERNEL_OUT, s, [&] { return hstu::launch_out(d->dtype, oa, s); }) != hipSuccess)
       return HSTU_ERR_HIP;
   }

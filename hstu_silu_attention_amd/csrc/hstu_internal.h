@@ -12,7 +12,7 @@ namespace hstu {
 //  coff/c:  candidate rows Nu+coff..Nu+coff+c-1 of the packed row space
 //  m:       cached history length (positions 0..m-1 live in the cache)
 //  key_row: row of key 0 in the key/value source (cache: slot*capacity;
-//           no cache: uoff, i.e. the user's first history row of the uvqk buffer)
+//           no cache: uoff, i.e. the user's first history row of the vqk buffer)
 struct UserRec {
   int32_t uoff, n, coff, c, m, key_row, pad0, pad1;
 };
@@ -33,8 +33,13 @@ struct PlanArgs {
   int2* row_info;        // [T] {user, position}
 };
 
-// Row-padded buffers: the GEMM operands in the workspace have a multiple of kRowPad
-// rows; rows T.. are never written and only ever feed discarded output rows.
+// Workspace buffers of one layer (rows in the packed order: history rows of every
+// user, then candidate rows), each padded to a multiple of kRowPad rows; rows T..
+// are never written and only ever feed discarded GEMM output rows.
+//  xn   [T_pad][D]   normalised layer input (the projection's A operand)
+//  vqk  [T_pad][3D]  V | Q | K after SiLU and position bias
+//  aout [T_pad][3D]  U | O | bf16(U*O): the output GEMM's A operand, written by the
+//                    projection (U) and the attention (O and the gate)
 constexpr int kRowPad = 256;
 
 // Normalised layer input Xn = (X - mean) / sqrt(var + eps), per row over D.
@@ -48,13 +53,14 @@ struct NormArgs {
 constexpr float kNormEps = 1e-6f;
 
 struct UvqkArgs {
-  const void* xn;        // [T_pad][D] normalised input rows
+  const void* xn;        // [T_pad][D]
   int32_t Nu, T, D;
   const void* w;         // [4D][D]
   const void* pos;       // [max_len][3D]
   const int2* row_info;
   const UserRec* users;
-  void* uvqk;            // [T_pad][4D] out (rows < T written)
+  void* vqk;             // [T_pad][3D] out: V, Q, K (rows < T written)
+  void* aout;            // [T_pad][3D] out: U into columns [0, D)
   void* cache_k;         // this layer's [slots][cap][D] or nullptr
   void* cache_v;
 };
@@ -65,16 +71,15 @@ struct AttnArgs {
   const UserRec* users;
   int32_t Nu, D;
   float inv;             // 1 / max_len
-  const void* uvqk;      // [T][4D]: Q, and the candidates' own K, V
+  const void* vqk;       // [T_pad][3D]: Q, and the candidates' own K, V
   const void* kbase;     // key row r of user b is kbase + (key_row_b + r) * ld
   const void* vbase;
   int64_t ld;
-  void* o;               // [T_pad][D] out (rows < T written)
+  void* aout;            // [T_pad][3D]: reads U, writes O and bf16(U*O)
 };
 
 struct OutArgs {
-  const void* uvqk;      // [T_pad][4D]; U = columns [0, D)
-  const void* o;         // [T_pad][D]
+  const void* aout;      // [T_pad][3D] A operand [U | O | U*O]
   const void* w;         // [D][3D]
   const void* x_lo;      // residual rows [0, Nu)
   const void* x_hi;      // residual rows [Nu, T)

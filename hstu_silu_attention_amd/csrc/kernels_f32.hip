@@ -54,42 +54,32 @@ __device__ __forceinline__ void gemm_f32(const ALoad& aload, const float* __rest
   }
 }
 
-// The normalised layer input, as stored.
-struct XLoadF {
-  const float* xn;
-  int D;
-  __device__ __forceinline__ float operator()(int row, int k) const { return xn[(size_t)row * D + k]; }
-};
-
-struct GateLoadF {
-  const float* uvqk;
-  const float* o;
-  int D;
-  __device__ __forceinline__ float operator()(int row, int k) const {
-    const float* urow = uvqk + (size_t)row * 4 * D;
-    const float* orow = o + (size_t)row * D;
-    if (k < D) return urow[k];
-    if (k < 2 * D) return orow[k - D];
-    return urow[k - 2 * D] * orow[k - 2 * D];
-  }
+// A operands as stored: the normalised layer input, and [U | O | U*O].
+struct RowLoadF {
+  const float* base;
+  int ld;
+  __device__ __forceinline__ float operator()(int row, int k) const { return base[(size_t)row * ld + k]; }
 };
 
 __global__ __launch_bounds__(256) void uvqk_f32_kernel(UvqkArgs a) {
   const int D = a.D;
   const float* pos = (const float*)a.pos;
-  float* out = (float*)a.uvqk;
   auto epi = [&](int row, int col, float g) {
     const int2 ri = a.row_info[row];
     const int slice = col / D, cc = col - slice * D;
     float v = silu(g);
     if (slice > 0) v += pos[(size_t)ri.y * 3 * D + (slice - 1) * D + cc];
-    out[(size_t)row * 4 * D + col] = v;
+    // U into the output GEMM's operand buffer, V / Q / K into the attention's
+    if (slice == 0)
+      ((float*)a.aout)[(size_t)row * 3 * D + cc] = v;
+    else
+      ((float*)a.vqk)[(size_t)row * 3 * D + (slice - 1) * D + cc] = v;
     if (a.cache_k != nullptr && row < a.Nu && (slice == 1 || slice == 3)) {
       float* dst = (float*)(slice == 1 ? a.cache_v : a.cache_k);
       dst[((size_t)a.users[ri.x].key_row + ri.y) * D + cc] = v;
     }
   };
-  gemm_f32(XLoadF{(const float*)a.xn, D}, (const float*)a.w, D, a.T,
+  gemm_f32(RowLoadF{(const float*)a.xn, D}, (const float*)a.w, D, a.T,
            4 * D / FT, epi);
 }
 
@@ -102,7 +92,7 @@ __global__ __launch_bounds__(256) void out_f32_kernel(OutArgs a) {
       ((float*)a.y_hi)[(size_t)(row - a.Nu) * D + col] =
           ((const float*)a.x_hi)[(size_t)(row - a.Nu) * D + col] + z;
   };
-  gemm_f32(GateLoadF{(const float*)a.uvqk, (const float*)a.o, D}, (const float*)a.w, 3 * D, a.T,
+  gemm_f32(RowLoadF{(const float*)a.aout, 3 * D}, (const float*)a.w, 3 * D, a.T,
            D / FT, epi);
 }
 
@@ -125,11 +115,11 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   const bool qok = tid < nq;
   const int qi = q0 + tid;
   const size_t row = cand ? (size_t)a.Nu + u.coff + qi : (size_t)u.uoff + qi;
-  const float* uvqk = (const float*)a.uvqk;
+  const float* vqk = (const float*)a.vqk + row * 3 * D + head * DH;  // V | Q | K of this row
   float q[DH], acc[DH];
 #pragma unroll
   for (int e = 0; e < DH; ++e) {
-    q[e] = qok ? uvqk[row * 4 * D + 2 * D + head * DH + e] : 0.0f;
+    q[e] = qok ? vqk[D + e] : 0.0f;
     acc[e] = 0.0f;
   }
   const int key_end = cand ? u.m + u.n : u.m + q0 + nq;
@@ -159,8 +149,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   }
   if (!qok) return;
   if (cand) {
-    const float* krow = uvqk + row * 4 * D + 3 * D + head * DH;
-    const float* vrow = uvqk + row * 4 * D + 1 * D + head * DH;
+    const float* krow = vqk + 2 * D;
+    const float* vrow = vqk;
     float s = 0.0f;
 #pragma unroll
     for (int e = 0; e < DH; ++e) s += q[e] * krow[e];
@@ -168,9 +158,14 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < DH; ++e) acc[e] += w * vrow[e];
   }
-  float* orow = (float*)a.o + row * D + head * DH;
+  // O into columns [D, 2D) of the output GEMM's operand row, U*O into [2D, 3D)
+  float* arow = (float*)a.aout + row * 3 * D + head * DH;
 #pragma unroll
-  for (int e = 0; e < DH; ++e) orow[e] = a.inv * acc[e];
+  for (int e = 0; e < DH; ++e) {
+    const float o = a.inv * acc[e];
+    arow[D + e] = o;
+    arow[2 * D + e] = arow[e] * o;
+  }
 }
 
 }  // namespace
