@@ -183,29 +183,46 @@ void uvqk_kernel(UvqkArgs a) {
       for (int g = 0; g < 4; ++g)
         bias[i][j][g] = slice > 0 ? *reinterpret_cast<const uint2*>(prow + j * 32 + g * 8) : make_uint2(0, 0);
   }
-  // U goes to the output GEMM's operand buffer, V/Q/K to the attention's (both 3D wide)
-  u16* out = slice == 0 ? (u16*)a.aout : (u16*)a.vqk + (slice - 1) * D;
-  u16* cache = slice == 1 ? (u16*)a.cache_v : slice == 3 ? (u16*)a.cache_k : nullptr;
-  if (a.cache_k == nullptr) cache = nullptr;
+  // The finished tile goes through the (now idle) LDS: each lane writes its rounded
+  // values there, then every 32 consecutive threads store 512 contiguous bytes of one
+  // row, so the global writes are whole cache lines.
+  constexpr int OLD = C::BN + 8;                     // LDS row stride of the output tile
+  static_assert(C::BM * OLD <= 2 * C::STAGE, "output tile must fit the LDS stages");
 #pragma unroll
   for (int i = 0; i < C::MI; ++i) {
-    const int row = row0 + wm * C::TM + i * 32 + l32;
-    if (row >= a.T) continue;
-    const bool append = cache != nullptr && row < a.Nu;
-    const size_t crow = append ? (size_t)a.users[ri[i].x].key_row + ri[i].y : 0;
+    const int r = wm * C::TM + i * 32 + l32;
 #pragma unroll
     for (int j = 0; j < C::NI; ++j) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int cc = cbase + j * 32 + g * 8;
         const float v0 = silu(acc[i][j][4 * g + 0]) + bf2f_lo(bias[i][j][g].x);
         const float v1 = silu(acc[i][j][4 * g + 1]) + bf2f_hi(bias[i][j][g].x);
         const float v2 = silu(acc[i][j][4 * g + 2]) + bf2f_lo(bias[i][j][g].y);
         const float v3 = silu(acc[i][j][4 * g + 3]) + bf2f_hi(bias[i][j][g].y);
-        const uint2 pk = make_uint2(pack2(v0, v1), pack2(v2, v3));
-        *reinterpret_cast<uint2*>(out + (size_t)row * 3 * D + cc) = pk;
-        if (append) *reinterpret_cast<uint2*>(cache + crow * D + cc) = pk;
+        *reinterpret_cast<uint2*>(smem + r * OLD + wn * C::TN + j * 32 + g * 8 + hi * 4) =
+            make_uint2(pack2(v0, v1), pack2(v2, v3));
       }
+    }
+  }
+  __syncthreads();
+  // U goes to the output GEMM's operand buffer, V/Q/K to the attention's (both 3D wide);
+  // new history rows' V and K are also appended to the cache.
+  const int ccol = col0 - slice * D;
+  u16* out = (slice == 0 ? (u16*)a.aout : (u16*)a.vqk + (slice - 1) * D) + ccol;
+  u16* cache = a.cache_k == nullptr ? nullptr
+               : slice == 1 ? (u16*)a.cache_v + ccol
+               : slice == 3 ? (u16*)a.cache_k + ccol : nullptr;
+  constexpr int CPR = C::BN / 8;                     // 16-byte chunks per tile row
+#pragma unroll
+  for (int i = 0; i < C::BM * CPR / C::NT; ++i) {
+    const int c = threadIdx.x + C::NT * i, r = c / CPR, cc = (c % CPR) * 8;
+    const int row = row0 + r;
+    if (row >= a.T) continue;
+    const uint4 v = *reinterpret_cast<const uint4*>(smem + r * OLD + cc);
+    *reinterpret_cast<uint4*>(out + (size_t)row * 3 * D + cc) = v;
+    if (cache != nullptr && row < a.Nu) {
+      const int2 q = a.row_info[row];
+      *reinterpret_cast<uint4*>(cache + ((size_t)a.users[q.x].key_row + q.y) * D + cc) = v;
     }
   }
 }
