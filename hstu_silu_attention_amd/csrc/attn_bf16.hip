@@ -23,12 +23,13 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 // rows. The key order inside the PV contraction is permuted to match the layout in
 // which S^T's accumulators hold the weights; both operands use the same order.
 //
-// K rows are 8 elements longer than dh (16-byte reads of 8 consecutive rows hit
-// distinct banks); V rows 16 longer (the 4 rows of one transpose read do).
+// Row strides (measured with the LDS bank-conflict counter on gfx950): K rows of
+// dh + 8 elements make the 16-byte fragment reads conflict-free; V rows need dh + 32
+// for the transpose reads (dh + 16 costs about two cycles per read).
 template <int DH>
 struct AttnTile {
   static constexpr int BM = 128, KB = 64;
-  static constexpr int LDK = DH + 8, LDV = DH + 16;
+  static constexpr int LDK = DH + 8, LDV = DH + 32;
   static constexpr int KSZ = KB * LDK, STAGE = KB * (LDK + LDV);
   static constexpr int CPR = DH / 8;             // 16-byte chunks per key row
   static constexpr int CPT = KB * CPR / 256;     // chunks per thread per matrix
