@@ -317,6 +317,9 @@ hstu_status hstu_encode(const hstu_dims* d, int32_t B, const int32_t* uih_offset
       if (m + n > kv->capacity) return HSTU_ERR_CAPACITY;
     }
     if (m + n + 1 > d->max_len) return HSTU_ERR_CAPACITY;
+    // the attention kernel addresses one user's key rows with 32-bit byte offsets
+    if ((m + n) * (int64_t)(kv ? d->d_model : 3 * d->d_model) * (d->dtype == HSTU_F32 ? 4 : 2) > INT32_MAX)
+      return HSTU_ERR_CAPACITY;
   }
   if (!workspace || workspace_bytes < lay.total) return HSTU_ERR_WORKSPACE;
   if (((uintptr_t)workspace & (kAlign - 1)) != 0) return HSTU_ERR_ALIGN;

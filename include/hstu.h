@@ -69,7 +69,9 @@ enum hstu_status_code {
   HSTU_ERR_SHAPE = 2,      /* unsupported dims/dtype (see hstu_dims), B < 0                */
   HSTU_ERR_OFFSETS = 3,    /* offsets do not start at 0 or decrease                        */
   HSTU_ERR_CAPACITY = 4,   /* m+n >= max_len, cache capacity < m+n, bad or repeated slot,   */
-                           /* or cached_len < 0                                             */
+                           /* cached_len < 0, or one user's keys of one layer span 2 GiB or */
+                           /* more ((m+n) * row pitch in bytes; the pitch is D elements with */
+                           /* a cache, 3D without)                                          */
   HSTU_ERR_WORKSPACE = 5,  /* workspace NULL or smaller than hstu_workspace_size()          */
   HSTU_ERR_HIP = 6,        /* a HIP runtime call failed; outputs and cache are undefined    */
   HSTU_ERR_ALIGN = 7       /* a device pointer is not 16-byte aligned                       */
