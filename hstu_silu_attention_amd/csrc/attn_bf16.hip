@@ -323,25 +323,15 @@ void attn_kernel(AttnArgs a) {
       }
     }
     if (qok[qb]) {
-      // O = bf16(inv * acc) into columns [D, 2D) of the output GEMM's operand row, and
-      // the gate bf16(U * O), from this row's U (columns [0, D)), into columns [2D, 3D)
-      u16* arow = (u16*)a.aout + row[qb] * ld3 + head * DH;
-      uint2 uv[C::MB][4];
-#pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) uv[mb][i] = *reinterpret_cast<const uint2*>(arow + mb * 32 + i * 8 + hi * 4);
+      // O = bf16(inv * acc) into columns [D, 2D) of the output GEMM's operand row
+      u16* orow = (u16*)a.aout + row[qb] * ld3 + D + head * DH;
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float o0 = round_bf(a.inv * oacc[qb][mb][4 * i + 0]), o1 = round_bf(a.inv * oacc[qb][mb][4 * i + 1]);
-          const float o2 = round_bf(a.inv * oacc[qb][mb][4 * i + 2]), o3 = round_bf(a.inv * oacc[qb][mb][4 * i + 3]);
-          const int c = mb * 32 + i * 8 + hi * 4;
-          *reinterpret_cast<uint2*>(arow + D + c) = make_uint2(pack2(o0, o1), pack2(o2, o3));
-          const uint2 g = make_uint2(pack2(bf2f_lo(uv[mb][i].x) * o0, bf2f_hi(uv[mb][i].x) * o1),
-                                     pack2(bf2f_lo(uv[mb][i].y) * o2, bf2f_hi(uv[mb][i].y) * o3));
-          *reinterpret_cast<uint2*>(arow + 2 * D + c) = g;
+          const float o0 = a.inv * oacc[qb][mb][4 * i + 0], o1 = a.inv * oacc[qb][mb][4 * i + 1];
+          const float o2 = a.inv * oacc[qb][mb][4 * i + 2], o3 = a.inv * oacc[qb][mb][4 * i + 3];
+          *reinterpret_cast<uint2*>(orow + mb * 32 + i * 8 + hi * 4) = make_uint2(pack2(o0, o1), pack2(o2, o3));
         }
     }
   }

@@ -1,6 +1,7 @@
 // bfloat16 GEMMs of the encoder layer on gfx950: the uvqk projection (normalised
 // input rows x W1, SiLU + position bias + KV-cache append in the epilogue) and the
-// output GEMM ([U | O | U*O] x W2, residual in the epilogue). bf16 MFMA 32x32x16 with
+// output GEMM ([U | O | U*O] x W2 with the gate formed while staging, residual in the
+// epilogue). bf16 MFMA 32x32x16 with
 // float32 accumulation.
 #include "bf16_common.h"
 #include "hstu_internal.h"
@@ -17,7 +18,8 @@ namespace {
 // makes the 16-byte fragment reads of 8 consecutive rows hit distinct banks). The
 // next step's global loads are issued into registers before the current step's
 // MFMAs and written to the other stage after them, so each step needs one barrier.
-// Both GEMMs read their A operand as stored (the normalised input; [U | O | U*O]).
+// The projection reads its A operand as stored; the output GEMM forms the gate
+// columns of [U | O | U*O] from U and O while staging.
 template <int BM_, int BN_, int WM_, int WN_>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
@@ -34,10 +36,15 @@ struct Tile {
 
 // Thread t moves the chunks of rows t/8 + RSTEP*i (i < AC or BC), k offset (t%8)*8.
 
-// A rows read as stored (the normalised layer input): one base pointer. The buffer is
-// padded to whole tiles, so no row needs a bounds check.
+// A-operand loaders. A GEMM's K range is walked in steps of BK; a loader with PARTS
+// parts visits step t as part t % PARTS of chunk t / PARTS and says which K offset of
+// W that step multiplies (kw).
+
+// The normalised layer input, read as stored (one part): step t is columns t*BK...
+// The buffer is padded to whole tiles, so no row needs a bounds check.
 template <int AC, int RSTEP>
 struct PlainRows {
+  static constexpr int PARTS = 1;
   const u16* p;
   size_t step;
   uint4 v[AC];
@@ -45,11 +52,49 @@ struct PlainRows {
     p = base + (size_t)(row0 + (tid >> 3)) * ld + (tid & 7) * 8;
     step = (size_t)RSTEP * ld;
   }
-  __device__ __forceinline__ void fetch(int k0) {
+  __device__ __forceinline__ void fetch(int, int chunk) {
 #pragma unroll
-    for (int i = 0; i < AC; ++i) v[i] = *reinterpret_cast<const uint4*>(p + i * step + k0);
+    for (int i = 0; i < AC; ++i) v[i] = *reinterpret_cast<const uint4*>(p + i * step + chunk * 64);
   }
-  __device__ __forceinline__ uint4 get(int i, int) const { return v[i]; }
+  __device__ __forceinline__ uint4 get(int, int i) const { return v[i]; }
+  __device__ __forceinline__ int kw(int, int chunk) const { return chunk * 64; }
+};
+
+// The output GEMM's A = [U | O | U*O] with the gate formed on the fly: chunk c is
+// visited as U[c], O[c], then bf16(U[c] * O[c]) from the two chunks still held in
+// registers, so the gate is never stored. Row pitch 3D; U at column 0, O at column D.
+template <int AC, int RSTEP>
+struct GatedRows {
+  static constexpr int PARTS = 3;
+  const u16* p;
+  size_t step;
+  int D;
+  uint4 u[AC], o[AC];
+  __device__ __forceinline__ void init(const u16* base, int d, int row0, int tid) {
+    D = d;
+    p = base + (size_t)(row0 + (tid >> 3)) * 3 * d + (tid & 7) * 8;
+    step = (size_t)RSTEP * 3 * d;
+  }
+  __device__ __forceinline__ void fetch(int part, int chunk) {
+    if (part == 0) {
+#pragma unroll
+      for (int i = 0; i < AC; ++i) u[i] = *reinterpret_cast<const uint4*>(p + i * step + chunk * 64);
+    } else if (part == 1) {
+#pragma unroll
+      for (int i = 0; i < AC; ++i) o[i] = *reinterpret_cast<const uint4*>(p + i * step + D + chunk * 64);
+    }
+  }
+  __device__ __forceinline__ uint4 get(int part, int i) const {
+    if (part == 0) return u[i];
+    if (part == 1) return o[i];
+    const uint32_t uw[4] = {u[i].x, u[i].y, u[i].z, u[i].w}, ow[4] = {o[i].x, o[i].y, o[i].z, o[i].w};
+    uint32_t g[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      g[e] = pack2(bf2f_lo(uw[e]) * bf2f_lo(ow[e]), bf2f_hi(uw[e]) * bf2f_hi(ow[e]));
+    return make_uint4(g[0], g[1], g[2], g[3]);
+  }
+  __device__ __forceinline__ int kw(int part, int chunk) const { return part * D + chunk * 64; }
 };
 
 // Instruction order of one k step, pinned for the scheduler (which otherwise waits
@@ -81,6 +126,7 @@ __device__ __forceinline__ void schedule_step() {
 template <typename C, typename AL>
 __device__ __forceinline__ void gemm_tile(AL& al, const u16* __restrict__ w, int K, int col0,
                                           f32x16 (&acc)[C::MI][C::NI], u16* smem) {
+  constexpr int P = AL::PARTS;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int wm = wv / C::WN, wn = wv % C::WN, l32 = lane & 31, hi = lane >> 5;
   const int r0 = tid >> 3, kc = (tid & 7) * 8;
@@ -93,59 +139,65 @@ __device__ __forceinline__ void gemm_tile(AL& al, const u16* __restrict__ w, int
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  auto fetch = [&](int k0) {
-    al.fetch(k0);
+  auto fetch = [&](int part, int chunk) {
+    al.fetch(part, chunk);
+    const int k0 = al.kw(part, chunk);
 #pragma unroll
     for (int i = 0; i < C::BC; ++i) rb[i] = *reinterpret_cast<const uint4*>(wp + (size_t)C::RSTEP * i * K + k0);
   };
-  auto store = [&](int stage, int k0) {
+  auto store = [&](int stage, int part) {
     u16* sa = smem + stage * C::STAGE;
     u16* sb = sa + C::BM * C::LDK;
 #pragma unroll
     for (int i = 0; i < C::AC; ++i)
-      *reinterpret_cast<uint4*>(sa + (r0 + C::RSTEP * i) * C::LDK + kc) = al.get(i, k0);
+      *reinterpret_cast<uint4*>(sa + (r0 + C::RSTEP * i) * C::LDK + kc) = al.get(part, i);
 #pragma unroll
     for (int i = 0; i < C::BC; ++i) *reinterpret_cast<uint4*>(sb + (r0 + C::RSTEP * i) * C::LDK + kc) = rb[i];
   };
 
-  const int nk = K / C::BK;
-  fetch(0);
+  const int nchunk = K / C::BK / P;
+  fetch(0, 0);
   store(0, 0);
   __syncthreads();
-  for (int t = 0; t < nk; ++t) {
-    // The last step re-fetches its own k block into the idle stage: every step fetches
-    // and stores unconditionally, so the prefetch registers carry nothing across
-    // iterations and the step stays one basic block.
-    const int kn = (t + 1 < nk ? t + 1 : t) * C::BK;
-    fetch(kn);
-    const u16* sa = smem + (t & 1) * C::STAGE + (wm * C::TM + l32) * C::LDK + hi * 8;
-    const u16* sb = smem + (t & 1) * C::STAGE + C::BM * C::LDK + (wn * C::TN + l32) * C::LDK + hi * 8;
-    // Fragments double-buffered in registers: the LDS reads of sub-step kk+1 are in
-    // flight while the MFMAs of sub-step kk run.
-    bf16x8 af[2][C::MI], bw[2][C::NI];
+  for (int c = 0; c < nchunk; ++c) {
 #pragma unroll
-    for (int i = 0; i < C::MI; ++i) af[0][i] = as_bf16x8(*reinterpret_cast<const uint4*>(sa + i * 32 * C::LDK));
+    for (int part = 0; part < P; ++part) {
+      const int t = c * P + part;
+      // The next step's operands: the next part of this chunk, or part 0 of the next
+      // chunk (the last chunk's is fetched again into the idle stage, so every step
+      // fetches and stores unconditionally and stays one basic block).
+      const int np = part + 1 < P ? part + 1 : 0;
+      const int nc = part + 1 < P ? c : min(c + 1, nchunk - 1);
+      fetch(np, nc);
+      const u16* sa = smem + (t & 1) * C::STAGE + (wm * C::TM + l32) * C::LDK + hi * 8;
+      const u16* sb = smem + (t & 1) * C::STAGE + C::BM * C::LDK + (wn * C::TN + l32) * C::LDK + hi * 8;
+      // Fragments double-buffered in registers: the LDS reads of sub-step kk+1 are in
+      // flight while the MFMAs of sub-step kk run.
+      bf16x8 af[2][C::MI], bw[2][C::NI];
 #pragma unroll
-    for (int j = 0; j < C::NI; ++j) bw[0][j] = as_bf16x8(*reinterpret_cast<const uint4*>(sb + j * 32 * C::LDK));
+      for (int i = 0; i < C::MI; ++i) af[0][i] = as_bf16x8(*reinterpret_cast<const uint4*>(sa + i * 32 * C::LDK));
 #pragma unroll
-    for (int kk = 0; kk < C::BK / 16; ++kk) {
-      const int cur = kk & 1, nxt = cur ^ 1;
-      if (kk + 1 < C::BK / 16) {
+      for (int j = 0; j < C::NI; ++j) bw[0][j] = as_bf16x8(*reinterpret_cast<const uint4*>(sb + j * 32 * C::LDK));
+#pragma unroll
+      for (int kk = 0; kk < C::BK / 16; ++kk) {
+        const int cur = kk & 1, nxt = cur ^ 1;
+        if (kk + 1 < C::BK / 16) {
+#pragma unroll
+          for (int i = 0; i < C::MI; ++i)
+            af[nxt][i] = as_bf16x8(*reinterpret_cast<const uint4*>(sa + i * 32 * C::LDK + (kk + 1) * 16));
+#pragma unroll
+          for (int j = 0; j < C::NI; ++j)
+            bw[nxt][j] = as_bf16x8(*reinterpret_cast<const uint4*>(sb + j * 32 * C::LDK + (kk + 1) * 16));
+        }
 #pragma unroll
         for (int i = 0; i < C::MI; ++i)
-          af[nxt][i] = as_bf16x8(*reinterpret_cast<const uint4*>(sa + i * 32 * C::LDK + (kk + 1) * 16));
 #pragma unroll
-        for (int j = 0; j < C::NI; ++j)
-          bw[nxt][j] = as_bf16x8(*reinterpret_cast<const uint4*>(sb + j * 32 * C::LDK + (kk + 1) * 16));
+          for (int j = 0; j < C::NI; ++j) acc[i][j] = mfma32(bw[cur][j], af[cur][i], acc[i][j]);
       }
-#pragma unroll
-      for (int i = 0; i < C::MI; ++i)
-#pragma unroll
-        for (int j = 0; j < C::NI; ++j) acc[i][j] = mfma32(bw[cur][j], af[cur][i], acc[i][j]);
+      store((t + 1) & 1, np);
+      schedule_step<C>();
+      __syncthreads();
     }
-    store((t + 1) & 1, kn);
-    schedule_step<C>();
-    __syncthreads();
   }
 }
 
@@ -234,8 +286,8 @@ void out_kernel(OutArgs a) {
   const int D = a.D, ncol = D / C::BN;
   const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
   const int row0 = (tile / ncol) * C::BM, col0 = (tile % ncol) * C::BN;
-  PlainRows<C::AC, C::RSTEP> al;
-  al.init((const u16*)a.aout, 3 * D, row0, threadIdx.x);
+  GatedRows<C::AC, C::RSTEP> al;
+  al.init((const u16*)a.aout, D, row0, threadIdx.x);
   f32x16 acc[C::MI][C::NI];
   gemm_tile<C>(al, (const u16*)a.w, 3 * D, col0, acc, smem);
 

@@ -38,8 +38,10 @@ struct PlanArgs {
 // are never written and only ever feed discarded GEMM output rows.
 //  xn   [T_pad][D]   normalised layer input (the projection's A operand)
 //  vqk  [T_pad][3D]  V | Q | K after SiLU and position bias
-//  aout [T_pad][3D]  U | O | bf16(U*O): the output GEMM's A operand, written by the
-//                    projection (U) and the attention (O and the gate)
+//  aout [T_pad][3D]  U | O | U*O: the output GEMM's A operand. The projection writes
+//                    U and the attention O; the float32 attention also writes the
+//                    gate U*O, the bfloat16 output GEMM forms it from U and O while
+//                    staging (those columns stay unused)
 constexpr int kRowPad = 256;
 
 // Normalised layer input Xn = (X - mean) / sqrt(var + eps), per row over D.
@@ -75,11 +77,11 @@ struct AttnArgs {
   const void* kbase;     // key row r of user b is kbase + (key_row_b + r) * ld
   const void* vbase;
   int64_t ld;
-  void* aout;            // [T_pad][3D]: reads U, writes O and bf16(U*O)
+  void* aout;            // [T_pad][3D]: writes O (float32 also reads U, writes U*O)
 };
 
 struct OutArgs {
-  const void* aout;      // [T_pad][3D] A operand [U | O | U*O]
+  const void* aout;      // [T_pad][3D] A operand [U | O | U*O] (bfloat16: U | O read)
   const void* w;         // [D][3D]
   const void* x_lo;      // residual rows [0, Nu)
   const void* x_hi;      // residual rows [Nu, T)
