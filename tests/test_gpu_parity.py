@@ -62,9 +62,12 @@ def test_bf16_single_layer_many_tiles():
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_streaming_cache(dtype):
     """Fill each user's cache slot with its prefix (no candidates), then encode the new events
-    plus candidates against the cache; compare with the oracle doing the same, and check that
-    the GPU result equals the GPU's own one-shot encode of prefix + new events bit for bit
-    (the history mask is causal, so cached keys are exactly the recomputed ones)."""
+    plus candidates against the cache; compare with the oracle doing the same, and with the
+    GPU's own one-shot encode of prefix + new events. The cached keys are exactly the
+    recomputed ones (the history mask is causal), but the two calls sum the attention in a
+    different order: the kernel groups keys into 32-key halves counted from a key origin
+    shifted by the cached length, so agreement is to the floating-point tolerance, not bit
+    for bit."""
     torch = torch_cuda()
     D, H, L = (256, 2, 2) if dtype == "bf16" else (128, 2, 2)
     wl = workloads.make_custom(seed=401, dtype=dtype, layers=L, d_model=D, heads=H, max_len=500,
@@ -112,8 +115,10 @@ def test_streaming_cache(dtype):
     fu, fc = gpu_encode(wl, model=model, uih=full, uih_lengths=full_len)
     offs_f = workloads.lengths_to_offsets(full_len)
     new_rows = np.concatenate([fu[offs_f[b] + wl.cached_lengths[b]:offs_f[b + 1]] for b in range(B)])
-    assert np.array_equal(gu, new_rows)
-    assert np.array_equal(gc, fc)
+    eu1 = normwise_per_user(gu, new_rows, wl.uih_lengths)
+    ec1 = normwise_per_user(gc, fc, wl.cand_lengths)
+    say(f"  streaming vs one-shot {dtype}: uih={eu1:.3e} cand={ec1:.3e}")
+    assert eu1 <= tol and ec1 <= tol
 
 
 def test_uih_outputs_bit_identical_for_any_candidate_set():
