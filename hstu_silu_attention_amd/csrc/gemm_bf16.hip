@@ -216,30 +216,44 @@ void uvqk_kernel(UvqkArgs a) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int wm = wv / C::WN, wn = wv % C::WN, l32 = lane & 31, hi = lane >> 5;
   // A tile lies inside one of the U, V, Q, K column blocks (D is a multiple of BN).
-  const int slice = col0 / D, cbase = col0 - slice * D + wn * C::TN + hi * 4;
-  // Epilogue operands first: every row's position and bias values are requested
-  // before any is used, so their latencies overlap instead of adding up.
-  int2 ri[C::MI];
+  const int slice = col0 / D;
+  // The position-bias tile goes through the (now idle) LDS: every 32 consecutive
+  // threads read one row's 256 bias values as whole lines (the row's position comes
+  // from the row table), then each lane picks up the values of its accumulators.
+  constexpr int OLD = C::BN + 8;                     // LDS row stride of the staged tiles
+  static_assert(C::BM * OLD <= 2 * C::STAGE, "a staged tile must fit the LDS stages");
+  constexpr int CPR = C::BN / 8;                     // 16-byte chunks per tile row
   uint2 bias[C::MI][C::NI][4];
+  if (slice > 0) {
+    const u16* pos = (const u16*)a.pos + (slice - 1) * D + (col0 - slice * D);
 #pragma unroll
-  for (int i = 0; i < C::MI; ++i) {
-    const int row = min(row0 + wm * C::TM + i * 32 + l32, a.T - 1);
-    ri[i] = a.row_info[row];
+    for (int i = 0; i < C::BM * CPR / C::NT; ++i) {
+      const int c = threadIdx.x + C::NT * i, r = c / CPR, cc = (c % CPR) * 8;
+      const int2 q = a.row_info[min(row0 + r, a.T - 1)];
+      *reinterpret_cast<uint4*>(smem + r * OLD + cc) = *reinterpret_cast<const uint4*>(pos + (size_t)q.y * 3 * D + cc);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i) {
+      const int r = wm * C::TM + i * 32 + l32;
+#pragma unroll
+      for (int j = 0; j < C::NI; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          bias[i][j][g] = *reinterpret_cast<const uint2*>(smem + r * OLD + wn * C::TN + j * 32 + g * 8 + hi * 4);
+    }
+    __syncthreads();
+  } else {
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+      for (int j = 0; j < C::NI; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) bias[i][j][g] = make_uint2(0, 0);
   }
-#pragma unroll
-  for (int i = 0; i < C::MI; ++i) {
-    const u16* prow = (const u16*)a.pos + (size_t)ri[i].y * 3 * D + (slice > 0 ? slice - 1 : 0) * D + cbase;
-#pragma unroll
-    for (int j = 0; j < C::NI; ++j)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        bias[i][j][g] = slice > 0 ? *reinterpret_cast<const uint2*>(prow + j * 32 + g * 8) : make_uint2(0, 0);
-  }
-  // The finished tile goes through the (now idle) LDS: each lane writes its rounded
-  // values there, then every 32 consecutive threads store 512 contiguous bytes of one
-  // row, so the global writes are whole cache lines.
-  constexpr int OLD = C::BN + 8;                     // LDS row stride of the output tile
-  static_assert(C::BM * OLD <= 2 * C::STAGE, "output tile must fit the LDS stages");
+  // The finished tile goes through the LDS too: each lane writes its rounded values
+  // there, then every 32 consecutive threads store 512 contiguous bytes of one row, so
+  // the global writes are whole cache lines.
 #pragma unroll
   for (int i = 0; i < C::MI; ++i) {
     const int r = wm * C::TM + i * 32 + l32;
@@ -264,7 +278,6 @@ void uvqk_kernel(UvqkArgs a) {
   u16* cache = a.cache_k == nullptr ? nullptr
                : slice == 1 ? (u16*)a.cache_v + ccol
                : slice == 3 ? (u16*)a.cache_k + ccol : nullptr;
-  constexpr int CPR = C::BN / 8;                     // 16-byte chunks per tile row
 #pragma unroll
   for (int i = 0; i < C::BM * CPR / C::NT; ++i) {
     const int c = threadIdx.x + C::NT * i, r = c / CPR, cc = (c % CPR) * 8;
@@ -293,35 +306,48 @@ void out_kernel(OutArgs a) {
 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int wm = wv / C::WN, wn = wv % C::WN, l32 = lane & 31, hi = lane >> 5;
-  const int cbase = col0 + wn * C::TN + hi * 4;
-  // Residual operands first, all requested before any is used.
-  uint2 xres[C::MI][C::NI][4];
+  // The residual tile comes into the (now idle) LDS as whole lines (every 32
+  // consecutive threads read 512 contiguous bytes of one row); each lane adds its
+  // accumulators to its own elements there, rounds, and writes them back in place;
+  // then the tile leaves as whole lines too.
+  constexpr int OLD = C::BN + 8;                     // LDS row stride of the staged tile
+  static_assert(C::BM * OLD <= 2 * C::STAGE, "the staged tile must fit the LDS stages");
+  constexpr int CPR = C::BN / 8;                     // 16-byte chunks per tile row
+  auto xrow = [&](int row) {
+    return row < a.Nu ? (const u16*)a.x_lo + (size_t)row * D : (const u16*)a.x_hi + (size_t)(row - a.Nu) * D;
+  };
 #pragma unroll
-  for (int i = 0; i < C::MI; ++i) {
-    const int row = min(row0 + wm * C::TM + i * 32 + l32, a.T - 1);
-    const u16* x = row < a.Nu ? (const u16*)a.x_lo + (size_t)row * D : (const u16*)a.x_hi + (size_t)(row - a.Nu) * D;
-#pragma unroll
-    for (int j = 0; j < C::NI; ++j)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) xres[i][j][g] = *reinterpret_cast<const uint2*>(x + cbase + j * 32 + g * 8);
+  for (int i = 0; i < C::BM * CPR / C::NT; ++i) {
+    const int c = threadIdx.x + C::NT * i, r = c / CPR, cc = (c % CPR) * 8;
+    *reinterpret_cast<uint4*>(smem + r * OLD + cc) =
+        *reinterpret_cast<const uint4*>(xrow(min(row0 + r, a.T - 1)) + col0 + cc);
   }
+  __syncthreads();
 #pragma unroll
   for (int i = 0; i < C::MI; ++i) {
-    const int row = row0 + wm * C::TM + i * 32 + l32;
-    if (row >= a.T) continue;
-    u16* y = row < a.Nu ? (u16*)a.y_lo + (size_t)row * D : (u16*)a.y_hi + (size_t)(row - a.Nu) * D;
+    const int r = wm * C::TM + i * 32 + l32;
 #pragma unroll
     for (int j = 0; j < C::NI; ++j) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const uint2 xv = xres[i][j][g];
+        uint2* p = reinterpret_cast<uint2*>(smem + r * OLD + wn * C::TN + j * 32 + g * 8 + hi * 4);
+        const uint2 xv = *p;
         const float y0 = bf2f_lo(xv.x) + acc[i][j][4 * g + 0];
         const float y1 = bf2f_hi(xv.x) + acc[i][j][4 * g + 1];
         const float y2 = bf2f_lo(xv.y) + acc[i][j][4 * g + 2];
         const float y3 = bf2f_hi(xv.y) + acc[i][j][4 * g + 3];
-        *reinterpret_cast<uint2*>(y + cbase + j * 32 + g * 8) = make_uint2(pack2(y0, y1), pack2(y2, y3));
+        *p = make_uint2(pack2(y0, y1), pack2(y2, y3));
       }
     }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < C::BM * CPR / C::NT; ++i) {
+    const int c = threadIdx.x + C::NT * i, r = c / CPR, cc = (c % CPR) * 8;
+    const int row = row0 + r;
+    if (row >= a.T) continue;
+    u16* y = row < a.Nu ? (u16*)a.y_lo + (size_t)row * D : (u16*)a.y_hi + (size_t)(row - a.Nu) * D;
+    *reinterpret_cast<uint4*>(y + col0 + cc) = *reinterpret_cast<const uint4*>(smem + r * OLD + cc);
   }
 }
 
