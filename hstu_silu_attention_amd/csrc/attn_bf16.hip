@@ -10,17 +10,27 @@ namespace {
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 // One work item = (user, head, up to 128 query rows of one kind): four waves of QB
 // blocks of 32 query rows each; two work items share a CU, so every SIMD runs two
-// independent waves that hide each other's stalls. Keys advance 64 at a time through
-// two LDS stages; K and V are staged row-major with 16-byte buffer loads whose range
-// check returns zero for keys outside the user's [0, key_end).
+// independent waves that hide each other's stalls.
+//
+// Keys advance 64 at a time (a "block"). K and V blocks go from global memory straight
+// into LDS (buffer loads with the LDS destination; their range check returns zero for
+// keys outside the user's [0, key_end)), each into a ring of two slots. A slot holds
+// its 64 rows unpadded, with the 16-byte chunks of a row permuted by an XOR of the row
+// index (k_swz, v_swz) so the fragment reads below hit distinct banks. Each block has
+// one barrier, after its first step; right after it a wave requests K of block b+2 and
+// V of block b+1 (into the slots of K(b) and V(b-1), whose last reads came before the
+// barrier) and waits for them at the next block's barrier, two steps later. The slots
+// are separate arrays and the block loop is unrolled by two, so every access names its
+// slot statically and the compiler never stalls an LDS read on an unrelated load.
 //
 // Per 32-key "half" h a wave computes, for each of its query blocks, S^T = K Q^T
 // (queries along lanes), the bf16 weights a = SiLU(s), and O^T += V^T A^T; every K
 // and V fragment read from LDS feeds all QB blocks. The V^T operand comes from the
-// row-major V stage by the LDS transpose read: in each 16-lane group, lanes 4r..4r+3
+// row-major V slot by the LDS transpose read: in each 16-lane group, lanes 4r..4r+3
 // address 16 consecutive columns of key row r and lane i receives column i of those
 // four rows. The key order inside the PV contraction is permuted to match the layout
 // in which S^T's accumulators hold the weights; both operands use it.
@@ -41,27 +51,52 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 // and a short pass after it adds the diagonal halves with a per-element mask.
 // Candidate rows take bias 0 everywhere (keys past the last history key are zero, and
 // SiLU(0) = 0) and add their own key in the epilogue.
-//
-// QB = 2 (64 rows per wave, one wave per SIMD, half the LDS reads per score) also
-// compiles; on gfx950 it measured slower, a single wave per SIMD exposing its own
-// dependency stalls.
-//
-// Row strides (measured with the LDS bank-conflict counter on gfx950): K rows of
-// dh + 8 elements make the 16-byte fragment reads conflict-free; V rows need dh + 32
-// for the transpose reads.
 template <int DH>
 struct AttnTile {
   static constexpr int WAVES = 4, NT = 64 * WAVES, QB = 1;
   static constexpr int BM = WAVES * QB * 32;     // query rows per work item
-  static constexpr int KB = 64;                  // keys per LDS stage
-  static constexpr int LDK = DH + 8, LDV = DH + 32;
-  static constexpr int KSZ = KB * LDK, STAGE = KB * (LDK + LDV);
+  static constexpr int KB = 64;                  // keys per block
+  static constexpr int SLOT = KB * DH;           // elements of one K or V slot
   static constexpr int CPR = DH / 8;             // 16-byte chunks per key row
-  static constexpr int CPT = KB * CPR / NT;      // chunks per thread per matrix
+  static constexpr int RPI = 64 / CPR;           // rows one 64-lane LDS load covers
+  static constexpr int IPW = KB / RPI / WAVES;   // such loads per wave per matrix and block
   static constexpr int KK = DH / 16, MB = DH / 32;
 };
 
 constexpr uint32_t kBufferWord3 = 0x00020000u;   // raw buffer, 32-bit data format
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor: base address, no stride, num_records bytes (loads at or past
+// it return zero).
+__device__ __forceinline__ i32x4 buffer_desc(const void* base, int num_records) {
+  const uint64_t a = (uint64_t)base;
+  return i32x4{(int)(uint32_t)a, (int)(uint32_t)(a >> 32) & 0xffff, num_records, (int)kBufferWord3};
+}
+
+// One 64-lane load of 16 bytes per lane from the buffer at byte offset voff into LDS
+// at lds_addr + 16 * lane. Written out so the compiler does not track it: it would
+// otherwise make LDS reads of other slots wait for it. The kernel waits for these loads
+// itself (vmcnt, then a barrier) before any wave reads the rows they bring. M0 holds
+// the LDS address and needs one wait state before the load reads it.
+__device__ __forceinline__ void lds_load16(const i32x4& desc, uint32_t lds_addr, int voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds_addr), "v"(voff), "s"(desc)
+      : "memory", "m0");
+}
+
+// Chunk permutations of the slots. gfx950's LDS has 64 four-byte banks; a 16-byte read
+// is served 16 lanes at a time (16 consecutive K rows of one fragment) and a transpose
+// read 32 lanes at a time (4 V rows x 4 chunks), so each group must cover distinct
+// 16-byte bank groups.
+template <int DH>
+__device__ __forceinline__ int k_swz(int r) { return DH == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int DH>
+__device__ __forceinline__ int v_swz(int r) { return DH == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
 __device__ __forceinline__ float silu_bias(float x, float nlog2e, float bias) {
   return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(__builtin_fmaf(x, nlog2e, bias)));
@@ -71,7 +106,7 @@ template <int DH>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_kernel(AttnArgs a) {
   using C = AttnTile<DH>;
-  __shared__ __attribute__((aligned(16))) u16 smem[2 * C::STAGE];
+  __shared__ __attribute__((aligned(16))) u16 ks0[C::SLOT], ks1[C::SLOT], vs0[C::SLOT], vs1[C::SLOT];
 
   const int2 bin = a.bins[blockIdx.x % kXcds];
   if ((int)(blockIdx.x / kXcds) >= bin.y) return;
@@ -84,7 +119,7 @@ void attn_kernel(AttnArgs a) {
   const int D = a.D;
   const size_t ld3 = 3 * (size_t)D;
 
-  // this lane's two query rows (one per query block)
+  // this lane's query rows (one per query block)
   bool qok[C::QB];
   size_t row[C::QB];
   bf16x8 qf[C::QB][C::KK];
@@ -103,7 +138,7 @@ void attn_kernel(AttnArgs a) {
   const int key_end = cand ? u.m + u.n : u.m + q0 + nq;  // keys [0, key_end)
   const int shift = cand ? 0 : (-u.m) & 31;               // kappa = key + shift
   const int nblk = (key_end + shift + C::KB - 1) / C::KB;
-  const int wf = u.m + q0 + wv * 32 * C::QB + shift;              // kappa of this wave's first row (history)
+  const int wf = u.m + q0 + wv * 32 * C::QB + shift;      // kappa of this wave's first row (history)
 
   f32x16 oacc[C::QB][C::MB];
 #pragma unroll
@@ -117,61 +152,51 @@ void attn_kernel(AttnArgs a) {
   // rows outside [0, key_end) read as zero
   const int ld = (int)a.ld;
   const int nbytes = key_end * ld * 2;
-  const __amdgpu_buffer_rsrc_t rk_src = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const u16*)a.kbase + (size_t)u.key_row * a.ld + head * DH), (short)0, nbytes, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t rv_src = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((const u16*)a.vbase + (size_t)u.key_row * a.ld + head * DH), (short)0, nbytes, kBufferWord3);
-  auto load_row_chunk = [&](const __amdgpu_buffer_rsrc_t& src, int key, int col) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(src, (key * ld + col) * 2, 0, 0);
-    return make_uint4(v[0], v[1], v[2], v[3]);
-  };
+  const i32x4 rk_src = buffer_desc((const u16*)a.kbase + (size_t)u.key_row * a.ld + head * DH, nbytes);
+  const i32x4 rv_src = buffer_desc((const u16*)a.vbase + (size_t)u.key_row * a.ld + head * DH, nbytes);
 
-  // staging: thread t moves chunk t + NT*i (i < CPT): key row c / CPR, column (c % CPR) * 8
-  uint4 rk[C::CPT], rv[C::CPT];
-  auto fetch = [&](int blk) {
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int c = tid + C::NT * i, key = blk * C::KB + c / C::CPR - shift, col = (c % C::CPR) * 8;
-      rk[i] = load_row_chunk(rk_src, key, col);
-      rv[i] = load_row_chunk(rv_src, key, col);
-    }
+  // 64-lane LDS loads: load j of a region covers rows RPI*j.. of it; lane i brings the
+  // global chunk that belongs at row RPI*j + i/CPR, slot i%CPR
+  auto lds_rows = [&](const i32x4& src, u16* dst, int key0, int j, bool is_v) {
+    const int r = C::RPI * j + lane / C::CPR, slot = lane % C::CPR;
+    const int chunk = slot ^ (is_v ? v_swz<DH>(r) : k_swz<DH>(r));
+    const uint32_t addr = (uint32_t)(uintptr_t)(lds_void*)(dst + j * 512);
+    lds_load16(src, __builtin_amdgcn_readfirstlane(addr), ((key0 + r) * ld + chunk * 8) * 2);
   };
-  auto store = [&](int stage) {
-    u16* sk = smem + stage * C::STAGE;
-    u16* sv = sk + C::KSZ;
+  auto load_k = [&](u16* slot, int blk) {
 #pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int c = tid + C::NT * i, r = c / C::CPR, col = (c % C::CPR) * 8;
-      *reinterpret_cast<uint4*>(sk + r * C::LDK + col) = rk[i];
-      *reinterpret_cast<uint4*>(sv + r * C::LDV + col) = rv[i];
-    }
+    for (int i = 0; i < C::IPW; ++i) lds_rows(rk_src, slot, blk * C::KB - shift, wv + C::WAVES * i, false);
   };
+  auto load_v = [&](u16* slot, int blk) {
+#pragma unroll
+    for (int i = 0; i < C::IPW; ++i) lds_rows(rv_src, slot, blk * C::KB - shift, wv + C::WAVES * i, true);
+  };
+  // every LDS load of this wave has landed
+  auto wait_loads = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
   // LDS fragments: K rows for the scores, V^T columns for PV (weight chunk c, element
   // e <-> key 16c + 8*(e/4) + 4*hi + e%4 of the half; the transpose reads fetch V rows
   // 16c + 4*hi + r and + 8)
   const int tr_row = 4 * hi + ((lane & 15) >> 2);
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1), tr_off = 4 * (lane & 1);
   auto read_k_at = [&](const u16* rows, bf16x8 (&kf)[C::KK]) {   // rows: key row 0 of the half
-    const u16* sk = rows + l32 * C::LDK + hi * 8;
+    const u16* sk = rows + l32 * DH;
 #pragma unroll
-    for (int kk = 0; kk < C::KK; ++kk) kf[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(sk + kk * 16));
+    for (int kk = 0; kk < C::KK; ++kk)
+      kf[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(sk + (((2 * kk + hi) ^ k_swz<DH>(l32)) * 8)));
   };
   auto read_v_at = [&](const u16* rows, bf16x8 (&vf)[2][C::MB]) {
-    const u16* sv = rows + tr_row * C::LDV + tr_col;
+    const int sw = v_swz<DH>(tr_row);
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb) {
-        const u16* p = sv + 16 * c * C::LDV + mb * 32;
+        const u16* p = rows + (16 * c + tr_row) * DH + ((tr_chunk + 4 * mb) ^ sw) * 8 + tr_off;
         const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
-        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 8 * C::LDV));
+        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 8 * DH));
         vf[c][mb] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
       }
   };
-  // half h lives in stage (h / 2) % 2 at rows 32 * (h % 2) ("half -1": stage 1, rows 32..)
-  auto k_rows = [&](int h) { return smem + ((h >> 1) & 1) * C::STAGE + (h & 1) * 32 * C::LDK; };
-  auto v_rows = [&](int h) { return smem + ((h >> 1) & 1) * C::STAGE + C::KSZ + (h & 1) * 32 * C::LDV; };
 
   // S^T = K Q^T for query block qb; s[4*i + j] = q . k(key 8*i + 4*hi + j of the half)
   auto score_mfma = [&](const bf16x8 (&kf)[C::KK], int qb, f32x16& s) {
@@ -194,11 +219,16 @@ void attn_kernel(AttnArgs a) {
 
   // Step h: (si, wi) = scores of half h, weights of half h - 1 -> (so, wo) = scores of
   // half h + 1, weights of half h.
-  auto body = [&](int h, const f32x16 (&si)[C::QB], const bf16x8 (&wi)[C::QB][2], f32x16 (&so)[C::QB], bf16x8 (&wo)[C::QB][2]) {
+  // krows / vrows: the 32 K rows of half h + 1 and the 32 V rows of half h - 1
+  // after_reads runs once the step's fragment reads are issued
+  auto body = [&](int h, const u16* krows, const u16* vrows, const f32x16 (&si)[C::QB], const bf16x8 (&wi)[C::QB][2],
+                  f32x16 (&so)[C::QB], bf16x8 (&wo)[C::QB][2], auto after_reads) {
     bf16x8 kf[C::KK], vf[2][C::MB];
-    read_k_at(k_rows(h + 1), kf);
-    read_v_at(v_rows(h - 1), vf);
+    read_k_at(krows, kf);
+    read_v_at(vrows, vf);
     __builtin_amdgcn_sched_barrier(0);   // every fragment read goes out before the step's math
+    after_reads();
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int qb = 0; qb < C::QB; ++qb) score_mfma(kf, qb, so[qb]);
 #pragma unroll
@@ -221,14 +251,14 @@ void attn_kernel(AttnArgs a) {
     }
   };
 
-  // V rows of "half -1" are multiplied by the zero weights of the first step: make
-  // them finite
-  {
-    u16* sv = smem + C::STAGE + C::KSZ;
-    for (int i = tid; i < C::KB * C::LDV / 8; i += C::NT) *reinterpret_cast<uint4*>(sv + 8 * i) = make_uint4(0, 0, 0, 0);
-  }
-  fetch(0);
-  store(0);
+  // V rows of "half -1" (V slot 1, rows 32..63) are multiplied by the zero weights of
+  // the first step: make them finite
+  for (int i = tid; i < 32 * DH / 8; i += C::NT)
+    *reinterpret_cast<uint4*>(vs1 + 32 * DH + 8 * i) = make_uint4(0, 0, 0, 0);
+  load_k(ks0, 0);
+  load_k(ks1, 1);
+  load_v(vs0, 0);
+  wait_loads();
   __syncthreads();
   // ping-pong state: (sA, wA) enters the even steps, (sB, wB) the odd ones
   f32x16 sA[C::QB], sB[C::QB];
@@ -237,52 +267,62 @@ void attn_kernel(AttnArgs a) {
   for (int qb = 0; qb < C::QB; ++qb) wA[qb][0] = wA[qb][1] = as_bf16x8(make_uint4(0, 0, 0, 0));
   {
     bf16x8 kf[C::KK];
-    read_k_at(k_rows(0), kf);
+    read_k_at(ks0, kf);
 #pragma unroll
     for (int qb = 0; qb < C::QB; ++qb) score_mfma(kf, qb, sA[qb]);
   }
-  for (int b = 0; b < nblk; ++b) {
-    // the last block re-fetches itself into the idle stage (unconditional steps keep
-    // the loop body free of branches)
-    fetch(b + 1 < nblk ? b + 1 : b);
-    body(2 * b, sA, wA, sB, wB);       // K of block b, V of block b - 1
-    __syncthreads();                   // every wave is past its reads of block b - 1
-    store((b + 1) & 1);
-    __syncthreads();                   // block b + 1 visible
-    body(2 * b + 1, sB, wB, sA, wA);   // K of block b + 1, V of block b
+  // Block b with its K in kb (the other K slot holds block b + 1) and its V in vb (the
+  // other V slot holds block b - 1).
+  auto block = [&](int b, u16* kb, u16* kn, u16* vb, u16* vp) {
+    body(2 * b, kb + 32 * DH, vp + 32 * DH, sA, wA, sB, wB, [] {});   // K rows of half 2b+1, V of half 2b-1
+    wait_loads();                      // this wave's K(b + 1) and V(b) have landed
+    __syncthreads();                   // ... everyone's; K(b) and V(b - 1) are no longer read
+    body(2 * b + 1, kn, vb, sB, wB, sA, wA, [&] {                  // K rows of half 2b+2, V of half 2b
+      load_k(kb, b + 2);               // past the last block these rows read as zero
+      load_v(vp, b + 1);
+    });
+  };
+  int b = 0;
+  for (; b + 1 < nblk; b += 2) {
+    block(b, ks0, ks1, vs0, vs1);
+    block(b + 1, ks1, ks0, vs1, vs0);
   }
+  if (b < nblk) block(b, ks0, ks1, vs0, vs1);
   if (nblk > 0) {
-    // PV of the last half (its weights are in wA)
+    // PV of the last half (its weights are in wA): V of block nblk - 1, rows 32..
     bf16x8 vf[2][C::MB];
-    read_v_at(v_rows(2 * nblk - 1), vf);
+    read_v_at(((nblk - 1) & 1 ? vs1 : vs0) + 32 * DH, vf);
 #pragma unroll
     for (int qb = 0; qb < C::QB; ++qb) pv_mfma(vf, qb, wA[qb]);
   }
 
   if (!cand) {
-    // The diagonal half of each history block, in a private LDS area per wave: key
-    // offset j of the half is visible to row offset i when j <= i.
-    u16* dk = smem + wv * 32 * (C::LDK + C::LDV);
-    u16* dv = dk + 32 * C::LDK;
+    // The diagonal half of each history block, in a private LDS area per wave (32 K
+    // rows, then 32 V rows, laid out like the slots): key offset j of the half is
+    // visible to row offset i when j <= i.
+    static_assert(C::WAVES == 4 && 64 * DH == C::SLOT, "one slot per wave for the diagonal pass");
+    u16* dk = wv == 0 ? ks0 : wv == 1 ? ks1 : wv == 2 ? vs0 : vs1;
+    u16* dv = dk + 32 * DH;
 #pragma unroll
     for (int qb = 0; qb < C::QB; ++qb) {
-      __syncthreads();   // the stages (or the previous block's area) are free
+      wait_loads();
+      __syncthreads();   // the slots (or the previous block's area) are free
       const int k0 = wf + 32 * qb - shift;   // key of the half's first row
 #pragma unroll
-      for (int i = 0; i < C::CPR / 2; ++i) {
-        const int c = lane + 64 * i, r = c / C::CPR, col = (c % C::CPR) * 8;
-        *reinterpret_cast<uint4*>(dk + r * C::LDK + col) = load_row_chunk(rk_src, k0 + r, col);
-        *reinterpret_cast<uint4*>(dv + r * C::LDV + col) = load_row_chunk(rv_src, k0 + r, col);
+      for (int j = 0; j < 32 / C::RPI; ++j) {
+        lds_rows(rk_src, dk, k0, j, false);
+        lds_rows(rv_src, dv, k0, j, true);
       }
+      wait_loads();
       __syncthreads();
       bf16x8 kf[C::KK], vf[2][C::MB], w[2];
-      f32x16 s;
+      f32x16 sd;
       read_k_at(dk, kf);
-      score_mfma(kf, qb, s);
+      score_mfma(kf, qb, sd);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int j = 8 * (e >> 2) + 4 * hi + (e & 3);
-        w[e >> 3][e & 7] = (__bf16)silu_bias(s[e], nlog2e, j <= l32 ? 0.0f : kInf);
+        w[e >> 3][e & 7] = (__bf16)silu_bias(sd[e], nlog2e, j <= l32 ? 0.0f : kInf);
       }
       read_v_at(dv, vf);
       pv_mfma(vf, qb, w);
