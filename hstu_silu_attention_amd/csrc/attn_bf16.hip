@@ -220,34 +220,54 @@ void attn_kernel(AttnArgs a) {
   // Step h: (si, wi) = scores of half h, weights of half h - 1 -> (so, wo) = scores of
   // half h + 1, weights of half h.
   // krows / vrows: the 32 K rows of half h + 1 and the 32 V rows of half h - 1
-  // after_reads runs once the step's fragment reads are issued
+  // after_reads runs once the step's K fragment reads are issued. The V fragments are
+  // read after the score MFMAs have consumed the K fragments, so the two sets never
+  // occupy registers at the same time.
   auto body = [&](int h, const u16* krows, const u16* vrows, const f32x16 (&si)[C::QB], const bf16x8 (&wi)[C::QB][2],
                   f32x16 (&so)[C::QB], bf16x8 (&wo)[C::QB][2], auto after_reads) {
-    bf16x8 kf[C::KK], vf[2][C::MB];
+    bf16x8 kf[C::KK];
     read_k_at(krows, kf);
-    read_v_at(vrows, vf);
-    __builtin_amdgcn_sched_barrier(0);   // every fragment read goes out before the step's math
+    __builtin_amdgcn_sched_barrier(0);
     after_reads();
     __builtin_amdgcn_sched_barrier(0);
+    // score MFMAs with the first half of the SiLU work
 #pragma unroll
     for (int qb = 0; qb < C::QB; ++qb) score_mfma(kf, qb, so[qb]);
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) {
+      const float b = bias(h, qb);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wo[qb][e >> 3][e & 7] = (__bf16)silu_bias(si[qb][e], nlog2e, b);
+    }
+    {
+      constexpr unsigned MFMA = 0x008, VALU = 0x002;
+      __builtin_amdgcn_sched_group_barrier(VALU, 8, 0);
+#pragma unroll
+      for (int i = 0; i < C::QB * C::KK; ++i) {
+        __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(VALU, 5, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 vf[2][C::MB];
+    read_v_at(vrows, vf);
 #pragma unroll
     for (int qb = 0; qb < C::QB; ++qb) pv_mfma(vf, qb, wi[qb]);
 #pragma unroll
     for (int qb = 0; qb < C::QB; ++qb) {
       const float b = bias(h, qb);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) wo[qb][e >> 3][e & 7] = (__bf16)silu_bias(si[qb][e], nlog2e, b);
+      for (int e = 8; e < 16; ++e) wo[qb][e >> 3][e & 7] = (__bf16)silu_bias(si[qb][e], nlog2e, b);
     }
-    // SiLU work first (its inputs are ready while the reads are in flight), then each
-    // MFMA followed by a share of the rest
-    constexpr unsigned MFMA = 0x008, VALU = 0x002;
-    constexpr int kMfma = C::QB * (C::KK + 2 * C::MB);
-    __builtin_amdgcn_sched_group_barrier(VALU, 16, 0);
+    {
+      constexpr unsigned MFMA = 0x008, VALU = 0x002, DS_READ = 0x100;
+      __builtin_amdgcn_sched_group_barrier(DS_READ, 4 * C::MB, 0);
+      __builtin_amdgcn_sched_group_barrier(VALU, 12, 0);
 #pragma unroll
-    for (int i = 0; i < kMfma; ++i) {
-      __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(VALU, 5, 0);
+      for (int i = 0; i < C::QB * 2 * C::MB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(VALU, 4, 0);
+      }
     }
   };
 
