@@ -1,5 +1,6 @@
-// bfloat16 GEMMs of the encoder layer on gfx950: the uvqk projection (normalised
-// input rows x W1, SiLU + position bias + KV-cache append in the epilogue) and the
+// bfloat16 GEMMs of the encoder layer on gfx950: the uvqk projection (layer input rows
+// x W1 with the row normalisation applied to the product, SiLU + position bias +
+// KV-cache append in the epilogue) and the
 // output GEMM ([U | O | U*O] x W2 with the gate formed while staging, residual in the
 // epilogue). bf16 MFMA 32x32x16 with
 // float32 accumulation.
@@ -18,8 +19,9 @@ namespace {
 // makes the 16-byte fragment reads of 8 consecutive rows hit distinct banks). The
 // next step's global loads are issued into registers before the current step's
 // MFMAs and written to the other stage after them, so each step needs one barrier.
-// The projection reads its A operand as stored; the output GEMM forms the gate
-// columns of [U | O | U*O] from U and O while staging.
+// The projection reads the layer input rows as stored and gathers their statistics
+// while staging; the output GEMM forms the gate columns of [U | O | U*O] from U and O
+// while staging.
 template <int BM_, int BN_, int WM_, int WN_>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
@@ -56,13 +58,31 @@ struct PlainRows {
 #pragma unroll
     for (int i = 0; i < AC; ++i) v[i] = *reinterpret_cast<const uint4*>(p + i * step + chunk * 64);
   }
-  __device__ __forceinline__ uint4 get(int, int i) const { return v[i]; }
+  __device__ __forceinline__ uint4 get(int, int i, float) const { return v[i]; }
   __device__ __forceinline__ int kw(int, int chunk) const { return chunk * 64; }
 };
 
-// The output GEMM's A = [U | O | U*O] with the gate formed on the fly: chunk c is
-// visited as U[c], O[c], then bf16(U[c] * O[c]) from the two chunks still held in
-// registers, so the gate is never stored. Row pitch 3D; U at column 0, O at column D.
+// The layer input rows X as stored (one part), rows [0, Nu) from x_lo and [Nu, T) from
+// x_hi (rows past T repeat row T-1; their results are discarded).
+template <int AC, int RSTEP>
+struct SplitRows {
+  static constexpr int PARTS = 1;
+  const u16* p[AC];
+  uint4 v[AC];
+  __device__ __forceinline__ void init(const void* x_lo, const void* x_hi, int Nu, int T, int D, int row0, int tid) {
+#pragma unroll
+    for (int i = 0; i < AC; ++i) {
+      const int row = min(row0 + (tid >> 3) + RSTEP * i, T - 1);
+      p[i] = (row < Nu ? (const u16*)x_lo + (size_t)row * D : (const u16*)x_hi + (size_t)(row - Nu) * D) + (tid & 7) * 8;
+    }
+  }
+  __device__ __forceinline__ void fetch(int, int chunk) {
+#pragma unroll
+    for (int i = 0; i < AC; ++i) v[i] = *reinterpret_cast<const uint4*>(p[i] + chunk * 64);
+  }
+  __device__ __forceinline__ uint4 get(int, int i, float) const { return v[i]; }
+  __device__ __forceinline__ int kw(int, int chunk) const { return chunk * 64; }
+};
 template <int AC, int RSTEP>
 struct GatedRows {
   static constexpr int PARTS = 3;
@@ -84,7 +104,7 @@ struct GatedRows {
       for (int i = 0; i < AC; ++i) o[i] = *reinterpret_cast<const uint4*>(p + i * step + D + chunk * 64);
     }
   }
-  __device__ __forceinline__ uint4 get(int part, int i) const {
+  __device__ __forceinline__ uint4 get(int part, int i, float) const {
     if (part == 0) return u[i];
     if (part == 1) return o[i];
     const uint32_t uw[4] = {u[i].x, u[i].y, u[i].z, u[i].w}, ow[4] = {o[i].x, o[i].y, o[i].z, o[i].w};
@@ -145,19 +165,19 @@ __device__ __forceinline__ void gemm_tile(AL& al, const u16* __restrict__ w, int
 #pragma unroll
     for (int i = 0; i < C::BC; ++i) rb[i] = *reinterpret_cast<const uint4*>(wp + (size_t)C::RSTEP * i * K + k0);
   };
-  auto store = [&](int stage, int part) {
+  auto store = [&](int stage, int part, float fresh) {
     u16* sa = smem + stage * C::STAGE;
     u16* sb = sa + C::BM * C::LDK;
 #pragma unroll
     for (int i = 0; i < C::AC; ++i)
-      *reinterpret_cast<uint4*>(sa + (r0 + C::RSTEP * i) * C::LDK + kc) = al.get(part, i);
+      *reinterpret_cast<uint4*>(sa + (r0 + C::RSTEP * i) * C::LDK + kc) = al.get(part, i, fresh);
 #pragma unroll
     for (int i = 0; i < C::BC; ++i) *reinterpret_cast<uint4*>(sb + (r0 + C::RSTEP * i) * C::LDK + kc) = rb[i];
   };
 
   const int nchunk = K / C::BK / P;
   fetch(0, 0);
-  store(0, 0);
+  store(0, 0, 1.0f);
   __syncthreads();
   for (int c = 0; c < nchunk; ++c) {
 #pragma unroll
@@ -194,7 +214,7 @@ __device__ __forceinline__ void gemm_tile(AL& al, const u16* __restrict__ w, int
 #pragma unroll
           for (int j = 0; j < C::NI; ++j) acc[i][j] = mfma32(bw[cur][j], af[cur][i], acc[i][j]);
       }
-      store((t + 1) & 1, np);
+      store((t + 1) & 1, np, part + 1 < P || c + 1 < nchunk ? 1.0f : 0.0f);
       schedule_step<C>();
       __syncthreads();
     }
@@ -208,13 +228,52 @@ void uvqk_kernel(UvqkArgs a) {
   const int D = a.D, N = 4 * D, ncol = N / C::BN;
   const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
   const int row0 = (tile / ncol) * C::BM, col0 = (tile % ncol) * C::BN;
-  PlainRows<C::AC, C::RSTEP> al;
-  al.init((const u16*)a.xn, D, row0, threadIdx.x);
+  __shared__ float2 row_norm[C::BM];                 // {mean, 1/sqrt(var + eps)} per tile row
+  SplitRows<C::AC, C::RSTEP> al;
+  al.init(a.x_lo, a.x_hi, a.Nu, a.T, D, row0, threadIdx.x);
   f32x16 acc[C::MI][C::NI];
   gemm_tile<C>(al, (const u16*)a.w, D, col0, acc, smem);
 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int wm = wv / C::WN, wn = wv % C::WN, l32 = lane & 31, hi = lane >> 5;
+  // Row statistics from the per-128-column partial sums, added in column order.
+  for (int r = threadIdx.x; r < C::BM; r += C::NT) {
+    const float2* sp = a.st + (size_t)min(row0 + r, a.T - 1) * (D / 128);
+    float s1 = 0.0f, s2 = 0.0f;
+    for (int g = 0; g < D / 128; ++g) {
+      const float2 v = sp[g];
+      s1 += v.x;
+      s2 += v.y;
+    }
+    const float mean = s1 / (float)D;
+    const float var = fmaxf(s2 / (float)D - mean * mean, 0.0f);
+    row_norm[r] = make_float2(mean, 1.0f / sqrtf(var + kNormEps));
+  }
+  // Column sums of W1 for this lane's columns: the normalisation is applied to the
+  // product, Xn W1 = rstd * (X W1 - mean * colsum(W1)) row by row, exactly.
+  float csum[C::NI][4][4];
+#pragma unroll
+  for (int j = 0; j < C::NI; ++j)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float4 c4 = *reinterpret_cast<const float4*>(a.cs + col0 + wn * C::TN + j * 32 + g * 8 + hi * 4);
+      csum[j][g][0] = c4.x;
+      csum[j][g][1] = c4.y;
+      csum[j][g][2] = c4.z;
+      csum[j][g][3] = c4.w;
+    }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < C::MI; ++i) {
+    const float2 nr = row_norm[wm * C::TM + i * 32 + l32];
+#pragma unroll
+    for (int j = 0; j < C::NI; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[i][j][4 * g + e] = nr.y * __builtin_fmaf(-nr.x, csum[j][g][e], acc[i][j][4 * g + e]);
+  }
   // A tile lies inside one of the U, V, Q, K column blocks (D is a multiple of BN).
   const int slice = col0 / D;
   // The position-bias tile goes through the (now idle) LDS: every 32 consecutive
@@ -341,13 +400,34 @@ void out_kernel(OutArgs a) {
     }
   }
   __syncthreads();
+  // Also the next layer's row statistics: each 16 consecutive threads hold one row's
+  // 128-column group and add their {sum, sum of squares} in a fixed butterfly order
+  // (the same order as the first layer's row pass).
+  static_assert(CPR % 16 == 0, "whole 128-column groups per tile row");
 #pragma unroll
   for (int i = 0; i < C::BM * CPR / C::NT; ++i) {
     const int c = threadIdx.x + C::NT * i, r = c / CPR, cc = (c % CPR) * 8;
     const int row = row0 + r;
+    const uint4 v = *reinterpret_cast<const uint4*>(smem + r * OLD + cc);
+    if (a.st != nullptr) {
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      float s1 = 0.0f, s2 = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = bf2f_lo(w[e]), hi = bf2f_hi(w[e]);
+        s1 += lo + hi;
+        s2 = __builtin_fmaf(lo, lo, __builtin_fmaf(hi, hi, s2));
+      }
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) {
+        s1 += __shfl_xor(s1, m);
+        s2 += __shfl_xor(s2, m);
+      }
+      if ((c & 15) == 0 && row < a.T) a.st[(size_t)row * (D / 128) + (col0 + cc) / 128] = make_float2(s1, s2);
+    }
     if (row >= a.T) continue;
     u16* y = row < a.Nu ? (u16*)a.y_lo + (size_t)row * D : (u16*)a.y_hi + (size_t)(row - a.Nu) * D;
-    *reinterpret_cast<uint4*>(y + col0 + cc) = *reinterpret_cast<const uint4*>(smem + r * OLD + cc);
+    *reinterpret_cast<uint4*>(y + col0 + cc) = v;
   }
 }
 

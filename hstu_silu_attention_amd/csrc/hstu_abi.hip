@@ -54,8 +54,8 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 struct Layout {
   int32_t Nu = 0, Nc = 0, T = 0;
   int64_t ntiles = 0;
-  size_t users = 0, bins = 0, tiles = 0, rows = 0, xn = 0, vqk = 0, aout = 0, x = 0, total = 0;
-  size_t staged = 0;  // bytes copied from the host: users table + XCD bins + tile list
+  size_t users = 0, bins = 0, tiles = 0, wptr = 0, rows = 0, xn = 0, cs = 0, st = 0, vqk = 0, aout = 0, x = 0, total = 0;
+  size_t staged = 0;  // bytes copied from the host: users table + XCD bins + tile list + W1 pointers
 };
 
 Layout make_layout(const hstu_dims* d, int32_t B, const int32_t* uo, const int32_t* co) {
@@ -76,9 +76,14 @@ Layout make_layout(const hstu_dims* d, int32_t B, const int32_t* uo, const int32
   L.users = off; off += align_up((size_t)B * sizeof(UserRec));
   L.bins = off; off += align_up((size_t)hstu::kXcds * 8);
   L.tiles = off; off += align_up((size_t)L.ntiles * 16);
+  L.wptr = off; off += align_up((size_t)d->layers * sizeof(void*));
   L.staged = off;
   L.rows = off; off += align_up(T * 8);
-  L.xn = off; off += align_up(Tp * D * es);
+  // float32 models normalise into xn; bfloat16 models normalise inside the projection
+  // and need the column sums of W1 instead
+  L.xn = off; off += d->dtype == HSTU_F32 ? align_up(Tp * D * es) : 0;
+  L.cs = off; off += d->dtype == HSTU_F32 ? 0 : align_up((size_t)d->layers * 4 * D * sizeof(float));
+  L.st = off; off += d->dtype == HSTU_F32 ? 0 : align_up(T * (D / 128) * 2 * sizeof(float));
   L.vqk = off; off += align_up(Tp * 3 * D * es);
   L.aout = off; off += align_up(Tp * 3 * D * es);
   L.x = off; off += d->layers > 1 ? align_up(T * D * es) : 0;
@@ -390,6 +395,8 @@ hstu_status hstu_encode(const hstu_dims* d, int32_t B, const int32_t* uih_offset
     }
   }
   const int attn_grid = hstu::kXcds * longest;
+  const void** wptr = reinterpret_cast<const void**>(staged.data() + lay.wptr);
+  for (int32_t l = 0; l < L; ++l) wptr[l] = w[l].w_uvqk;
 
   // ------------------------------------------------------------ enqueue
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -401,6 +408,8 @@ hstu_status hstu_encode(const hstu_dims* d, int32_t B, const int32_t* uih_offset
   const int2* d_bins = reinterpret_cast<const int2*>(ws + lay.bins);
   int2* d_rows = reinterpret_cast<int2*>(ws + lay.rows);
   char* xn = ws + lay.xn;
+  float* cs = reinterpret_cast<float*>(ws + lay.cs);
+  float2* rstat = reinterpret_cast<float2*>(ws + lay.st);
   const size_t es = d->dtype == HSTU_F32 ? 4 : 2;
   char* vqk = ws + lay.vqk;
   char* aout = ws + lay.aout;
@@ -410,6 +419,15 @@ hstu_status hstu_encode(const hstu_dims* d, int32_t B, const int32_t* uih_offset
   hstu::PlanArgs pa{d_users, B, lay.Nu, lay.T, d_rows};
   if (timed_launch(HSTU_KERNEL_PLAN, s, [&] { return hstu::launch_plan(pa, s); }) != hipSuccess)
     return HSTU_ERR_HIP;
+
+  if (d->dtype != HSTU_F32) {
+    hstu::ColsumArgs ca{reinterpret_cast<const void* const*>(ws + lay.wptr), L, D, cs};
+    if (timed_launch(HSTU_KERNEL_NORM, s, [&] { return hstu::launch_colsum(ca, s); }) != hipSuccess)
+      return HSTU_ERR_HIP;
+    if (timed_launch(HSTU_KERNEL_NORM, s,
+                     [&] { return hstu::launch_rowstats(uih, cand, lay.Nu, lay.T, D, rstat, s); }) != hipSuccess)
+      return HSTU_ERR_HIP;
+  }
 
   const int dh = D / d->heads;
   const size_t layer_cache = kv ? (size_t)kv->slots * kv->capacity * D * es : 0;
@@ -421,10 +439,12 @@ hstu_status hstu_encode(const hstu_dims* d, int32_t B, const int32_t* uih_offset
     void* ck = kv ? (void*)((char*)kv->k + l * layer_cache) : nullptr;
     void* cv = kv ? (void*)((char*)kv->v + l * layer_cache) : nullptr;
 
-    hstu::NormArgs na{x_lo, x_hi, lay.Nu, lay.T, D, xn};
-    if (timed_launch(HSTU_KERNEL_NORM, s, [&] { return hstu::launch_norm(d->dtype, na, s); }) != hipSuccess)
-      return HSTU_ERR_HIP;
-    hstu::UvqkArgs ua{xn, lay.Nu, lay.T, D, w[l].w_uvqk, w[l].pos_bias, d_rows, d_users,
+    if (d->dtype == HSTU_F32) {
+      hstu::NormArgs na{x_lo, x_hi, lay.Nu, lay.T, D, xn};
+      if (timed_launch(HSTU_KERNEL_NORM, s, [&] { return hstu::launch_norm(d->dtype, na, s); }) != hipSuccess)
+        return HSTU_ERR_HIP;
+    }
+    hstu::UvqkArgs ua{xn, x_lo, x_hi, cs + (size_t)l * 4 * D, rstat, lay.Nu, lay.T, D, w[l].w_uvqk, w[l].pos_bias, d_rows, d_users,
                       vqk, aout, ck, cv};
     if (timed_launch(HSTU_KERNEL_UVQK, s, [&] { return hstu::launch_uvqk(d->dtype, ua, s); }) != hipSuccess)
       return HSTU_ERR_HIP;
@@ -451,7 +471,9 @@ hstu_status hstu_encode(const hstu_dims* d, int32_t B, const int32_t* uih_offset
                      [&] { return hstu::launch_attn(d->dtype, dh, aa, attn_grid, s); }) != hipSuccess)
       return HSTU_ERR_HIP;
 
-    hstu::OutArgs oa{aout, w[l].w_out, x_lo, x_hi, y_lo, y_hi, lay.Nu, lay.T, D};
+    // the output GEMM also leaves the next layer's row statistics (bfloat16 path)
+    hstu::OutArgs oa{aout, w[l].w_out, x_lo, x_hi, y_lo, y_hi,
+                     d->dtype == HSTU_F32 || l == L - 1 ? nullptr : rstat, lay.Nu, lay.T, D};
     if (timed_launch(HSTU_KERNEL_OUT, s, [&] { return hstu::launch_out(d->dtype, oa, s); }) != hipSuccess)
       return HSTU_ERR_HIP;
   }

@@ -36,7 +36,12 @@ struct PlanArgs {
 // Workspace buffers of one layer (rows in the packed order: history rows of every
 // user, then candidate rows), each padded to a multiple of kRowPad rows; rows T..
 // are never written and only ever feed discarded GEMM output rows.
-//  xn   [T_pad][D]   normalised layer input (the projection's A operand)
+//  xn   [T_pad][D]   normalised layer input, the float32 projection's A operand (the
+//                    bfloat16 projection normalises inside: no buffer)
+//  cs   [L][4D]      float32 column sums of each layer's W1 (bfloat16 only)
+//  st   [T][D/128]   float2 {sum, sum of squares} of each layer-input row over each
+//                    128-column group, in float32 (bfloat16 only): written by the
+//                    previous layer's output GEMM (the first layer's by a row pass)
 //  vqk  [T_pad][3D]  V | Q | K after SiLU and position bias
 //  aout [T_pad][3D]  U | O | U*O: the output GEMM's A operand. The projection writes
 //                    U and the attention O; the float32 attention also writes the
@@ -54,8 +59,20 @@ struct NormArgs {
 
 constexpr float kNormEps = 1e-6f;
 
+// Column sums cs[l][n] = sum_k W1_l[n][k] (float32) of every layer's projection weight,
+// which is stored [4D][D] (output feature n in row n).
+struct ColsumArgs {
+  const void* const* w;  // [L] device pointers to the layers' W1
+  int32_t L, D;
+  float* cs;             // [L][4D] out
+};
+
 struct UvqkArgs {
-  const void* xn;        // [T_pad][D]
+  const void* xn;        // [T_pad][D] normalised rows (float32 path)
+  const void* x_lo;      // layer input rows [0, Nu) (bfloat16 path, normalised inside)
+  const void* x_hi;      // layer input rows [Nu, T)
+  const float* cs;       // [4D] column sums of this layer's W1 (bfloat16 path)
+  const float2* st;      // [T][D/128] row statistics of the layer input (bfloat16 path)
   int32_t Nu, T, D;
   const void* w;         // [4D][D]
   const void* pos;       // [max_len][3D]
@@ -87,6 +104,7 @@ struct OutArgs {
   const void* x_hi;      // residual rows [Nu, T)
   void* y_lo;            // output rows [0, Nu)
   void* y_hi;            // output rows [Nu, T)
+  float2* st;            // [T][D/128] out: statistics of the output rows (or nullptr)
   int32_t Nu, T, D;
 };
 
@@ -95,6 +113,9 @@ int attn_block_rows(int dtype);
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_norm(int dtype, const NormArgs& a, hipStream_t s);
+hipError_t launch_colsum(const ColsumArgs& a, hipStream_t s);   // bfloat16 weights
+// st[row][g] of the rows [0, Nu) of x_lo and [Nu, T) of x_hi (bfloat16)
+hipError_t launch_rowstats(const void* x_lo, const void* x_hi, int Nu, int T, int D, float2* st, hipStream_t s);
 hipError_t launch_uvqk(int dtype, const UvqkArgs& a, hipStream_t s);
 // grid = kXcds * (longest bin)
 hipError_t launch_attn(int dtype, int dh, const AttnArgs& a, int grid, hipStream_t s);

@@ -100,7 +100,67 @@ __global__ __launch_bounds__(256) void norm_kernel(NormArgs a) {
   }
 }
 
+// One wave per row of W1 (one output feature): the sum of its D bfloat16 values, in a
+// fixed order (each lane's chunks in turn, then the wave's butterfly).
+__global__ __launch_bounds__(256) void colsum_kernel(ColsumArgs a) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int nrow = 4 * a.D;
+  if (row >= a.L * nrow) return;
+  const u16* w = (const u16*)a.w[row / nrow] + (size_t)(row % nrow) * a.D;
+  float s = 0.0f;
+  for (int c = lane; c < a.D / 8; c += 64) {
+    float v[8];
+    load_chunk(w + c * 8, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += v[e];
+  }
+  s = wave_sum(s);
+  if (lane == 0) a.cs[row] = s;
+}
+
+// One wave per row: {sum, sum of squares} of each 128-column group (16 lanes of 8
+// values each, reduced in a fixed butterfly order). The order of every addition is the
+// one the output GEMM uses for the later layers' rows, so a row's statistics come out
+// bit-identical whichever kernel produced them.
+__global__ __launch_bounds__(256) void rowstats_kernel(const void* x_lo, const void* x_hi, int Nu, int T, int D, float2* st) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= T) return;
+  const u16* x = row < Nu ? (const u16*)x_lo + (size_t)row * D : (const u16*)x_hi + (size_t)(row - Nu) * D;
+  for (int c0 = 0; c0 < D / 8; c0 += 64) {          // 64 chunks = 4 groups per pass
+    const int c = c0 + lane;
+    float s1 = 0.0f, s2 = 0.0f;
+    if (c < D / 8) {
+      float v[8];
+      load_chunk(x + c * 8, v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s1 += v[2 * e] + v[2 * e + 1];
+        s2 = __builtin_fmaf(v[2 * e], v[2 * e], __builtin_fmaf(v[2 * e + 1], v[2 * e + 1], s2));
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+      s1 += __shfl_xor(s1, m);
+      s2 += __shfl_xor(s2, m);
+    }
+    if ((lane & 15) == 0 && c < D / 8) st[(size_t)row * (D / 128) + c / 16] = make_float2(s1, s2);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_rowstats(const void* x_lo, const void* x_hi, int Nu, int T, int D, float2* st, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  rowstats_kernel<<<(T + 3) / 4, 256, 0, s>>>(x_lo, x_hi, Nu, T, D, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_colsum(const ColsumArgs& a, hipStream_t s) {
+  const int rows = a.L * 4 * a.D;
+  if (rows <= 0) return hipSuccess;
+  colsum_kernel<<<(rows + 3) / 4, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
 
 hipError_t launch_norm(int dtype, const NormArgs& a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;

@@ -177,7 +177,10 @@ enum hstu_kernel_kind {
   HSTU_KERNEL_UVQK = 1,       /* projection GEMM + SiLU + bias + append  */
   HSTU_KERNEL_ATTENTION = 2,  /* target-aware causal SiLU attention      */
   HSTU_KERNEL_OUT = 3,        /* gated output GEMM + residual            */
-  HSTU_KERNEL_NORM = 4,       /* per-row normalisation of the layer input */
+  HSTU_KERNEL_NORM = 4,       /* normalisation work: float32 models normalise each  */
+                              /* layer's input rows; bfloat16 models run two passes  */
+                              /* per call (W1 column sums, first-layer row sums) and */
+                              /* normalise inside the projection                     */
   HSTU_KERNEL_KINDS = 5
 };
 hstu_status hstu_timing_enable(int32_t enable);

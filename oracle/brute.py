@@ -73,7 +73,7 @@ def encode_brute(uih, uih_offsets, cand, cand_offsets, params, *, heads: int, ma
             for r in range(n + c):
                 mean = sum(xs[r]) / D
                 var = sum((t - mean) * (t - mean) for t in xs[r]) / D
-                xn = [rnd((t - mean) / math.sqrt(var + _EPS)) for t in xs[r]]
+                xn = [(t - mean) / math.sqrt(var + _EPS) for t in xs[r]]   # never stored: no rounding
                 for j in range(4 * D):
                     g = 0.0
                     for k in range(D):

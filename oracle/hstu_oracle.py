@@ -30,9 +30,11 @@ included.
 
 Arithmetic is float64 throughout. ``mode="f64"`` applies no intermediate
 rounding. ``mode="bf16"`` mirrors a bfloat16 pipeline by rounding (to nearest,
-ties to even) at exactly these points: the normalised layer input; U, V, Q, K
-after bias; every attention weight SiLU(q.k); every attention output; the gate
-U*O; and X + Z.
+ties to even) at exactly the values such a pipeline stores: U, V, Q, K after
+bias; every attention weight SiLU(q.k); every attention output; the gate U*O;
+and X + Z. The normalised layer input is not among them: the pipeline applies
+the normalisation to the projection's float32 product and never stores
+normalised rows.
 
 Parity pins for every function here live in tests/test_oracle_pins.py (brute
 force on tiny inputs, closed forms, invariants, the page's jagged example and
@@ -192,10 +194,11 @@ def attention_user(q_u, k_all, v_all, q_c, k_c, v_c, *, m: int, heads: int, inv:
 
 
 def _project(x, w1, pos_table, positions, bf16, counter):
-    """S = SiLU(norm(X) W1) split into U, V, Q, K; position bias on V, Q, K (not U)."""
+    """S = SiLU(norm(X) W1) split into U, V, Q, K; position bias on V, Q, K (not U).
+    The normalised rows are never stored, so they take no rounding in either mode."""
     D = x.shape[1]
     R = round_bf16 if bf16 else (lambda a: a)
-    s = silu(R(normalize_rows(x)) @ w1)
+    s = silu(normalize_rows(x) @ w1)
     if counter is not None:
         counter.gemm_uvqk += x.shape[0] * D * 4 * D
     bias = pos_table[positions]

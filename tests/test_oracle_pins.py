@@ -273,7 +273,7 @@ def test_zero_query_gives_zero_attention(mode):
                                        heads=2, max_len=40, bf16=bf16)
     # attention outputs directly
     xn = oracle.normalize_rows(xu[:7])
-    s = oracle.silu((oracle.round_bf16(xn) if bf16 else xn) @ w1)
+    s = oracle.silu(xn @ w1)   # the normalised rows are never stored, so never rounded
     q = s[:, 2 * D:3 * D] + pos[:7, D:2 * D]
     assert np.all(q == 0)
     kk = s[:, 3 * D:] + pos[:7, 2 * D:]
