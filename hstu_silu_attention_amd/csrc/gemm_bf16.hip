@@ -444,8 +444,9 @@ long tiles_of(int T, int N) {
 }  // namespace
 
 hipError_t launch_uvqk_bf16(const UvqkArgs& a, hipStream_t s) {
+  // A tile must lie inside one of the U, V, Q, K column blocks: D % BN == 0.
   const int N = 4 * a.D;
-  if (tiles_of<BigTile>(a.T, N) >= 256)
+  if (a.D % BigTile::BN == 0 && tiles_of<BigTile>(a.T, N) >= 256)
     uvqk_kernel<BigTile><<<tiles_of<BigTile>(a.T, N), BigTile::NT, 0, s>>>(a);
   else
     uvqk_kernel<SmallTile><<<tiles_of<SmallTile>(a.T, N), SmallTile::NT, 0, s>>>(a);

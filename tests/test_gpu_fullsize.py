@@ -50,6 +50,16 @@ def test_d256_workload_all_users():
     assert eu <= BF16_TOL and ec <= BF16_TOL
 
 
+def test_d384_projection_tiles_inside_column_blocks():
+    """D=384 (three 128-wide heads) over enough rows that the projection would fill the
+    GPU with its widest tiles: D is not a multiple of their width, so those tiles would
+    straddle the U/V/Q/K column blocks; every user is checked."""
+    wl = workloads.make_custom(seed=384, dtype="bf16", layers=1, d_model=384, heads=3, max_len=4400,
+                               uih_lengths=[4000, 3000, 2500, 1500], cand_lengths=[300, 64, 17, 0])
+    gu, gc = gpu_encode(wl)
+    compare_users(wl, gu, gc, [0, 1, 2, 3])
+
+
 def test_streaming_workload_sampled_user():
     """64 users, each with a 3000-event cached prefix (filled by hstu_encode with no
     candidates), then 300 new events + 2048 candidates against the cache. One user is
