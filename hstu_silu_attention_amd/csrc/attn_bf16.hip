@@ -108,12 +108,10 @@ void attn_kernel(AttnArgs a) {
   using C = AttnTile<DH>;
   __shared__ __attribute__((aligned(16))) u16 ks0[C::SLOT], ks1[C::SLOT], vs0[C::SLOT], vs1[C::SLOT];
 
-  const int2 bin = a.bins[blockIdx.x % kXcds];
-  if ((int)(blockIdx.x / kXcds) >= bin.y) return;
-  const int4 t = a.tiles[bin.x + blockIdx.x / kXcds];
-  const UserRec u = a.users[t.x];
-  const int head = t.y >> 1, q0 = t.z, nq = t.w;
-  const bool cand = (t.y & 1) != 0;
+  const AttnItem it = a.items[blockIdx.x];
+  if (it.nq <= 0) return;
+  const int head = it.hk >> 1, q0 = it.q0, nq = it.nq;
+  const bool cand = (it.hk & 1) != 0;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, so are the biases
   const int D = a.D;
@@ -127,18 +125,17 @@ void attn_kernel(AttnArgs a) {
   for (int qb = 0; qb < C::QB; ++qb) {
     const int qloc = wv * 32 * C::QB + qb * 32 + l32;
     qok[qb] = qloc < nq;
-    const int qi = q0 + (qok[qb] ? qloc : 0);
-    row[qb] = cand ? (size_t)a.Nu + u.coff + qi : (size_t)u.uoff + qi;
+    row[qb] = (size_t)it.rbase + (qok[qb] ? qloc : 0);
     const u16* qrow = (const u16*)a.vqk + row[qb] * ld3 + D + head * DH;
 #pragma unroll
     for (int kk = 0; kk < C::KK; ++kk)
       qf[qb][kk] = as_bf16x8(qok[qb] ? *reinterpret_cast<const uint4*>(qrow + kk * 16 + hi * 8) : make_uint4(0, 0, 0, 0));
   }
 
-  const int key_end = cand ? u.m + u.n : u.m + q0 + nq;  // keys [0, key_end)
-  const int shift = cand ? 0 : (-u.m) & 31;               // kappa = key + shift
+  const int key_end = it.key_end;                         // keys [0, key_end)
+  const int shift = cand ? 0 : (-it.m) & 31;              // kappa = key + shift
   const int nblk = (key_end + shift + C::KB - 1) / C::KB;
-  const int wf = u.m + q0 + wv * 32 * C::QB + shift;      // kappa of this wave's first row (history)
+  const int wf = it.m + q0 + wv * 32 * C::QB + shift;     // kappa of this wave's first row (history)
 
   f32x16 oacc[C::QB][C::MB];
 #pragma unroll
@@ -152,8 +149,8 @@ void attn_kernel(AttnArgs a) {
   // rows outside [0, key_end) read as zero
   const int ld = (int)a.ld;
   const int nbytes = key_end * ld * 2;
-  const i32x4 rk_src = buffer_desc((const u16*)a.kbase + (size_t)u.key_row * a.ld + head * DH, nbytes);
-  const i32x4 rv_src = buffer_desc((const u16*)a.vbase + (size_t)u.key_row * a.ld + head * DH, nbytes);
+  const i32x4 rk_src = buffer_desc((const u16*)a.kbase + (size_t)it.key_row * a.ld + head * DH, nbytes);
+  const i32x4 rv_src = buffer_desc((const u16*)a.vbase + (size_t)it.key_row * a.ld + head * DH, nbytes);
 
   // 64-lane LDS loads: load j of a region covers rows RPI*j.. of it; lane i brings the
   // global chunk that belongs at row RPI*j + i/CPR, slot i%CPR

@@ -54,8 +54,8 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 struct Layout {
   int32_t Nu = 0, Nc = 0, T = 0;
   int64_t ntiles = 0;
-  size_t users = 0, bins = 0, tiles = 0, wptr = 0, rows = 0, xn = 0, cs = 0, st = 0, vqk = 0, aout = 0, x = 0, total = 0;
-  size_t staged = 0;  // bytes copied from the host: users table + XCD bins + tile list + W1 pointers
+  size_t users = 0, wptr = 0, items = 0, rows = 0, xn = 0, cs = 0, st = 0, vqk = 0, aout = 0, x = 0, total = 0;
+  size_t staged = 0;  // host-planned part: users table, W1 pointers, attention items (copied up to the grid)
 };
 
 Layout make_layout(const hstu_dims* d, int32_t B, const int32_t* uo, const int32_t* co) {
@@ -74,9 +74,9 @@ Layout make_layout(const hstu_dims* d, int32_t B, const int32_t* uo, const int32
   const size_t Tp = (size_t)cdiv(L.T, hstu::kRowPad) * hstu::kRowPad;
   size_t off = 0;
   L.users = off; off += align_up((size_t)B * sizeof(UserRec));
-  L.bins = off; off += align_up((size_t)hstu::kXcds * 8);
-  L.tiles = off; off += align_up((size_t)L.ntiles * 16);
   L.wptr = off; off += align_up((size_t)d->layers * sizeof(void*));
+  // one item per attention workgroup: kXcds bins of at most ntiles items each
+  L.items = off; off += align_up((size_t)hstu::kXcds * L.ntiles * sizeof(hstu::AttnItem));
   L.staged = off;
   L.rows = off; off += align_up(T * 8);
   // float32 models normalise into xn; bfloat16 models normalise inside the projection
@@ -379,33 +379,40 @@ hstu_status hstu_encode(const hstu_dims* d, int32_t B, const int32_t* uih_offset
     bin_cost[x] += g.cost;
     for (const Item& it : g.items) bin_items[x].push_back(&it);
   }
-  int32_t* bins = reinterpret_cast<int32_t*>(staged.data() + lay.bins);
-  int32_t* tiles = reinterpret_cast<int32_t*>(staged.data() + lay.tiles);
-  int32_t next = 0, longest = 0;
-  for (int x = 0; x < hstu::kXcds; ++x) {
-    bins[2 * x] = next;
-    bins[2 * x + 1] = (int32_t)bin_items[x].size();
-    longest = std::max(longest, (int32_t)bin_items[x].size());
-    for (const Item* it : bin_items[x]) {
-      tiles[4 * next + 0] = it->user;
-      tiles[4 * next + 1] = it->hk;
-      tiles[4 * next + 2] = it->q0;
-      tiles[4 * next + 3] = it->nq;
-      ++next;
-    }
+  size_t longest = 0;
+  for (int x = 0; x < hstu::kXcds; ++x) longest = std::max(longest, bin_items[x].size());
+  const int attn_grid = hstu::kXcds * (int)longest;
+  // workgroup w runs on XCD w % kXcds: it takes position w / kXcds of that XCD's bin
+  // (nq = 0 past the bin's end)
+  hstu::AttnItem* items = reinterpret_cast<hstu::AttnItem*>(staged.data() + lay.items);
+  for (int w = 0; w < attn_grid; ++w) {
+    const std::vector<const Item*>& bin = bin_items[w % hstu::kXcds];
+    const size_t j = (size_t)(w / hstu::kXcds);
+    hstu::AttnItem& a = items[w];
+    a = hstu::AttnItem{0, 0, 0, 0, 0, 0, 0, 0};
+    if (j >= bin.size()) continue;
+    const Item& it = *bin[j];
+    const UserRec& u = users[it.user];
+    const bool is_cand = (it.hk & 1) != 0;
+    a.hk = it.hk;
+    a.q0 = it.q0;
+    a.nq = it.nq;
+    a.m = u.m;
+    a.rbase = (is_cand ? lay.Nu + u.coff : u.uoff) + it.q0;
+    a.key_end = is_cand ? u.m + u.n : u.m + it.q0 + it.nq;
+    a.key_row = u.key_row;
   }
-  const int attn_grid = hstu::kXcds * longest;
+  const size_t staged_bytes = lay.items + (size_t)attn_grid * sizeof(hstu::AttnItem);
   const void** wptr = reinterpret_cast<const void**>(staged.data() + lay.wptr);
   for (int32_t l = 0; l < L; ++l) wptr[l] = w[l].w_uvqk;
 
   // ------------------------------------------------------------ enqueue
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  st = stage_and_copy(staged.data(), lay.staged, ws, s);
+  st = stage_and_copy(staged.data(), staged_bytes, ws, s);
   if (st != HSTU_OK) return st;
   const UserRec* d_users = reinterpret_cast<const UserRec*>(ws + lay.users);
-  const int4* d_tiles = reinterpret_cast<const int4*>(ws + lay.tiles);
-  const int2* d_bins = reinterpret_cast<const int2*>(ws + lay.bins);
+  const hstu::AttnItem* d_items = reinterpret_cast<const hstu::AttnItem*>(ws + lay.items);
   int2* d_rows = reinterpret_cast<int2*>(ws + lay.rows);
   char* xn = ws + lay.xn;
   float* cs = reinterpret_cast<float*>(ws + lay.cs);
@@ -450,9 +457,7 @@ hstu_status hstu_encode(const hstu_dims* d, int32_t B, const int32_t* uih_offset
       return HSTU_ERR_HIP;
 
     hstu::AttnArgs aa{};
-    aa.tiles = d_tiles;
-    aa.bins = d_bins;
-    aa.users = d_users;
+    aa.items = d_items;
     aa.Nu = lay.Nu;
     aa.D = D;
     aa.inv = 1.0f / (float)d->max_len;

@@ -17,15 +17,25 @@ struct UserRec {
   int32_t uoff, n, coff, c, m, key_row, pad0, pad1;
 };
 
-// Attention work item: 16 bytes = {user, (head << 1) | is_candidate_tile, q0, nq}.
-// q0 is the tile's first query within the user's history (or candidate) rows,
-// nq <= the kernel's query-block size.
+// Attention work item (32 bytes), everything a workgroup needs to start: one load.
+//  hk:      (head << 1) | is_candidate_tile
+//  q0, nq:  the tile's first query within the user's history (or candidate) rows and
+//           its query count (<= the kernel's query-block size; 0: no work)
+//  m:       the user's cached history length
+//  rbase:   packed row of the tile's first query
+//  key_end: keys [0, key_end) are visible to the tile
+//  key_row: row of key 0 in the key/value source
 //
-// The work items are grouped into kXcds bins, one per XCD: workgroups are dealt to
-// the XCDs round-robin, so workgroup w runs on XCD w % kXcds and takes item
-// bins[w % kXcds].x + w / kXcds when w / kXcds < bins[w % kXcds].y. All items of one
-// (user, head) share a bin, so that user's keys and values stay in one L2.
+// The items are grouped into kXcds bins, one per XCD, and laid out per workgroup:
+// workgroups are dealt to the XCDs round-robin, so workgroup w runs on XCD w % kXcds
+// and takes item w, which the planner fills from bin w % kXcds (position w / kXcds).
+// All items of one (user, head) share a bin, so that user's keys and values stay in
+// one L2.
 constexpr int kXcds = 8;
+
+struct AttnItem {
+  int32_t hk, q0, nq, m, rbase, key_end, key_row, pad;
+};
 
 struct PlanArgs {
   const UserRec* users;
@@ -85,9 +95,7 @@ struct UvqkArgs {
 };
 
 struct AttnArgs {
-  const int4* tiles;
-  const int2* bins;      // [kXcds] {first item, item count}
-  const UserRec* users;
+  const AttnItem* items; // [grid], item w for workgroup w
   int32_t Nu, D;
   float inv;             // 1 / max_len
   const void* vqk;       // [T_pad][3D]: Q, and the candidates' own K, V

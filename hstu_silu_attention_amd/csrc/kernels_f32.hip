@@ -104,17 +104,14 @@ template <int DH>
 __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   __shared__ float sk[FKB][DH];
   __shared__ float sv[FKB][DH];
-  const int2 bin = a.bins[blockIdx.x % kXcds];
-  if ((int)(blockIdx.x / kXcds) >= bin.y) return;
-  const int4 t = a.tiles[bin.x + blockIdx.x / kXcds];
-  const UserRec u = a.users[t.x];
-  const int head = t.y >> 1, q0 = t.z, nq = t.w;
-  const bool cand = (t.y & 1) != 0;
+  const AttnItem it = a.items[blockIdx.x];
+  if (it.nq <= 0) return;
+  const int head = it.hk >> 1, nq = it.nq;
+  const bool cand = (it.hk & 1) != 0;
   const int tid = threadIdx.x;
   const int D = a.D;
   const bool qok = tid < nq;
-  const int qi = q0 + tid;
-  const size_t row = cand ? (size_t)a.Nu + u.coff + qi : (size_t)u.uoff + qi;
+  const size_t row = (size_t)it.rbase + tid;
   const float* vqk = (const float*)a.vqk + row * 3 * D + head * DH;  // V | Q | K of this row
   float q[DH], acc[DH];
 #pragma unroll
@@ -122,10 +119,10 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
     q[e] = qok ? vqk[D + e] : 0.0f;
     acc[e] = 0.0f;
   }
-  const int key_end = cand ? u.m + u.n : u.m + q0 + nq;
-  const int qpos = u.m + qi;
-  const float* kp = (const float*)a.kbase + (size_t)u.key_row * a.ld + head * DH;
-  const float* vp = (const float*)a.vbase + (size_t)u.key_row * a.ld + head * DH;
+  const int key_end = it.key_end;
+  const int qpos = it.m + it.q0 + tid;
+  const float* kp = (const float*)a.kbase + (size_t)it.key_row * a.ld + head * DH;
+  const float* vp = (const float*)a.vbase + (size_t)it.key_row * a.ld + head * DH;
   for (int k0 = 0; k0 < key_end; k0 += FKB) {
     __syncthreads();
     for (int id = tid; id < FKB * DH; id += 64) {
