@@ -283,13 +283,20 @@ void uvqk_kernel(UvqkArgs a) {
   static_assert(C::BM * OLD <= 2 * C::STAGE, "a staged tile must fit the LDS stages");
   constexpr int CPR = C::BN / 8;                     // 16-byte chunks per tile row
   uint2 bias[C::MI][C::NI][4];
+  // Thread t moves the 16-byte chunk (t % CPR) of tile rows t / CPR + RSTEP_O * i.
+  constexpr int RSTEP_O = C::NT / CPR;
+  static_assert(C::NT % CPR == 0, "a thread keeps its chunk column");
+  const int r_first = threadIdx.x / CPR, cc = (threadIdx.x % CPR) * 8;
   if (slice > 0) {
-    const u16* pos = (const u16*)a.pos + (slice - 1) * D + (col0 - slice * D);
+    // a position table has fewer than 2^31 elements (checked on the host), so a
+    // position's element offset is a 24 x 24-bit product
+    const u16* pos = (const u16*)a.pos + (slice - 1) * D + (col0 - slice * D) + cc;
 #pragma unroll
     for (int i = 0; i < C::BM * CPR / C::NT; ++i) {
-      const int c = threadIdx.x + C::NT * i, r = c / CPR, cc = (c % CPR) * 8;
+      const int r = r_first + RSTEP_O * i;
       const int2 q = a.row_info[min(row0 + r, a.T - 1)];
-      *reinterpret_cast<uint4*>(smem + r * OLD + cc) = *reinterpret_cast<const uint4*>(pos + (size_t)q.y * 3 * D + cc);
+      *reinterpret_cast<uint4*>(smem + r * OLD + cc) =
+          *reinterpret_cast<const uint4*>(pos + __umul24((unsigned)q.y, 3u * (unsigned)D));
     }
     __syncthreads();
 #pragma unroll
@@ -337,13 +344,14 @@ void uvqk_kernel(UvqkArgs a) {
   u16* cache = a.cache_k == nullptr ? nullptr
                : slice == 1 ? (u16*)a.cache_v + ccol
                : slice == 3 ? (u16*)a.cache_k + ccol : nullptr;
+  u16* const out0 = out + (size_t)(row0 + r_first) * 3 * D + cc;
 #pragma unroll
   for (int i = 0; i < C::BM * CPR / C::NT; ++i) {
-    const int c = threadIdx.x + C::NT * i, r = c / CPR, cc = (c % CPR) * 8;
+    const int r = r_first + RSTEP_O * i;
     const int row = row0 + r;
     if (row >= a.T) continue;
     const uint4 v = *reinterpret_cast<const uint4*>(smem + r * OLD + cc);
-    *reinterpret_cast<uint4*>(out + (size_t)row * 3 * D + cc) = v;
+    *reinterpret_cast<uint4*>(out0 + (size_t)i * RSTEP_O * 3 * D) = v;
     if (cache != nullptr && row < a.Nu) {
       const int2 q = a.row_info[row];
       *reinterpret_cast<uint4*>(cache + ((size_t)a.users[q.x].key_row + q.y) * D + cc) = v;

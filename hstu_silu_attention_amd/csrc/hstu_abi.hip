@@ -26,6 +26,8 @@ hstu_status check_dims(const hstu_dims* d) {
   if (!d) return HSTU_ERR_NULL;
   if (d->layers < 1 || d->d_model <= 0 || d->heads <= 0 || d->max_len < 1) return HSTU_ERR_SHAPE;
   if (d->d_model % d->heads) return HSTU_ERR_SHAPE;
+  // a position table holds fewer than 2^31 elements (the kernels index it in 32 bits)
+  if ((int64_t)d->max_len * 3 * d->d_model >= ((int64_t)1 << 31)) return HSTU_ERR_SHAPE;
   const int dh = d->d_model / d->heads;
   if (d->dtype == HSTU_F32) {
     if (d->d_model % 64 || (dh != 32 && dh != 64 && dh != 128)) return HSTU_ERR_SHAPE;

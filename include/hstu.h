@@ -85,7 +85,8 @@ typedef int32_t hstu_status;
  *           bfloat16: D % 128 == 0 and dh in {64, 128}
  *  max_len  rows of each position-bias table; every user needs m + n + 1 <= max_len
  *           (history positions 0..m+n-1 plus the candidate slot m+n). The attention
- *           scale is 1/max_len.
+ *           scale is 1/max_len. A table has fewer than 2^31 elements:
+ *           max_len * 3 * D < 2^31.
  *  dtype    enum hstu_dtype. */
 typedef struct hstu_dims {
   int32_t layers;

@@ -56,6 +56,8 @@ def dims(L=2, D=256, H=4, max_len=64, dtype=hsa.HSTU_BF16):
     (dims(dtype=2), ERR_SHAPE),
     (dims(L=0), ERR_SHAPE),
     (dims(max_len=0), ERR_SHAPE),
+    (dims(D=512, max_len=1398101), OK),          # 3 * D * max_len = 2^31 - 512
+    (dims(D=512, max_len=1398102), ERR_SHAPE),   # a position table of 2^31 elements
     (dims(D=64, H=2, dtype=hsa.HSTU_F32), OK),   # fp32, dh = 32
     (dims(D=96, H=3, dtype=hsa.HSTU_F32), ERR_SHAPE),
     (dims(D=512, H=2, dtype=hsa.HSTU_F32), ERR_SHAPE),   # dh = 256
