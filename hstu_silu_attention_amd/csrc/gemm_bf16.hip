@@ -15,13 +15,13 @@ namespace {
 // blocks (the MFMA's A operand is a W row block), so a lane owns one output row and
 // runs of 4 consecutive output columns.
 //
-// K advances 64 at a time through two LDS stages (rows padded to 72 elements, which
-// makes the 16-byte fragment reads of 8 consecutive rows hit distinct banks). The
-// next step's global loads are issued into registers before the current step's
-// MFMAs and written to the other stage after them, so each step needs one barrier.
-// The projection reads the layer input rows as stored and gathers their statistics
-// while staging; the output GEMM forms the gate columns of [U | O | U*O] from U and O
-// while staging.
+// The output GEMM (gemm_tile) advances K 64 at a time through two LDS stages (rows
+// padded to 72 elements, which makes the 16-byte fragment reads of 8 consecutive rows
+// hit distinct banks). The next step's global loads are issued into registers before
+// the current step's MFMAs and written to the other stage after them, so each step
+// needs one barrier; staging through registers lets it form the gate columns of
+// [U | O | U*O] from U and O on the way. The projection (gemm_tile_dma) loads its
+// operands, the layer input rows as stored and W1, straight into LDS.
 template <int BM_, int BN_, int WM_, int WN_>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
@@ -38,51 +38,11 @@ struct Tile {
 
 // Thread t moves the chunks of rows t/8 + RSTEP*i (i < AC or BC), k offset (t%8)*8.
 
-// A-operand loaders. A GEMM's K range is walked in steps of BK; a loader with PARTS
-// parts visits step t as part t % PARTS of chunk t / PARTS and says which K offset of
-// W that step multiplies (kw).
-
-// The normalised layer input, read as stored (one part): step t is columns t*BK...
-// The buffer is padded to whole tiles, so no row needs a bounds check.
-template <int AC, int RSTEP>
-struct PlainRows {
-  static constexpr int PARTS = 1;
-  const u16* p;
-  size_t step;
-  uint4 v[AC];
-  __device__ __forceinline__ void init(const u16* base, int ld, int row0, int tid) {
-    p = base + (size_t)(row0 + (tid >> 3)) * ld + (tid & 7) * 8;
-    step = (size_t)RSTEP * ld;
-  }
-  __device__ __forceinline__ void fetch(int, int chunk) {
-#pragma unroll
-    for (int i = 0; i < AC; ++i) v[i] = *reinterpret_cast<const uint4*>(p + i * step + chunk * 64);
-  }
-  __device__ __forceinline__ uint4 get(int, int i, float) const { return v[i]; }
-  __device__ __forceinline__ int kw(int, int chunk) const { return chunk * 64; }
-};
-
-// The layer input rows X as stored (one part), rows [0, Nu) from x_lo and [Nu, T) from
-// x_hi (rows past T repeat row T-1; their results are discarded).
-template <int AC, int RSTEP>
-struct SplitRows {
-  static constexpr int PARTS = 1;
-  const u16* p[AC];
-  uint4 v[AC];
-  __device__ __forceinline__ void init(const void* x_lo, const void* x_hi, int Nu, int T, int D, int row0, int tid) {
-#pragma unroll
-    for (int i = 0; i < AC; ++i) {
-      const int row = min(row0 + (tid >> 3) + RSTEP * i, T - 1);
-      p[i] = (row < Nu ? (const u16*)x_lo + (size_t)row * D : (const u16*)x_hi + (size_t)(row - Nu) * D) + (tid & 7) * 8;
-    }
-  }
-  __device__ __forceinline__ void fetch(int, int chunk) {
-#pragma unroll
-    for (int i = 0; i < AC; ++i) v[i] = *reinterpret_cast<const uint4*>(p[i] + chunk * 64);
-  }
-  __device__ __forceinline__ uint4 get(int, int i, float) const { return v[i]; }
-  __device__ __forceinline__ int kw(int, int chunk) const { return chunk * 64; }
-};
+// A-operand loader of gemm_tile. A GEMM's K range is walked in steps of BK; a loader
+// with PARTS parts visits step t as part t % PARTS of chunk t / PARTS and says which K
+// offset of W that step multiplies (kw). GatedRows reads the output GEMM's operand rows
+// [U | O | U*O]: part 0 is a chunk of U, part 1 the same chunk of O, and part 2 its gate
+// U*O, formed from the two in registers and rounded to bfloat16.
 template <int AC, int RSTEP>
 struct GatedRows {
   static constexpr int PARTS = 3;
@@ -221,18 +181,123 @@ __device__ __forceinline__ void gemm_tile(AL& al, const u16* __restrict__ w, int
   }
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One 64-lane load of 16 bytes per lane from global memory straight into LDS at
+// lds_addr + 16 * lane (no register round trip). Written out so the compiler does not
+// track it (it would make every later LDS read wait for it); the caller waits with
+// vmcnt and a barrier before any wave reads the rows. M0 needs one wait state.
+__device__ __forceinline__ void lds_load16(uint32_t lds_addr, const void* src) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off"
+      :
+      : "s"(lds_addr), "v"(src)
+      : "memory", "m0");
+}
+
+// The projection's main loop with its operands loaded straight into LDS. A stage holds
+// BM A rows then BN W rows of BK = 64 elements, unpadded (128 bytes a row); the 16-byte
+// chunk c of row r sits at slot c ^ ((r >> 1) & 7), which keeps the fragment reads of
+// 16 consecutive rows on distinct banks. Load j of a stage (64 lanes, 8 rows) fills its
+// rows 8j..8j+7; wave w issues loads w, w + WAVES, ... Each step waits for its own
+// stage (issued one whole step earlier), synchronises, requests the next stage into the
+// other buffer, then runs its MFMAs.
+template <typename C>
+__device__ __forceinline__ void gemm_tile_dma(const UvqkArgs& a, int row0, int col0, f32x16 (&acc)[C::MI][C::NI],
+                                              u16* smem) {
+  static_assert(C::BK == 64 && (C::BM + C::BN) % (8 * C::NT / 64) == 0, "whole loads per wave");
+  constexpr int WAVES = C::NT / 64;
+  constexpr int LOADS = (C::BM + C::BN) / 8 / WAVES;     // per wave per stage
+  constexpr int SROWS = C::BM + C::BN;                   // rows of a stage
+  const int D = a.D, K = D;
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wv / C::WN, wn = wv % C::WN, l32 = lane & 31, hi = lane >> 5;
+  // this lane's source row of each of its loads, at k = 0
+  const u16* src[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int r = 8 * (wv + WAVES * i) + lane / 8;          // row of the stage
+    const int c = (lane & 7) ^ ((r >> 1) & 7);              // chunk that belongs in this slot
+    if (r < C::BM) {
+      const int row = min(row0 + r, a.T - 1);
+      src[i] = (row < a.Nu ? (const u16*)a.x_lo + (size_t)row * D : (const u16*)a.x_hi + (size_t)(row - a.Nu) * D) + c * 8;
+    } else {
+      src[i] = (const u16*)a.w + (size_t)(col0 + r - C::BM) * K + c * 8;
+    }
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)smem;
+  auto issue = [&](int stage, int k0) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i)
+      lds_load16(lds0 + stage * SROWS * 128 + (wv + WAVES * i) * 1024, src[i] + k0);
+  };
+  auto wait_loads = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+#pragma unroll
+  for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+    for (int j = 0; j < C::NI; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  const int sw = (l32 >> 1) & 7;                             // this lane's rows' chunk swizzle
+  const int nstep = K / C::BK;
+  issue(0, 0);
+  for (int t = 0; t < nstep; ++t) {
+    wait_loads();
+    __syncthreads();                                          // stage t & 1 is complete; stage (t + 1) & 1 is free
+    if (t + 1 < nstep) issue((t + 1) & 1, (t + 1) * C::BK);
+    const u16* sa = smem + (t & 1) * SROWS * 64 + (wm * C::TM + l32) * 64;
+    const u16* sb = smem + (t & 1) * SROWS * 64 + (C::BM + wn * C::TN + l32) * 64;
+    bf16x8 af[2][C::MI], bw[2][C::NI];
+    auto rd = [&](const u16* p, int kk) { return as_bf16x8(*reinterpret_cast<const uint4*>(p + (((2 * kk + hi) ^ sw) * 8))); };
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i) af[0][i] = rd(sa + i * 32 * 64, 0);
+#pragma unroll
+    for (int j = 0; j < C::NI; ++j) bw[0][j] = rd(sb + j * 32 * 64, 0);
+#pragma unroll
+    for (int kk = 0; kk < C::BK / 16; ++kk) {
+      const int cur = kk & 1, nxt = cur ^ 1;
+      if (kk + 1 < C::BK / 16) {
+#pragma unroll
+        for (int i = 0; i < C::MI; ++i) af[nxt][i] = rd(sa + i * 32 * 64, kk + 1);
+#pragma unroll
+        for (int j = 0; j < C::NI; ++j) bw[nxt][j] = rd(sb + j * 32 * 64, kk + 1);
+      }
+#pragma unroll
+      for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NI; ++j) acc[i][j] = mfma32(bw[cur][j], af[cur][i], acc[i][j]);
+    }
+    {
+      constexpr int kRead = C::MI + C::NI, kMfma = C::MI * C::NI;
+      constexpr unsigned MFMA = 0x008, DS_READ = 0x100;
+      __builtin_amdgcn_sched_group_barrier(DS_READ, kRead, 0);
+#pragma unroll
+      for (int kk = 0; kk + 1 < C::BK / 16; ++kk)
+#pragma unroll
+        for (int i = 0; i < (kMfma > kRead ? kMfma : kRead); ++i) {
+          if (i < kRead) __builtin_amdgcn_sched_group_barrier(DS_READ, 1, 0);
+          if (i < kMfma) __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+        }
+      __builtin_amdgcn_sched_group_barrier(MFMA, kMfma, 0);
+    }
+  }
+  __syncthreads();                                            // the stages are free for the epilogue
+}
+
 template <typename C>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WAVES_PER_EU, C::WAVES_PER_EU)))
 void uvqk_kernel(UvqkArgs a) {
-  __shared__ __attribute__((aligned(16))) u16 smem[2 * C::STAGE];
+  constexpr int SMEM = 2 * (C::BM + C::BN) * 64 > C::BM * (C::BN + 8) ? 2 * (C::BM + C::BN) * 64 : C::BM * (C::BN + 8);
+  __shared__ __attribute__((aligned(1024))) u16 smem[SMEM];
   const int D = a.D, N = 4 * D, ncol = N / C::BN;
   const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
   const int row0 = (tile / ncol) * C::BM, col0 = (tile % ncol) * C::BN;
   __shared__ float2 row_norm[C::BM];                 // {mean, 1/sqrt(var + eps)} per tile row
-  SplitRows<C::AC, C::RSTEP> al;
-  al.init(a.x_lo, a.x_hi, a.Nu, a.T, D, row0, threadIdx.x);
   f32x16 acc[C::MI][C::NI];
-  gemm_tile<C>(al, (const u16*)a.w, D, col0, acc, smem);
+  gemm_tile_dma<C>(a, row0, col0, acc, smem);
 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int wm = wv / C::WN, wn = wv % C::WN, l32 = lane & 31, hi = lane >> 5;
@@ -280,7 +345,7 @@ void uvqk_kernel(UvqkArgs a) {
   // threads read one row's 256 bias values as whole lines (the row's position comes
   // from the row table), then each lane picks up the values of its accumulators.
   constexpr int OLD = C::BN + 8;                     // LDS row stride of the staged tiles
-  static_assert(C::BM * OLD <= 2 * C::STAGE, "a staged tile must fit the LDS stages");
+  static_assert(C::BM * OLD <= SMEM, "a staged tile must fit the LDS stages");
   constexpr int CPR = C::BN / 8;                     // 16-byte chunks per tile row
   uint2 bias[C::MI][C::NI][4];
   // Thread t moves the 16-byte chunk (t % CPR) of tile rows t / CPR + RSTEP_O * i.
