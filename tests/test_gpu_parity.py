@@ -51,6 +51,16 @@ def test_bf16_ragged(D, H):
         f"cand={normwise_per_user(gc, fc, wl.cand_lengths):.3e}")
 
 
+@pytest.mark.parametrize("dtype,tol", [("bf16", BF16_TOL), ("f32", F32_TOL)])
+def test_history_fills_the_position_table(dtype, tol):
+    """m + n + 1 == max_len: the candidates of the long user take the table's last row, its
+    history rows every other one; a second user has no history (candidates at position 0)."""
+    wl = workloads.make_custom(seed=811, dtype=dtype, layers=2, d_model=256 if dtype == "bf16" else 128,
+                               heads=2, max_len=301, uih_lengths=[300, 0], cand_lengths=[4, 2])
+    gu, gc = gpu_encode(wl)
+    check(wl, gu, gc, "bf16" if dtype == "bf16" else "f64", tol, label=f"{dtype} full position table")
+
+
 def test_bf16_single_layer_many_tiles():
     """One layer, long rows: attention work items of up to 16 key blocks per query tile."""
     wl = workloads.make_custom(seed=301, dtype="bf16", layers=1, d_model=256, heads=2, max_len=1100,
