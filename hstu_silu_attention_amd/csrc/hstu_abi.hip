@@ -347,8 +347,7 @@ hstu_status hstu_encode(const hstu_dims* d, int32_t B, const int32_t* uih_offset
   }
   // Attention work items, grouped per (user, head). Each group goes whole to one of
   // the kXcds bins (one bin per XCD), so a user's keys and values are read into one
-  // L2 only; groups are placed largest first on the least loaded bin, and inside a
-  // bin the groups keep that order with their items most keys first. The order never
+  // L2 only; groups are placed largest first on the least loaded bin. The order never
   // changes any result: each item writes its own rows, with a fixed key order inside.
   struct Item { int32_t user, hk, q0, nq; int64_t cost; };
   struct Group { std::vector<Item> items; int64_t cost = 0; };
@@ -381,6 +380,11 @@ hstu_status hstu_encode(const hstu_dims* d, int32_t B, const int32_t* uih_offset
     bin_cost[x] += g.cost;
     for (const Item& it : g.items) bin_items[x].push_back(&it);
   }
+  // Inside a bin, items run longest first (workgroups take them in order as CUs free
+  // up), so the bin ends on short items instead of one user's long tail.
+  for (int x = 0; x < hstu::kXcds; ++x)
+    std::stable_sort(bin_items[x].begin(), bin_items[x].end(),
+                     [](const Item* p, const Item* q) { return p->cost > q->cost; });
   size_t longest = 0;
   for (int x = 0; x < hstu::kXcds; ++x) longest = std::max(longest, bin_items[x].size());
   const int attn_grid = hstu::kXcds * (int)longest;
