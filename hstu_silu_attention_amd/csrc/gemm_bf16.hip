@@ -295,7 +295,8 @@ void uvqk_kernel(UvqkArgs a) {
   const int D = a.D, N = 4 * D, ncol = N / C::BN;
   const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
   const int row0 = (tile / ncol) * C::BM, col0 = (tile % ncol) * C::BN;
-  __shared__ float2 row_norm[C::BM];                 // {mean, 1/sqrt(var + eps)} per tile row
+  __shared__ float row_mean[C::BM];
+  __shared__ float2 row_scale[C::BM];                // {-log2(e) / sigma, sigma}, sigma = sqrt(var + eps)
   f32x16 acc[C::MI][C::NI];
   gemm_tile_dma<C>(a, row0, col0, acc, smem);
 
@@ -312,7 +313,9 @@ void uvqk_kernel(UvqkArgs a) {
     }
     const float mean = s1 / (float)D;
     const float var = fmaxf(s2 / (float)D - mean * mean, 0.0f);
-    row_norm[r] = make_float2(mean, 1.0f / sqrtf(var + kNormEps));
+    const float sigma = sqrtf(var + kNormEps);
+    row_mean[r] = mean;
+    row_scale[r] = make_float2(-1.4426950408889634f / sigma, sigma);
   }
   // Column sums of W1 for this lane's columns: the normalisation is applied to the
   // product, Xn W1 = rstd * (X W1 - mean * colsum(W1)) row by row, exactly.
@@ -330,14 +333,14 @@ void uvqk_kernel(UvqkArgs a) {
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < C::MI; ++i) {
-    const float2 nr = row_norm[wm * C::TM + i * 32 + l32];
+    const float mean = row_mean[wm * C::TM + i * 32 + l32];
 #pragma unroll
     for (int j = 0; j < C::NI; ++j)
 #pragma unroll
       for (int g = 0; g < 4; ++g)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          acc[i][j][4 * g + e] = nr.y * __builtin_fmaf(-nr.x, csum[j][g][e], acc[i][j][4 * g + e]);
+          acc[i][j][4 * g + e] = __builtin_fmaf(-mean, csum[j][g][e], acc[i][j][4 * g + e]);
   }
   // A tile lies inside one of the U, V, Q, K column blocks (D is a multiple of BN).
   const int slice = col0 / D;
@@ -385,17 +388,23 @@ void uvqk_kernel(UvqkArgs a) {
   // The finished tile goes through the LDS too: each lane writes its rounded values
   // there, then every 32 consecutive threads store 512 contiguous bytes of one row, so
   // the global writes are whole cache lines.
+  // With a = X W1 - mean * colsum(W1) and y = a / sigma: SiLU(y) = y / (1 + 2^(-y log2 e))
+  // = a / (sigma + sigma * 2^(a * (-log2(e) / sigma))).
+  auto silu_n = [](float a, float2 sc) {
+    return a * __builtin_amdgcn_rcpf(__builtin_fmaf(__builtin_amdgcn_exp2f(a * sc.x), sc.y, sc.y));
+  };
 #pragma unroll
   for (int i = 0; i < C::MI; ++i) {
     const int r = wm * C::TM + i * 32 + l32;
+    const float2 sc = row_scale[r];
 #pragma unroll
     for (int j = 0; j < C::NI; ++j) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const float v0 = silu(acc[i][j][4 * g + 0]) + bf2f_lo(bias[i][j][g].x);
-        const float v1 = silu(acc[i][j][4 * g + 1]) + bf2f_hi(bias[i][j][g].x);
-        const float v2 = silu(acc[i][j][4 * g + 2]) + bf2f_lo(bias[i][j][g].y);
-        const float v3 = silu(acc[i][j][4 * g + 3]) + bf2f_hi(bias[i][j][g].y);
+        const float v0 = silu_n(acc[i][j][4 * g + 0], sc) + bf2f_lo(bias[i][j][g].x);
+        const float v1 = silu_n(acc[i][j][4 * g + 1], sc) + bf2f_hi(bias[i][j][g].x);
+        const float v2 = silu_n(acc[i][j][4 * g + 2], sc) + bf2f_lo(bias[i][j][g].y);
+        const float v3 = silu_n(acc[i][j][4 * g + 3], sc) + bf2f_hi(bias[i][j][g].y);
         *reinterpret_cast<uint2*>(smem + r * OLD + wn * C::TN + j * 32 + g * 8 + hi * 4) =
             make_uint2(pack2(v0, v1), pack2(v2, v3));
       }
