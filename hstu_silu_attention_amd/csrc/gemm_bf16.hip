@@ -318,7 +318,8 @@ void uvqk_kernel(UvqkArgs a) {
     row_scale[r] = make_float2(-1.4426950408889634f / sigma, sigma);
   }
   // Column sums of W1 for this lane's columns: the normalisation is applied to the
-  // product, Xn W1 = rstd * (X W1 - mean * colsum(W1)) row by row, exactly.
+  // product, Xn W1 = (X W1 - mean * colsum(W1)) / sigma row by row, exactly; the mean
+  // term is taken here, the 1 / sigma inside the SiLU below.
   float csum[C::NI][4][4];
 #pragma unroll
   for (int j = 0; j < C::NI; ++j)
