@@ -3,7 +3,8 @@
 Re-derives every output element of the layer stack with plain Python floats and
 explicit index loops, straight from the definition (the attention core
 Mask(SiLU(Q K^T)) V with absolute position bias on Q, K, V, from the DLRMv3
-benchmark review's "Model selection" section; the target-aware candidate mask;
+benchmark review's "Model selection" section, and the original form it replaced,
+Mask(SiLU(Q K^T) + bias) V with a relative position bias; the target-aware candidate mask;
 the per-row input normalisation, the D -> 4D projection and the 3D -> D output
 GEMM). It shares nothing with
 ``hstu_oracle`` (no NumPy arithmetic, its own bfloat16 rounding and SiLU), so the
@@ -50,9 +51,10 @@ def _mat(rows: int, cols: int) -> List[List[float]]:
 
 def encode_brute(uih, uih_offsets, cand, cand_offsets, params, *, heads: int, max_len: int,
                  bf16: bool, cached_k=None, cached_v=None, cached_len: Optional[Sequence[int]] = None):
-    """uih/cand: lists of D-lists; params: list of (w1 [D][4D], w2 [3D][D], pos [max_len][3D])
-    as nested lists; cached_k/cached_v: per layer, per user, list of D-lists (the user's
-    earlier history keys/values), cached_len per user. Returns (uih_out, cand_out)."""
+    """uih/cand: lists of D-lists; params: list of (w1 [D][4D], w2 [3D][D], pos [max_len][3D]
+    or None[, rel [heads][max_len] or None]) as nested lists; cached_k/cached_v: per layer,
+    per user, list of D-lists (the user's earlier history keys/values), cached_len per
+    user. Returns (uih_out, cand_out)."""
     rnd = bf16_round if bf16 else (lambda v: v)
     B = len(uih_offsets) - 1
     D = len(params[0][0])
@@ -65,7 +67,9 @@ def encode_brute(uih, uih_offsets, cand, cand_offsets, params, *, heads: int, ma
         xs_c = [list(r) for r in cand[cand_offsets[b]:cand_offsets[b + 1]]]
         m = 0 if cached_len is None else cached_len[b]
         n, c = len(xs_u), len(xs_c)
-        for l, (w1, w2, pos) in enumerate(params):
+        for l, lp in enumerate(params):
+            w1, w2, pos = lp[0], lp[1], lp[2]
+            rel = lp[3] if len(lp) > 3 else None
             # rows in one list: history rows first (positions m..m+n-1), then candidates (m+n)
             xs = xs_u + xs_c
             posn = [m + i for i in range(n)] + [m + n] * c
@@ -83,11 +87,11 @@ def encode_brute(uih, uih_offsets, cand, cand_offsets, params, *, heads: int, ma
                     if blk == 0:
                         U[r][col] = rnd(s)
                     elif blk == 1:
-                        V[r][col] = rnd(s + pos[posn[r]][col])
+                        V[r][col] = rnd(s + (pos[posn[r]][col] if pos is not None else 0.0))
                     elif blk == 2:
-                        Q[r][col] = rnd(s + pos[posn[r]][D + col])
+                        Q[r][col] = rnd(s + (pos[posn[r]][D + col] if pos is not None else 0.0))
                     else:
-                        K[r][col] = rnd(s + pos[posn[r]][2 * D + col])
+                        K[r][col] = rnd(s + (pos[posn[r]][2 * D + col] if pos is not None else 0.0))
             keys_k = ([list(x) for x in cached_k[l][b]] if m else []) + K[:n]
             keys_v = ([list(x) for x in cached_v[l][b]] if m else []) + V[:n]
             O = _mat(n + c, D)
@@ -100,14 +104,20 @@ def encode_brute(uih, uih_offsets, cand, cand_offsets, params, *, heads: int, ma
                         sc = 0.0
                         for t in range(dh):
                             sc += Q[r][h * dh + t] * keys_k[j][h * dh + t]
-                        a = rnd(silu_scalar(sc))
+                        w = silu_scalar(sc)
+                        if rel is not None:          # key j sits at position j
+                            w += rel[h][posn[r] - j]
+                        a = rnd(w)
                         for t in range(dh):
                             acc[t] += a * keys_v[j][h * dh + t]
                     if r >= n:                         # a candidate also sees itself
                         sc = 0.0
                         for t in range(dh):
                             sc += Q[r][h * dh + t] * K[r][h * dh + t]
-                        a = rnd(silu_scalar(sc))
+                        w = silu_scalar(sc)
+                        if rel is not None:          # relative position 0
+                            w += rel[h][0]
+                        a = rnd(w)
                         for t in range(dh):
                             acc[t] += a * V[r][h * dh + t]
                     for t in range(dh):

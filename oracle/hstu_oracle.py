@@ -17,6 +17,12 @@ depends on the candidates. Jagged batches are concatenated values plus per-user
 lengths (the KeyedJaggedTensor example of the TorchRec DLRM tutorial page,
 section 2.1).
 
+The same page's "Time/position encoding" paragraph (section "Model selection")
+describes the form it replaced: the original HSTU attention Mask(SiLU(Q K^T) + bias) V
+with a relative position bias. Layers may carry that bias too (``rel``, one value per
+head and relative position pos_i - pos_j, added to each attention weight after the
+SiLU, as the page writes it), and may omit the absolute table (``pos`` None).
+
 Readings adopted where the pages are silent (each listed in the design notes):
 the 3*D*D GEMM consumes [U | O | U*O]; the residual is X + Z; each layer
 normalises its input rows (zero mean, unit variance over D, eps 1e-6, no learned
@@ -31,7 +37,8 @@ included.
 Arithmetic is float64 throughout. ``mode="f64"`` applies no intermediate
 rounding. ``mode="bf16"`` mirrors a bfloat16 pipeline by rounding (to nearest,
 ties to even) at exactly the values such a pipeline stores: U, V, Q, K after
-bias; every attention weight SiLU(q.k); every attention output; the gate U*O;
+bias; every attention weight (SiLU(q.k), plus the relative bias when present); every
+attention output; the gate U*O;
 and X + Z. The normalised layer input is not among them: the pipeline applies
 the normalisation to the projection's float32 product and never stores
 normalised rows.
@@ -146,13 +153,15 @@ def user_positions(m: int, n: int, c: int) -> Tuple[np.ndarray, np.ndarray]:
 def attention_user(q_u, k_all, v_all, q_c, k_c, v_c, *, m: int, heads: int, inv: float,
                    bf16: bool, counter: Optional[MacCounter] = None,
                    uih_rows: Optional[Sequence[int]] = None,
-                   cand_rows: Optional[Sequence[int]] = None, block: int = 256):
+                   cand_rows: Optional[Sequence[int]] = None, block: int = 256, rel=None):
     """Target-aware causal SiLU attention for one user.
 
     q_u [n, D]: new history queries (row i at position m+i); k_all, v_all [m+n, D]:
     every history key/value, row j at position j; q_c, k_c, v_c [c, D]: candidates.
-    History row i: O_i = inv * sum_{j <= m+i} SiLU(q_i.k_j) v_j.
-    Candidate r:   O_r = inv * (sum_{all j} SiLU(q_r.k_j) v_j + SiLU(q_r.k_r) v_r).
+    History row i: O_i = inv * sum_{j <= m+i} a(i, j) v_j.
+    Candidate r:   O_r = inv * (sum_{all j} a(r, j) v_j + a(r, r) v_r).
+    The weight is a(i, j) = SiLU(q_i.k_j), plus rel[h, pos_i - pos_j] when a relative
+    bias table rel [heads, >= m+n+1] is given (candidates sit at position m+n).
     Per head h the columns [h*dh, (h+1)*dh) are used. ``uih_rows`` / ``cand_rows``
     restrict the outputs to the listed rows (the results then have that many rows).
     Returns (O_u, O_c).
@@ -175,7 +184,10 @@ def attention_user(q_u, k_all, v_all, q_c, k_c, v_c, *, m: int, heads: int, inv:
         for s in range(0, rows.shape[0], block):
             rb = rows[s:s + block]
             allowed = key_pos[None, :] <= (m + rb)[:, None]
-            a = np.where(allowed, silu(q_u[rb][:, cols] @ kh.T), 0.0)
+            w = silu(q_u[rb][:, cols] @ kh.T)
+            if rel is not None:
+                w = w + rel[h][np.maximum((m + rb)[:, None] - key_pos[None, :], 0)]
+            a = np.where(allowed, w, 0.0)
             a = R(a)
             o_u[s:s + block, cols] = R(inv * (a @ vh))
             if counter is not None:
@@ -183,8 +195,13 @@ def attention_user(q_u, k_all, v_all, q_c, k_c, v_c, *, m: int, heads: int, inv:
                 counter.attn_pv += int(allowed.sum()) * dh
         for s in range(0, c, block):
             qc = q_c[s:s + block, cols]
-            a = R(silu(qc @ kh.T))
-            a_self = R(silu(np.sum(qc * k_c[s:s + block, cols], axis=1)))
+            w = silu(qc @ kh.T)
+            w_self = silu(np.sum(qc * k_c[s:s + block, cols], axis=1))
+            if rel is not None:
+                w = w + rel[h][(m + n) - key_pos][None, :]
+                w_self = w_self + rel[h][0]
+            a = R(w)
+            a_self = R(w_self)
             o_c[s:s + block, cols] = R(inv * (a @ vh + a_self[:, None] * v_c[s:s + block, cols]))
             if counter is not None:
                 counter.attn_qk += qc.shape[0] * nkeys * dh
@@ -194,14 +211,15 @@ def attention_user(q_u, k_all, v_all, q_c, k_c, v_c, *, m: int, heads: int, inv:
 
 
 def _project(x, w1, pos_table, positions, bf16, counter):
-    """S = SiLU(norm(X) W1) split into U, V, Q, K; position bias on V, Q, K (not U).
-    The normalised rows are never stored, so they take no rounding in either mode."""
+    """S = SiLU(norm(X) W1) split into U, V, Q, K; position bias on V, Q, K (not U),
+    none when pos_table is None. The normalised rows are never stored, so they take no
+    rounding in either mode."""
     D = x.shape[1]
     R = round_bf16 if bf16 else (lambda a: a)
     s = silu(normalize_rows(x) @ w1)
     if counter is not None:
         counter.gemm_uvqk += x.shape[0] * D * 4 * D
-    bias = pos_table[positions]
+    bias = pos_table[positions] if pos_table is not None else np.zeros((x.shape[0], 3 * D))
     u = R(s[:, 0:D])
     v = R(s[:, D:2 * D] + bias[:, 0:D])
     q = R(s[:, 2 * D:3 * D] + bias[:, D:2 * D])
@@ -223,7 +241,7 @@ def _output(x, u, o, w2, bf16, counter):
 def layer_user(x_u, x_c, w1, w2, pos_table, *, k_cached, v_cached, heads: int, max_len: int,
                bf16: bool, counter: Optional[MacCounter] = None,
                uih_rows: Optional[Sequence[int]] = None,
-               cand_rows: Optional[Sequence[int]] = None):
+               cand_rows: Optional[Sequence[int]] = None, rel=None):
     """One encoder layer for one user.
 
     x_u [n, D] new history tokens, x_c [c, D] candidates, k_cached/v_cached [m, D]
@@ -245,7 +263,7 @@ def layer_user(x_u, x_c, w1, w2, pos_table, *, k_cached, v_cached, heads: int, m
     k_all = np.concatenate([k_cached, k_u], axis=0)
     v_all = np.concatenate([v_cached, v_u], axis=0)
     o_u, o_c = attention_user(q_u, k_all, v_all, q_c, k_c, v_c, m=m, heads=heads,
-                              inv=1.0 / max_len, bf16=bf16, counter=counter, uih_rows=uih_rows)
+                              inv=1.0 / max_len, bf16=bf16, counter=counter, uih_rows=uih_rows, rel=rel)
     rows = np.arange(n) if uih_rows is None else np.asarray(uih_rows, dtype=np.int64)
     y_u = _output(x_u[rows], u_u[rows], o_u, w2, bf16, counter)
     y_c = _output(x_c, u_c, o_c, w2, bf16, counter)
@@ -258,8 +276,9 @@ def encode(uih, uih_offsets, cand, cand_offsets, params, *, heads: int, max_len:
     """The whole layer stack over a jagged batch.
 
     uih [Nu, D], cand [Nc, D]: tokens in jagged layout with int offsets [B+1].
-    params: per layer (w1 [D,4D], w2 [3D,D], pos [max_len,3D]) in math layout
-    (objects with .w1/.w2/.pos or 3-tuples). mode: "f64" or "bf16".
+    params: per layer (w1 [D,4D], w2 [3D,D], pos [max_len,3D] or None, and optionally
+    rel [heads, max_len] or None) in math layout (objects with .w1/.w2/.pos[/.rel] or
+    3- or 4-tuples). mode: "f64" or "bf16".
     cache: None (no earlier history) or an OracleCache; a copy is returned with
     every layer's new keys/values appended and cached_len advanced.
     users: optional subset of user indices to compute (the others' rows are NaN).
@@ -271,8 +290,9 @@ def encode(uih, uih_offsets, cand, cand_offsets, params, *, heads: int, max_len:
     uih = np.asarray(uih, dtype=np.float64)
     cand = np.asarray(cand, dtype=np.float64)
     D = uih.shape[1]
-    layers = [(p.w1, p.w2, p.pos) if hasattr(p, "w1") else tuple(p) for p in params]
-    layers = [tuple(np.asarray(a, dtype=np.float64) for a in lp) for lp in layers]
+    layers = [(p.w1, p.w2, p.pos, getattr(p, "rel", None)) if hasattr(p, "w1") else (tuple(p) + (None,))[:4]
+              for p in params]
+    layers = [tuple(None if a is None else np.asarray(a, dtype=np.float64) for a in lp) for lp in layers]
     B = len(uih_offsets) - 1
     new_cache = cache.copy() if cache is not None else None
     uih_out = np.full_like(uih, np.nan)
@@ -287,14 +307,14 @@ def encode(uih, uih_offsets, cand, cand_offsets, params, *, heads: int, max_len:
                 raise ValueError("cache capacity exceeded")
         else:
             slot, m = -1, 0
-        for l, (w1, w2, pos) in enumerate(layers):
+        for l, (w1, w2, pos, rel) in enumerate(layers):
             if new_cache is not None:
                 kc, vc = new_cache.k[l, slot, :m], new_cache.v[l, slot, :m]
             else:
                 kc, vc = np.zeros((0, D)), np.zeros((0, D))
             xu, xc, k_new, v_new = layer_user(xu, xc, w1, w2, pos, k_cached=kc, v_cached=vc,
                                               heads=heads, max_len=max_len, bf16=bf16,
-                                              counter=counter)
+                                              counter=counter, rel=rel)
             if new_cache is not None:
                 new_cache.k[l, slot, m:m + n] = k_new
                 new_cache.v[l, slot, m:m + n] = v_new

@@ -291,6 +291,115 @@ def test_zero_query_gives_zero_attention(mode):
         assert rel(x_u, want) < 1e-14
 
 
+# --------------------------------------------------------------------------- relative bias
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_relative_bias_single_history_token(bf16):
+    """Pin (closed form): one history token with a relative bias table: its weight is
+    SiLU(q.k) + rel[h, 0] (relative position 0), so O = (SiLU(q.k) + rel[h, 0]) v / max_len."""
+    rng = np.random.default_rng(41)
+    D, H, max_len = 8, 2, 10
+    q, k, v = _qkv(rng, 1, D)
+    table = rng.standard_normal((H, max_len)) * 0.3
+    if bf16:
+        q, k, v, table = (oracle.round_bf16(a) for a in (q, k, v, table))
+    o_u, _ = oracle.attention_user(q, k, v, np.zeros((0, D)), np.zeros((0, D)), np.zeros((0, D)),
+                                   m=0, heads=H, inv=1.0 / max_len, bf16=bf16, rel=table)
+    for h in range(H):
+        s = slice(h * 4, h * 4 + 4)
+        dot = sum(q[0, t] * k[0, t] for t in range(h * 4, h * 4 + 4))
+        a = dot / (1 + math.exp(-dot)) + table[h, 0]
+        if bf16:
+            a = brute.bf16_round(a)
+            want = [brute.bf16_round(a * x / max_len) for x in v[0, s]]
+        else:
+            want = [a * x / max_len for x in v[0, s]]
+        assert np.allclose(o_u[0, s], want, rtol=1e-15, atol=0)
+
+
+def test_relative_bias_two_tokens_with_cache_and_candidate():
+    """Pin (closed form): one cached key (position 0), two new rows (positions 1, 2) and one
+    candidate (position 3): each weight picks rel[pos_query - pos_key]."""
+    rng = np.random.default_rng(42)
+    D, max_len = 4, 7
+    q, k, v = _qkv(rng, 3, D)                # row 0 is the cached key/value, rows 1, 2 are new
+    qc, kc, vc = _qkv(rng, 1, D)
+    t = rng.standard_normal((1, max_len))
+    o_u, o_c = oracle.attention_user(q[1:], k, v, qc, kc, vc, m=1, heads=1, inv=1.0 / max_len,
+                                     bf16=False, rel=t)
+    sl = lambda x: x / (1 + math.exp(-x))
+    want1 = ((sl(q[1] @ k[0]) + t[0, 1]) * v[0] + (sl(q[1] @ k[1]) + t[0, 0]) * v[1]) / max_len
+    want2 = ((sl(q[2] @ k[0]) + t[0, 2]) * v[0] + (sl(q[2] @ k[1]) + t[0, 1]) * v[1]
+             + (sl(q[2] @ k[2]) + t[0, 0]) * v[2]) / max_len
+    wantc = (sum((sl(qc[0] @ k[j]) + t[0, 3 - j]) * v[j] for j in range(3))
+             + (sl(qc[0] @ kc[0]) + t[0, 0]) * vc[0]) / max_len
+    assert np.allclose(o_u[0], want1, rtol=1e-14) and np.allclose(o_u[1], want2, rtol=1e-14)
+    assert np.allclose(o_c[0], wantc, rtol=1e-14)
+
+
+def test_relative_bias_zero_query_is_a_causal_convolution():
+    """Pin (library routine): with q = 0 every SiLU term vanishes and history row i gets
+    O_i = inv * sum_{j <= m+i} rel[m+i-j] v_j, a causal convolution of V with the table,
+    computed here by numpy.convolve; a candidate gets inv * (sum_j rel[m+n-j] v_j + rel[0] v_c)."""
+    rng = np.random.default_rng(43)
+    D, H, m, n, c, max_len = 6, 2, 3, 9, 2, 20
+    k_all = rng.standard_normal((m + n, D))
+    v_all = rng.standard_normal((m + n, D))
+    vc = rng.standard_normal((c, D))
+    table = rng.standard_normal((H, max_len))
+    o_u, o_c = oracle.attention_user(np.zeros((n, D)), k_all, v_all, np.zeros((c, D)),
+                                     rng.standard_normal((c, D)), vc, m=m, heads=H, inv=0.25,
+                                     bf16=False, rel=table)
+    dh = D // H
+    for h in range(H):
+        for t in range(h * dh, (h + 1) * dh):
+            conv = np.convolve(table[h], v_all[:, t])          # conv[p] = sum_j table[p - j] v_j
+            assert np.allclose(o_u[:, t], 0.25 * conv[m:m + n], rtol=1e-13, atol=1e-13)
+            cand_want = 0.25 * (conv[m + n] + table[h, 0] * vc[:, t])
+            assert np.allclose(o_c[:, t], cand_want, rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("position", ["relative", "both"])
+@pytest.mark.parametrize("mode", ["f64", "bf16"])
+def test_oracle_matches_brute_force_relative_bias(position, mode):
+    """Pin: the stack with a relative bias (alone, and with the absolute table) re-derived
+    with scalar loops, including cached history, an empty history and no candidates."""
+    uih, cand, cached = [3, 0, 5], [2, 3, 0], [2, 3, 0]
+    wl = workloads.make_custom(seed=44, dtype="bf16" if mode == "bf16" else "f32", layers=2, d_model=4,
+                               heads=2, max_len=16, uih_lengths=uih, cand_lengths=cand,
+                               cached_lengths=cached, position=position, rel_std=0.5)
+    assert (wl.params[0].pos is None) == (position == "relative") and wl.params[0].rel is not None
+    cache = random_cache(wl, 45, capacity=8, bf16=(mode == "bf16"))
+    got_u, got_c, _ = run_oracle(wl, mode, cache=cache)
+    ck = [[[list(map(float, cache.k[l, b, j])) for j in range(cached[b])] for b in range(3)]
+          for l in range(wl.layers)]
+    cv = [[[list(map(float, cache.v[l, b, j])) for j in range(cached[b])] for b in range(3)]
+          for l in range(wl.layers)]
+    tolist = lambda a: None if a is None else a.astype(np.float64).tolist()
+    params = [(tolist(p.w1), tolist(p.w2), tolist(p.pos), tolist(p.rel)) for p in wl.params]
+    bu, bc = brute.encode_brute(wl.uih.astype(np.float64).tolist(),
+                                workloads.lengths_to_offsets(uih).tolist(),
+                                wl.cand.astype(np.float64).tolist(),
+                                workloads.lengths_to_offsets(cand).tolist(), params,
+                                heads=wl.heads, max_len=wl.max_len, bf16=(mode == "bf16"),
+                                cached_k=ck, cached_v=cv, cached_len=cached)
+    assert rel(got_u, np.array(bu)) <= 1e-12
+    assert rel(got_c, np.array(bc)) <= 1e-12
+
+
+def test_relative_bias_history_independent_of_candidates():
+    """Pin (invariant): with a relative bias the history outputs are still bit-identical
+    for any candidate set (the bias depends on positions only)."""
+    base = workloads.make_custom(seed=46, dtype="bf16", layers=2, d_model=16, heads=2, max_len=80,
+                                 uih_lengths=[20, 33], cand_lengths=[6, 6], position="relative",
+                                 rel_std=0.5)
+    ref_u, _, _ = run_oracle(base, "bf16")
+    for cl in ([0, 0], [6, 6], [3, 1]):
+        cand = base.cand[:sum(cl)] if sum(cl) else np.zeros((0, 16), np.float32)
+        got_u, _, _ = run_oracle(base, "bf16", cand=cand, cand_lengths=np.array(cl))
+        assert np.array_equal(got_u, ref_u)
+
+
 # --------------------------------------------------------------------------- invariants
 
 def test_uih_outputs_bit_identical_for_any_candidate_set():

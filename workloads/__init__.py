@@ -13,12 +13,15 @@ time order. That dataset is not available here; the workloads below stand in for
   the encoder), N(0, 1);
 * per layer, the fused projection weight W1 [D, 4D] ~ N(0, var 1/D), the output
   weight W2 [3D, D] ~ N(0, var 1/D) and the absolute position-bias table
-  P [max_len, 3D] ~ N(0, std 0.02);
+  P [max_len, 3D] ~ N(0, std 0.02); workloads in the original HSTU form (the page's
+  "Time/position encoding" paragraph) draw instead, or as well, a relative bias
+  table R [heads, max_len] ~ N(0, std 0.02 unless stated) over pos_i - pos_j;
 * UIH lengths follow each workload's distribution; the streaming workload draws a
   cached prefix plus newly appended events per user.
 
 Values are drawn in float32 from ``numpy.random.Generator(PCG64(seed))`` in a fixed
-order (lengths; per user UIH then candidate embeddings; per layer W1, W2, P).
+order (lengths; per user UIH then candidate embeddings; per layer W1, W2, then P and/or
+R).
 For bfloat16 workloads every drawn value is then stored once as the nearest
 bfloat16 (round to nearest even), so both sides consume identical bits.
 """
@@ -47,6 +50,7 @@ class WorkloadSpec:
     d_model: int
     heads: int
     max_len: int          # rows of the position-bias table = UIH bound + 1 candidate slot
+    position: str = "absolute"   # "absolute" (P on V, Q, K), "relative" (R on the weights) or "both"
 
 
 # The five workloads. The headline one is "d512_uih2k_c2k" (D=512, UIH ~2K, 2K candidates).
@@ -58,6 +62,9 @@ WORKLOADS: Dict[str, WorkloadSpec] = {
                      512, 4, 4097),
         WorkloadSpec("stream_3000p300_c2k", 4, 8, "bf16", 64, ("fixed", 300), 3000, 2048, 512, 4, 3301),
         WorkloadSpec("long_uih16k_c2k", 5, 16, "bf16", 4, ("uniform", 8192, 16384), 0, 2048, 512, 8, 16385),
+        # the headline shapes in the original HSTU form: relative position bias only
+        WorkloadSpec("d512_uih2k_c2k_rel", 6, 8, "bf16", 16, ("lognormal", 2000, 0.5, 512, 4096), 0, 2048,
+                     512, 4, 4097, "relative"),
     ]
 }
 
@@ -68,11 +75,14 @@ class LayerParams:
 
     w1:  [D, 4D]; G = X @ w1; column blocks U, V, Q, K.
     w2:  [3D, D]; Z = [U | O | U*O] @ w2; row blocks U, O, U*O.
-    pos: [max_len, 3D]; column blocks added to V, Q, K.
+    pos: [max_len, 3D]; column blocks added to V, Q, K (None: no absolute bias).
+    rel: [heads, max_len]; rel[h, d] added to head h's attention weights at relative
+         position d = pos_i - pos_j (None: no relative bias).
     """
     w1: np.ndarray
     w2: np.ndarray
-    pos: np.ndarray
+    pos: Optional[np.ndarray]
+    rel: Optional[np.ndarray] = None
 
 
 @dataclasses.dataclass
@@ -140,7 +150,8 @@ def _finish(spec_dtype, arrays):
 
 
 def make_custom(*, seed: int, dtype: str, layers: int, d_model: int, heads: int, max_len: int,
-                uih_lengths, cand_lengths, cached_lengths=None, name: str = "custom") -> Workload:
+                uih_lengths, cand_lengths, cached_lengths=None, name: str = "custom",
+                position: str = "absolute", rel_std: float = 0.02) -> Workload:
     """A workload with explicit lengths (tests: ragged tails, empty users, tiny shapes)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     uih_lengths = np.asarray(uih_lengths, dtype=np.int64)
@@ -149,10 +160,13 @@ def make_custom(*, seed: int, dtype: str, layers: int, d_model: int, heads: int,
     cached_lengths = (np.zeros(B, dtype=np.int64) if cached_lengths is None
                       else np.asarray(cached_lengths, dtype=np.int64))
     return _draw_rest(rng, name, dtype, layers, d_model, heads, max_len,
-                      uih_lengths, cand_lengths, cached_lengths)
+                      uih_lengths, cand_lengths, cached_lengths, position, rel_std)
 
 
-def _draw_rest(rng, name, dtype, layers, D, H, max_len, uih_lengths, cand_lengths, cached_lengths):
+def _draw_rest(rng, name, dtype, layers, D, H, max_len, uih_lengths, cand_lengths, cached_lengths,
+               position="absolute", rel_std=0.02):
+    if position not in ("absolute", "relative", "both"):
+        raise ValueError(position)
     prefix_parts, uih_parts, cand_parts = [], [], []
     for b in range(uih_lengths.shape[0]):
         m, n, c = int(cached_lengths[b]), int(uih_lengths[b]), int(cand_lengths[b])
@@ -164,9 +178,13 @@ def _draw_rest(rng, name, dtype, layers, D, H, max_len, uih_lengths, cand_length
     for _ in range(layers):
         w1 = _normal(rng, (D, 4 * D), 1.0 / math.sqrt(D))
         w2 = _normal(rng, (3 * D, D), 1.0 / math.sqrt(D))
-        pos = _normal(rng, (max_len, 3 * D), 0.02)
-        w1, w2, pos = _finish(dtype, [w1, w2, pos])
-        params.append(LayerParams(w1, w2, pos))
+        w1, w2 = _finish(dtype, [w1, w2])
+        pos = rel = None
+        if position in ("absolute", "both"):
+            pos = _finish(dtype, [_normal(rng, (max_len, 3 * D), 0.02)])[0]
+        if position in ("relative", "both"):
+            rel = _finish(dtype, [_normal(rng, (H, max_len), rel_std)])[0]
+        params.append(LayerParams(w1, w2, pos, rel))
     cat = lambda parts: (np.concatenate(parts, axis=0) if parts else np.zeros((0, D), np.float32))
     prefix, uih, cand = _finish(dtype, [cat(prefix_parts), cat(uih_parts), cat(cand_parts)])
     return Workload(name=name, dtype=dtype, layers=layers, d_model=D, heads=H, max_len=max_len,
@@ -189,4 +207,4 @@ def make_workload(name: str, *, users: Optional[int] = None, layers: Optional[in
     cands = np.full(B, spec.cands, dtype=np.int64)
     cached = np.full(B, spec.cached, dtype=np.int64)
     return _draw_rest(rng, spec.name, spec.dtype, L, spec.d_model, spec.heads, spec.max_len,
-                      lengths, cands, cached)
+                      lengths, cands, cached, spec.position)
