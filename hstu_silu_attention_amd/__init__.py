@@ -32,7 +32,8 @@ class HstuDims(ctypes.Structure):
 
 
 class HstuLayerWeights(ctypes.Structure):
-    _fields_ = [("w_uvqk", ctypes.c_void_p), ("w_out", ctypes.c_void_p), ("pos_bias", ctypes.c_void_p)]
+    _fields_ = [("w_uvqk", ctypes.c_void_p), ("w_out", ctypes.c_void_p), ("pos_bias", ctypes.c_void_p),
+                ("rel_bias", ctypes.c_void_p)]
 
 
 class HstuKvCache(ctypes.Structure):
@@ -159,8 +160,9 @@ def _torch():
 class Model:
     """Device-resident parameters of an encoder stack in the ABI's layout.
 
-    ``params``: per layer objects with ``w1`` [D,4D], ``w2`` [3D,D], ``pos`` [max_len,3D]
-    (math layout, float32 numpy arrays); they are stored transposed as [out][in].
+    ``params``: per layer objects with ``w1`` [D,4D], ``w2`` [3D,D], ``pos`` [max_len,3D] or
+    None and optionally ``rel`` [heads,max_len] or None (math layout, float32 numpy
+    arrays); the weights are stored transposed as [out][in].
     """
 
     def __init__(self, params, *, d_model: int, heads: int, max_len: int, dtype: str, device="cuda"):
@@ -169,12 +171,12 @@ class Model:
         self.dtype_code = HSTU_BF16 if dtype == "bf16" else HSTU_F32
         self.torch_dtype = torch.bfloat16 if dtype == "bf16" else torch.float32
         self.layers: List[Tuple] = []
+        dev = lambda a: (None if a is None else
+                         torch.from_numpy(np.ascontiguousarray(a)).to(device=device, dtype=self.torch_dtype).contiguous())
+        ptr = lambda t: None if t is None else t.data_ptr()
         for p in params:
-            w1 = torch.from_numpy(np.ascontiguousarray(p.w1.T)).to(device=device, dtype=self.torch_dtype)
-            w2 = torch.from_numpy(np.ascontiguousarray(p.w2.T)).to(device=device, dtype=self.torch_dtype)
-            pos = torch.from_numpy(np.ascontiguousarray(p.pos)).to(device=device, dtype=self.torch_dtype)
-            self.layers.append((w1.contiguous(), w2.contiguous(), pos.contiguous()))
-        self.weights = [HstuLayerWeights(a.data_ptr(), b.data_ptr(), c.data_ptr()) for a, b, c in self.layers]
+            self.layers.append((dev(p.w1.T), dev(p.w2.T), dev(p.pos), dev(getattr(p, "rel", None))))
+        self.weights = [HstuLayerWeights(ptr(a), ptr(b), ptr(c), ptr(r)) for a, b, c, r in self.layers]
 
     def dims(self, layers: Optional[int] = None) -> HstuDims:
         return _dims(len(self.layers) if layers is None else layers, self.d_model, self.heads,

@@ -102,11 +102,20 @@ __device__ __forceinline__ float silu_bias(float x, float nlog2e, float bias) {
   return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(__builtin_fmaf(x, nlog2e, bias)));
 }
 
-template <int DH>
+// Relative bias (REL): each weight gains rel[h][pos_i - pos_j] after its SiLU. The head's
+// table is staged in LDS (kTabPad zero entries, then the table from the 16-byte-aligned
+// address at or before its start, mis entries early), so entry d sits at
+// tab[kTabPad + mis + d]; a lane reads its 16 weights' entries there. Wholly masked halves
+// read the zero pad instead, so every step stays branch-free.
+constexpr int kTabPad = 64, kTabEntries = 8192;
+static_assert(kTabPad + ((kRelMaxLen + 32 + 7 + 7) / 8 + 63) / 64 * 512 <= kTabEntries, "table must fit");
+
+template <int DH, bool REL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_kernel(AttnArgs a) {
   using C = AttnTile<DH>;
   __shared__ __attribute__((aligned(16))) u16 ks0[C::SLOT], ks1[C::SLOT], vs0[C::SLOT], vs1[C::SLOT];
+  __shared__ __attribute__((aligned(16))) u16 tab[REL ? kTabEntries : 8];
 
   const AttnItem it = a.items[blockIdx.x];
   if (it.nq <= 0) return;
@@ -151,6 +160,18 @@ void attn_kernel(AttnArgs a) {
   const int nbytes = key_end * ld * 2;
   const i32x4 rk_src = buffer_desc((const u16*)a.kbase + (size_t)it.key_row * a.ld + head * DH, nbytes);
   const i32x4 rv_src = buffer_desc((const u16*)a.vbase + (size_t)it.key_row * a.ld + head * DH, nbytes);
+  // relative bias table of this head, read from the 16-byte-aligned address at or before it
+  int mis = 0, tab_chunks = 0;
+  i32x4 rel_src = {0, 0, 0, 0};
+  if (REL) {
+    const uintptr_t hb = (uintptr_t)((const u16*)a.rel + (size_t)head * a.max_len);
+    const uintptr_t ab = hb & ~(uintptr_t)15;
+    const uintptr_t end = (uintptr_t)((const u16*)a.rel + (size_t)(D / DH) * a.max_len);
+    mis = (int)((hb - ab) / 2);
+    // entries mis .. mis + key_end + 32 cover every relative position a step looks up
+    tab_chunks = (mis + key_end + 32 + 7) / 8;
+    rel_src = buffer_desc((const void*)ab, (int)(end - ab));
+  }
 
   // 64-lane LDS loads: load j of a region covers rows RPI*j.. of it; lane i brings the
   // global chunk that belongs at row RPI*j + i/CPR, slot i%CPR
@@ -213,6 +234,18 @@ void attn_kernel(AttnArgs a) {
   const float kInf = __builtin_huge_valf();
   // bias of query block qb in half h: 0 for halves wholly before the block's first row
   auto bias = [&](int h, int qb) { return cand || wf + 32 * qb - 32 * h > 0 ? 0.0f : kInf; };
+  // Relative bias of the weights of query block qb in half h, elements e0 .. e0 + 7
+  // (element e <-> key 8*(e/4) + 4*hi + e%4 of the half, query row l32): pos_q - pos_k is
+  // wf + 32*qb - 32*h + l32 - key for history rows, key_end - 32*h - key for candidates.
+  auto rel_bias = [&](int h, int qb, int e0, float (&r)[8]) {
+    if (!REL) return;
+    const int d0 = cand ? key_end - 32 * h : wf + 32 * qb - 32 * h;
+    const int tb = bias(h, qb) == 0.0f ? kTabPad + mis + d0 : 31;   // masked: the zero pad
+    const u16* tl = tab + tb + (cand ? 0 : l32) - 4 * hi;
+#pragma unroll
+    for (int e = e0; e < e0 + 8; ++e)
+      r[e - e0] = __uint_as_float((uint32_t)tl[-(8 * (e >> 2) + (e & 3))] << 16);
+  };
 
   // Step h: (si, wi) = scores of half h, weights of half h - 1 -> (so, wo) = scores of
   // half h + 1, weights of half h.
@@ -234,8 +267,13 @@ void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int qb = 0; qb < C::QB; ++qb) {
       const float b = bias(h, qb);
+      float r[8] = {};
+      rel_bias(h, qb, 0, r);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) wo[qb][e >> 3][e & 7] = (__bf16)silu_bias(si[qb][e], nlog2e, b);
+      for (int e = 0; e < 8; ++e) {
+        const float x = silu_bias(si[qb][e], nlog2e, b);
+        wo[qb][e >> 3][e & 7] = (__bf16)(REL ? x + r[e] : x);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     bf16x8 vf[2][C::MB];
@@ -245,8 +283,13 @@ void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int qb = 0; qb < C::QB; ++qb) {
       const float b = bias(h, qb);
+      float r[8] = {};
+      rel_bias(h, qb, 8, r);
 #pragma unroll
-      for (int e = 8; e < 16; ++e) wo[qb][e >> 3][e & 7] = (__bf16)silu_bias(si[qb][e], nlog2e, b);
+      for (int e = 8; e < 16; ++e) {
+        const float x = silu_bias(si[qb][e], nlog2e, b);
+        wo[qb][e >> 3][e & 7] = (__bf16)(REL ? x + r[e - 8] : x);
+      }
     }
   };
 
@@ -257,6 +300,12 @@ void attn_kernel(AttnArgs a) {
   load_k(ks0, 0);
   load_k(ks1, 1);
   load_v(vs0, 0);
+  if (REL) {
+    if (tid < kTabPad / 8) *reinterpret_cast<uint4*>(tab + 8 * tid) = make_uint4(0, 0, 0, 0);
+    const uint32_t tab_lds = (uint32_t)(uintptr_t)(lds_void*)(tab + kTabPad);
+    for (int j = wv; j * 64 < tab_chunks; j += C::WAVES)   // 64 chunks of 8 entries per load
+      lds_load16(rel_src, __builtin_amdgcn_readfirstlane(tab_lds + j * 1024), (j * 64 + lane) * 16);
+  }
   wait_loads();
   __syncthreads();
   // ping-pong state: (sA, wA) enters the even steps, (sB, wB) the odd ones
@@ -321,7 +370,10 @@ void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int j = 8 * (e >> 2) + 4 * hi + (e & 3);
-        w[e >> 3][e & 7] = (__bf16)silu_bias(sd[e], nlog2e, j <= l32 ? 0.0f : kInf);
+        // relative position l32 - j on the diagonal
+        const float r = REL && j <= l32 ? __uint_as_float((uint32_t)tab[kTabPad + mis + l32 - j] << 16) : 0.0f;
+        const float x = silu_bias(sd[e], nlog2e, j <= l32 ? 0.0f : kInf);
+        w[e >> 3][e & 7] = (__bf16)(REL ? x + r : x);
       }
       read_v_at(dv, vf);
       pv_mfma(vf, qb, w);
@@ -347,7 +399,8 @@ void attn_kernel(AttnArgs a) {
         }
       }
       const float dot = part + __shfl_xor(part, 32);
-      const float as = qok[qb] ? round_bf(silu(dot)) : 0.0f;
+      const float r0 = REL ? __uint_as_float((uint32_t)tab[kTabPad + mis] << 16) : 0.0f;   // position 0
+      const float as = qok[qb] ? round_bf(REL ? silu(dot) + r0 : silu(dot)) : 0.0f;
       if (qok[qb]) {
 #pragma unroll
         for (int mb = 0; mb < C::MB; ++mb)
@@ -380,10 +433,15 @@ void attn_kernel(AttnArgs a) {
 
 hipError_t launch_attn_bf16(int dh, const AttnArgs& a, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  if (dh == 64)
-    attn_kernel<64><<<grid, AttnTile<64>::NT, 0, s>>>(a);
+  const bool rel = a.rel != nullptr;
+  if (dh == 64 && !rel)
+    attn_kernel<64, false><<<grid, AttnTile<64>::NT, 0, s>>>(a);
+  else if (dh == 64)
+    attn_kernel<64, true><<<grid, AttnTile<64>::NT, 0, s>>>(a);
+  else if (dh == 128 && !rel)
+    attn_kernel<128, false><<<grid, AttnTile<128>::NT, 0, s>>>(a);
   else if (dh == 128)
-    attn_kernel<128><<<grid, AttnTile<128>::NT, 0, s>>>(a);
+    attn_kernel<128, true><<<grid, AttnTile<128>::NT, 0, s>>>(a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -356,7 +356,7 @@ void uvqk_kernel(UvqkArgs a) {
   constexpr int RSTEP_O = C::NT / CPR;
   static_assert(C::NT % CPR == 0, "a thread keeps its chunk column");
   const int r_first = threadIdx.x / CPR, cc = (threadIdx.x % CPR) * 8;
-  if (slice > 0) {
+  if (slice > 0 && a.pos != nullptr) {
     // a position table has fewer than 2^31 elements (checked on the host), so a
     // position's element offset is a 24 x 24-bit product
     const u16* pos = (const u16*)a.pos + (slice - 1) * D + (col0 - slice * D) + cc;

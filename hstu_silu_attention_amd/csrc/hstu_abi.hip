@@ -299,9 +299,11 @@ hstu_status hstu_encode(const hstu_dims* d, int32_t B, const int32_t* uih_offset
   if (lay.T == 0) return HSTU_OK;  // nothing to encode; no history appended
   const int32_t L = d->layers, D = d->d_model;
   for (int32_t l = 0; l < L; ++l) {
-    if (!w[l].w_uvqk || !w[l].w_out || !w[l].pos_bias) return HSTU_ERR_NULL;
-    if (!aligned16(w[l].w_uvqk) || !aligned16(w[l].w_out) || !aligned16(w[l].pos_bias))
+    if (!w[l].w_uvqk || !w[l].w_out) return HSTU_ERR_NULL;
+    if (!aligned16(w[l].w_uvqk) || !aligned16(w[l].w_out) || !aligned16(w[l].pos_bias) ||
+        !aligned16(w[l].rel_bias))
       return HSTU_ERR_ALIGN;
+    if (w[l].rel_bias && d->dtype == HSTU_BF16 && d->max_len > hstu::kRelMaxLen) return HSTU_ERR_SHAPE;
   }
   if ((lay.Nu > 0 && (!uih || !uih_out)) || (lay.Nc > 0 && (!cand || !cand_out))) return HSTU_ERR_NULL;
   if ((lay.Nu > 0 && (!aligned16(uih) || !aligned16(uih_out))) ||
@@ -478,6 +480,8 @@ hstu_status hstu_encode(const hstu_dims* d, int32_t B, const int32_t* uih_offset
       aa.ld = 3 * (int64_t)D;
     }
     aa.aout = aout;
+    aa.rel = w[l].rel_bias;
+    aa.max_len = d->max_len;
     if (timed_launch(HSTU_KERNEL_ATTENTION, s,
                      [&] { return hstu::launch_attn(d->dtype, dh, aa, attn_grid, s); }) != hipSuccess)
       return HSTU_ERR_HIP;

@@ -85,7 +85,7 @@ struct UvqkArgs {
   const float2* st;      // [T][D/128] row statistics of the layer input (bfloat16 path)
   int32_t Nu, T, D;
   const void* w;         // [4D][D]
-  const void* pos;       // [max_len][3D]
+  const void* pos;       // [max_len][3D], or nullptr (no absolute position bias)
   const int2* row_info;
   const UserRec* users;
   void* vqk;             // [T_pad][3D] out: V, Q, K (rows < T written)
@@ -103,7 +103,13 @@ struct AttnArgs {
   const void* vbase;
   int64_t ld;
   void* aout;            // [T_pad][3D]: writes O (float32 also reads U, writes U*O)
+  const void* rel;       // this layer's relative bias [H][max_len], or nullptr
+  int32_t max_len;
 };
+
+// Largest max_len of a bfloat16 model with a relative bias: the attention stages a
+// head's table (plus a zero pad) in 16 KB of LDS.
+constexpr int kRelMaxLen = 7600;
 
 struct OutArgs {
   const void* aout;      // [T_pad][3D] A operand [U | O | U*O] (bfloat16: U | O read)

@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void uvqk_f32_kernel(UvqkArgs a) {
     const int2 ri = a.row_info[row];
     const int slice = col / D, cc = col - slice * D;
     float v = silu(g);
-    if (slice > 0) v += pos[(size_t)ri.y * 3 * D + (slice - 1) * D + cc];
+    if (slice > 0 && pos != nullptr) v += pos[(size_t)ri.y * 3 * D + (slice - 1) * D + cc];
     // U into the output GEMM's operand buffer, V / Q / K into the attention's
     if (slice == 0)
       ((float*)a.aout)[(size_t)row * 3 * D + cc] = v;
@@ -120,7 +120,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
     acc[e] = 0.0f;
   }
   const int key_end = it.key_end;
-  const int qpos = it.m + it.q0 + tid;
+  const int qpos = cand ? key_end : it.m + it.q0 + tid;   // candidates sit at m + n
+  const float* rel = a.rel == nullptr ? nullptr : (const float*)a.rel + (size_t)head * a.max_len;
   const float* kp = (const float*)a.kbase + (size_t)it.key_row * a.ld + head * DH;
   const float* vp = (const float*)a.vbase + (size_t)it.key_row * a.ld + head * DH;
   for (int k0 = 0; k0 < key_end; k0 += FKB) {
@@ -139,7 +140,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
       float s = 0.0f;
 #pragma unroll
       for (int e = 0; e < DH; ++e) s += q[e] * sk[j][e];
-      const float w = silu(s);
+      const float w = silu(s) + (rel != nullptr ? rel[qpos - key] : 0.0f);
 #pragma unroll
       for (int e = 0; e < DH; ++e) acc[e] += w * sv[j][e];
     }
@@ -151,7 +152,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
     float s = 0.0f;
 #pragma unroll
     for (int e = 0; e < DH; ++e) s += q[e] * krow[e];
-    const float w = silu(s);
+    const float w = silu(s) + (rel != nullptr ? rel[0] : 0.0f);
 #pragma unroll
     for (int e = 0; e < DH; ++e) acc[e] += w * vrow[e];
   }

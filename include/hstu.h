@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 1
+#define HSTU_ABI_VERSION 2
 
 /* Element type of every device tensor of a call. */
 enum hstu_dtype { HSTU_F32 = 0, HSTU_BF16 = 1 };
@@ -101,11 +101,18 @@ typedef struct hstu_dims {
  *           the math-layout W1 [D][4D]); row blocks U, V, Q, K.
  *  w_out    [D][3D]: output feature j of the output GEMM in row j (the transpose of
  *           W2 [3D][D]); column blocks U, O, U*O.
- *  pos_bias [max_len][3D]: row p is the bias of position p; column blocks V, Q, K. */
+ *  pos_bias [max_len][3D]: row p is the absolute bias of position p, added to V, Q, K
+ *           after the SiLU (column blocks V, Q, K); NULL: no absolute bias.
+ *  rel_bias [H][max_len]: rel_bias[h][d] is added to every attention weight
+ *           SiLU(q_i . k_j) of head h whose relative position pos_i - pos_j is d
+ *           (the original HSTU form Mask(SiLU(Q K^T) + bias) V from the DLRMv3
+ *           page's "Model selection" section); NULL: no relative bias.
+ * w_uvqk, w_out and any non-NULL table are 16-byte aligned. */
 typedef struct hstu_layer_weights {
   const void* w_uvqk;
   const void* w_out;
   const void* pos_bias;
+  const void* rel_bias;
 } hstu_layer_weights;
 
 /* Streaming key/value cache (caller-owned).

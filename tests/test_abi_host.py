@@ -176,6 +176,15 @@ def test_encode_rejects_before_launch():
     assert a.call() == ERR_NULL
     a.w[1] = hsa.HstuLayerWeights(0x10000, 0x20004, 0x30000)
     assert a.call() == ERR_ALIGN
+    a.w[1] = hsa.HstuLayerWeights(0x10000, 0x20000, 0x30000, 0x38008)   # relative table misaligned
+    assert a.call() == ERR_ALIGN
+
+
+def test_encode_rejects_relative_bias_past_the_staged_table():
+    """A bfloat16 model with a relative bias stages each head's table in LDS: max_len <= 7600."""
+    a = FakeArgs(max_len=7601)
+    a.w = [hsa.HstuLayerWeights(0x10000, 0x20000, 0, 0x38000) for _ in range(2)]
+    assert a.call() == ERR_SHAPE
 
 
 def test_encode_capacity_and_slots_leave_cached_len_unchanged():

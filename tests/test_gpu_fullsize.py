@@ -39,6 +39,16 @@ def test_headline_workload_sampled_users():
     compare_users(wl, gu, gc, [int(order[0]), int(order[len(order) // 2])])
 
 
+def test_relative_bias_workload_sampled_users():
+    """The headline workload in the original HSTU form (relative position bias, no absolute
+    table): the bench's second line; the shortest and the median-length user are checked."""
+    wl = workloads.make_workload("d512_uih2k_c2k_rel")
+    gu, gc = gpu_encode(wl)
+    assert np.all(np.isfinite(gu)) and np.all(np.isfinite(gc))
+    order = np.argsort(wl.uih_lengths)
+    compare_users(wl, gu, gc, [int(order[0]), int(order[len(order) // 2])])
+
+
 def test_d256_workload_all_users():
     """D=256, 4 layers, 32 users, UIH uniform [256, 1024], 64 candidates: every user checked."""
     wl = workloads.make_workload("d256_uih1k_c64")

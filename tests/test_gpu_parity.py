@@ -61,6 +61,35 @@ def test_history_fills_the_position_table(dtype, tol):
     check(wl, gu, gc, "bf16" if dtype == "bf16" else "f64", tol, label=f"{dtype} full position table")
 
 
+@pytest.mark.parametrize("position", ["relative", "both"])
+@pytest.mark.parametrize("D,H", [(256, 4), (512, 4)])
+def test_bf16_relative_bias(D, H, position):
+    """The original HSTU form: a relative position bias on every attention weight (alone,
+    and with the absolute table), dh = 64 and 128, the ragged lengths of the other tests."""
+    wl = workloads.make_custom(seed=900 + D + H, dtype="bf16", layers=2, d_model=D, heads=H, max_len=400,
+                               uih_lengths=[0, 1, 127, 129, 300], cand_lengths=[1, 0, 130, 5, 64],
+                               position=position, rel_std=0.3)
+    gu, gc = gpu_encode(wl)
+    check(wl, gu, gc, "bf16", BF16_TOL, label=f"bf16 {position} bias D={D} H={H}")
+
+
+@pytest.mark.parametrize("D,H", [(64, 2), (128, 2)])
+def test_f32_relative_bias(D, H):
+    wl = workloads.make_custom(seed=950 + D, dtype="f32", layers=2, d_model=D, heads=H, max_len=300,
+                               uih_lengths=[0, 1, 63, 65, 200], cand_lengths=[3, 0, 64, 1, 70],
+                               position="relative", rel_std=0.3)
+    gu, gc = gpu_encode(wl)
+    check(wl, gu, gc, "f64", F32_TOL, label=f"f32 relative bias D={D} H={H}")
+
+
+def test_bf16_relative_bias_long_table():
+    """One long history: the staged relative table spans several thousand positions."""
+    wl = workloads.make_custom(seed=977, dtype="bf16", layers=1, d_model=256, heads=4, max_len=7600,
+                               uih_lengths=[4500], cand_lengths=[2], position="relative", rel_std=0.3)
+    gu, gc = gpu_encode(wl)
+    check(wl, gu, gc, "bf16", BF16_TOL, label="bf16 relative bias, 4500 history rows")
+
+
 def test_bf16_single_layer_many_tiles():
     """One layer, long rows: attention work items of up to 16 key blocks per query tile."""
     wl = workloads.make_custom(seed=301, dtype="bf16", layers=1, d_model=256, heads=2, max_len=1100,
@@ -69,8 +98,9 @@ def test_bf16_single_layer_many_tiles():
     check(wl, gu, gc, "bf16", BF16_TOL, label="bf16 long rows")
 
 
+@pytest.mark.parametrize("position", ["absolute", "both"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_streaming_cache(dtype):
+def test_streaming_cache(dtype, position):
     """Fill each user's cache slot with its prefix (no candidates), then encode the new events
     plus candidates against the cache; compare with the oracle doing the same, and with the
     GPU's own one-shot encode of prefix + new events. The cached keys are exactly the
@@ -82,7 +112,7 @@ def test_streaming_cache(dtype):
     D, H, L = (256, 2, 2) if dtype == "bf16" else (128, 2, 2)
     wl = workloads.make_custom(seed=401, dtype=dtype, layers=L, d_model=D, heads=H, max_len=500,
                                uih_lengths=[40, 0, 130, 7], cand_lengths=[9, 3, 65, 0],
-                               cached_lengths=[200, 17, 129, 0])
+                               cached_lengths=[200, 17, 129, 0], position=position, rel_std=0.3)
     B = wl.users
     model = make_model(torch, wl)
     cache = hsa.KVCache(model, slots=6, capacity=384)

@@ -62,8 +62,9 @@ WORKLOADS: Dict[str, WorkloadSpec] = {
                      512, 4, 4097),
         WorkloadSpec("stream_3000p300_c2k", 4, 8, "bf16", 64, ("fixed", 300), 3000, 2048, 512, 4, 3301),
         WorkloadSpec("long_uih16k_c2k", 5, 16, "bf16", 4, ("uniform", 8192, 16384), 0, 2048, 512, 8, 16385),
-        # the headline shapes in the original HSTU form: relative position bias only
-        WorkloadSpec("d512_uih2k_c2k_rel", 6, 8, "bf16", 16, ("lognormal", 2000, 0.5, 512, 4096), 0, 2048,
+        # the headline workload (same seed: same lengths and tokens) in the original HSTU
+        # form: relative position bias only
+        WorkloadSpec("d512_uih2k_c2k_rel", 3, 8, "bf16", 16, ("lognormal", 2000, 0.5, 512, 4096), 0, 2048,
                      512, 4, 4097, "relative"),
     ]
 }
