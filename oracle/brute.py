@@ -141,3 +141,23 @@ def encode_brute(uih, uih_offsets, cand, cand_offsets, params, *, heads: int, ma
         for i, r in enumerate(xs_c):
             cand_out[cand_offsets[b] + i] = r
     return uih_out, cand_out
+
+
+def pack_brute(context, action, event_offsets, mode: str, *, bf16: bool):
+    """History tokens from per-event context and action embeddings (lists of D-lists),
+    one user and one event at a time: "interleave" emits the event's context token and
+    then its action token; "sum" emits one token, their element-wise sum (rounded to
+    bfloat16 when ``bf16``). Returns (tokens, token offsets)."""
+    rnd = bf16_round if bf16 else (lambda v: v)
+    tokens, offsets = [], [0]
+    for b in range(len(event_offsets) - 1):
+        for e in range(event_offsets[b], event_offsets[b + 1]):
+            if mode == "interleave":
+                tokens.append(list(context[e]))
+                tokens.append(list(action[e]))
+            elif mode == "sum":
+                tokens.append([rnd(x + y) for x, y in zip(context[e], action[e])])
+            else:
+                raise ValueError(mode)
+        offsets.append(len(tokens))
+    return tokens, offsets

@@ -23,6 +23,11 @@ with a relative position bias. Layers may carry that bias too (``rel``, one valu
 head and relative position pos_i - pos_j, added to each attention weight after the
 SiLU, as the page writes it), and may omit the absolute table (``pos`` None).
 
+The same section's action-embedding paragraph describes the input forms: the original
+HSTU weaves each event's context features and its action into the sequence as two
+tokens, doubling the sequence length, while DLRMv3 merges the two embeddings of an
+event into one token. ``pack_uih`` builds either form from per-event embeddings.
+
 Readings adopted where the pages are silent (each listed in the design notes):
 the 3*D*D GEMM consumes [U | O | U*O]; the residual is X + Z; each layer
 normalises its input rows (zero mean, unit variance over D, eps 1e-6, no learned
@@ -55,7 +60,7 @@ from typing import Dict, List, Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = ["round_bf16", "silu", "normalize_rows", "NORM_EPS", "jagged_offsets", "MacCounter", "OracleCache",
-           "encode", "layer_user", "attention_user", "user_positions", "count_macs"]
+           "encode", "layer_user", "attention_user", "user_positions", "count_macs", "pack_uih"]
 
 _BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
 _BF16_MIN_QUANTUM_EXP = -133          # smallest bfloat16 subnormal is 2**-133
@@ -323,6 +328,45 @@ def encode(uih, uih_offsets, cand, cand_offsets, params, *, heads: int, max_len:
         uih_out[uih_offsets[b]:uih_offsets[b + 1]] = xu
         cand_out[cand_offsets[b]:cand_offsets[b + 1]] = xc
     return uih_out, cand_out, new_cache
+
+
+def pack_uih(context, action, event_offsets, mode: str, *, bf16: bool = False):
+    """The encoder's history tokens from per-event context and action embeddings.
+
+    The DLRMv3 page (section "Model selection", action-embedding preprocessing): the
+    original HSTU interleaves context features and user actions in the input sequence,
+    which doubles its length; DLRMv3 merges an event's action and context embeddings
+    into one token instead. Readings: ``"interleave"`` gives user b the tokens
+    c_0, a_0, c_1, a_1, ... (an event's context token, then its action token);
+    ``"sum"`` merges by addition, c_i + a_i (rounded to bfloat16 when ``bf16``).
+
+    context, action: [E, D] in the jagged order of ``event_offsets`` [B+1].
+    Returns (tokens [rows, D] float64, token offsets [B+1] int64).
+    """
+    if mode not in ("sum", "interleave"):
+        raise ValueError(mode)
+    context = np.asarray(context, dtype=np.float64)
+    action = np.asarray(action, dtype=np.float64)
+    if context.shape != action.shape:
+        raise ValueError("context and action shapes differ")
+    D = context.shape[1]
+    B = len(event_offsets) - 1
+    parts, lengths = [], []
+    for b in range(B):
+        c = context[event_offsets[b]:event_offsets[b + 1]]
+        a = action[event_offsets[b]:event_offsets[b + 1]]
+        if mode == "sum":
+            t = c + a
+            if bf16:
+                t = round_bf16(t)
+        else:
+            t = np.empty((2 * c.shape[0], D))
+            t[0::2] = c
+            t[1::2] = a
+        parts.append(t)
+        lengths.append(t.shape[0])
+    tokens = np.concatenate(parts, axis=0) if parts else np.zeros((0, D))
+    return tokens, jagged_offsets(lengths)
 
 
 def count_macs(D: int, layers: int, n: int, c: int, m: int) -> Dict[str, int]:

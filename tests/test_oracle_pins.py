@@ -483,6 +483,146 @@ def test_streaming_equals_full_recompute(mode):
     assert after.cached_len.tolist() == full_len.tolist()
 
 
+# --------------------------------------------------------------------------- action/context packing
+
+def test_pack_sum_closed_forms():
+    """Pin (merging an event's two embeddings into one token): integer sums are exact; in
+    bfloat16 the sum is rounded once, ties to even (1 + 2^-8 lies halfway between 1 and
+    1 + 2^-7 and goes to 1; 1 + 3*2^-8 lies halfway between 1 + 2^-7 and 1 + 2^-6 and goes to
+    the even 1 + 2^-6)."""
+    c = np.array([[1.0, -3.0, 2.0, 0.0], [1.0, 1.0, 5.0, -7.0]])
+    a = np.array([[2.0, 3.0, -0.5, 0.0], [2.0 ** -8, 3 * 2.0 ** -8, 0.25, 7.0]])
+    t, off = oracle.pack_uih(c, a, [0, 2], "sum")
+    assert off.tolist() == [0, 2]
+    assert t.tolist() == [[3.0, 0.0, 1.5, 0.0], [1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 5.25, 0.0]]
+    tb, _ = oracle.pack_uih(c, a, [0, 2], "sum", bf16=True)
+    assert tb[1].tolist() == [1.0, 1.0 + 2.0 ** -6, 5.25, 0.0]
+
+
+@pytest.mark.parametrize("mode", ["sum", "interleave"])
+def test_pack_matches_brute_force(mode):
+    """Pin: the packed tokens and offsets re-derived one user and one event at a time, with
+    empty users at the front, middle and end."""
+    rng = np.random.default_rng(91)
+    lengths = [0, 3, 0, 1, 4, 0]
+    E, D = sum(lengths), 8
+    c = workloads.to_bf16_values(rng.standard_normal((E, D)).astype(np.float32)).astype(np.float64)
+    a = workloads.to_bf16_values(rng.standard_normal((E, D)).astype(np.float32)).astype(np.float64)
+    eo = workloads.lengths_to_offsets(lengths)
+    for bf16 in (False, True):
+        t, off = oracle.pack_uih(c, a, eo, mode, bf16=bf16)
+        bt, boff = brute.pack_brute(c.tolist(), a.tolist(), eo.tolist(), mode, bf16=bf16)
+        assert off.tolist() == boff
+        assert t.shape == (len(bt), D) and t.tolist() == bt
+
+
+def test_interleave_doubles_the_history():
+    """Pin (interleaving doubles the effective sequence length): every user's token count
+    is twice its event count, and its tokens alternate its own context and action rows."""
+    lengths = [2, 0, 5]
+    E, D = 7, 4
+    c = np.arange(E * D, dtype=np.float64).reshape(E, D)
+    a = -1.0 - c
+    eo = workloads.lengths_to_offsets(lengths)
+    t, off = oracle.pack_uih(c, a, eo, "interleave")
+    assert off.tolist() == [0, 4, 4, 14]
+    for b in range(3):
+        for i in range(lengths[b]):
+            e = eo[b] + i
+            assert t[off[b] + 2 * i].tolist() == c[e].tolist()
+            assert t[off[b] + 2 * i + 1].tolist() == a[e].tolist()
+
+
+def _packed(wl, mode, *, prefix=False):
+    """Tokens and token offsets of a packing workload's history (or of its cached prefix)."""
+    lengths = wl.cached_lengths if prefix else wl.uih_lengths
+    ctx, act = (wl.prefix, wl.prefix_action) if prefix else (wl.uih, wl.action)
+    return oracle.pack_uih(ctx, act, workloads.lengths_to_offsets(lengths), wl.packing,
+                           bf16=(mode == "bf16"))
+
+
+def test_interleaved_stack_matches_brute_force():
+    """Pin: interleaved tokens through the stack, re-derived end to end with scalar loops."""
+    wl = workloads.make_custom(seed=93, dtype="bf16", layers=2, d_model=4, heads=2, max_len=16,
+                               uih_lengths=[3, 0, 2], cand_lengths=[2, 1, 0], packing="interleave")
+    tok, off = _packed(wl, "bf16")
+    got_u, got_c, _ = oracle.encode(tok, off, wl.cand, workloads.lengths_to_offsets(wl.cand_lengths),
+                                    wl.params, heads=2, max_len=16, mode="bf16")
+    eo = workloads.lengths_to_offsets(wl.uih_lengths).tolist()
+    btok, boff = brute.pack_brute(wl.uih.astype(np.float64).tolist(), wl.action.astype(np.float64).tolist(),
+                                  eo, "interleave", bf16=True)
+    params = [(p.w1.astype(np.float64).tolist(), p.w2.astype(np.float64).tolist(),
+               p.pos.astype(np.float64).tolist()) for p in wl.params]
+    bu, bc = brute.encode_brute(btok, boff, wl.cand.astype(np.float64).tolist(),
+                                workloads.lengths_to_offsets(wl.cand_lengths).tolist(), params,
+                                heads=2, max_len=16, bf16=True)
+    assert rel(got_u, np.array(bu)) <= 1e-12 and rel(got_c, np.array(bc)) <= 1e-12
+
+
+def test_interleaved_action_is_seen_only_after_its_context():
+    """Pin (causal mask over the interleaved sequence): changing event i's action changes
+    nothing at or before that event's context token, changes the action token and every
+    later token of the same user and all of that user's candidates, and no other user."""
+    wl = workloads.make_custom(seed=95, dtype="f32", layers=2, d_model=8, heads=2, max_len=40,
+                               uih_lengths=[6, 4], cand_lengths=[3, 2], packing="interleave")
+    co = workloads.lengths_to_offsets(wl.cand_lengths)
+    run = lambda tok, off: oracle.encode(tok, off, wl.cand, co, wl.params, heads=2, max_len=40, mode="f64")
+    tok, off = _packed(wl, "f64")
+    u0, c0, _ = run(tok, off)
+    wl.action[3] += 0.5                   # user 0, event 3: tokens 6 (context) and 7 (action)
+    tok1, off1 = _packed(wl, "f64")
+    u1, c1, _ = run(tok1, off1)
+    changed = np.any(u1 != u0, axis=1)
+    assert not changed[:7].any() and changed[7:12].all() and not changed[12:].any()
+    assert np.any(c1[:3] != c0[:3], axis=1).all() and np.array_equal(c1[3:], c0[3:])
+
+
+def test_sum_with_zero_actions_is_the_plain_stack():
+    """Pin (special case): merging zero action embeddings leaves the tokens, and so the
+    stack's outputs, exactly those of the context embeddings alone."""
+    wl = workloads.make_custom(seed=97, dtype="bf16", layers=2, d_model=8, heads=2, max_len=32,
+                               uih_lengths=[5, 0, 7], cand_lengths=[2, 3, 1], packing="sum")
+    wl.action[:] = 0.0
+    tok, off = _packed(wl, "bf16")
+    assert np.array_equal(tok, wl.uih.astype(np.float64))
+    got_u, got_c, _ = oracle.encode(tok, off, wl.cand, workloads.lengths_to_offsets(wl.cand_lengths),
+                                    wl.params, heads=2, max_len=32, mode="bf16")
+    ref_u, ref_c, _ = run_oracle(wl, "bf16")
+    assert np.array_equal(got_u, ref_u) and np.array_equal(got_c, ref_c)
+
+
+@pytest.mark.parametrize("packing", ["sum", "interleave"])
+def test_packed_streaming_equals_one_shot(packing):
+    """Pin: packing a cached prefix's events, then the new events, and encoding them with the
+    cache gives the new tokens and candidates of packing and encoding all events at once."""
+    wl = workloads.make_custom(seed=99, dtype="bf16", layers=2, d_model=16, heads=2, max_len=64,
+                               uih_lengths=[4, 3], cand_lengths=[3, 2], cached_lengths=[5, 0],
+                               packing=packing)
+    B, L, D, cap = 2, 2, 16, 40
+    f = 2 if packing == "interleave" else 1
+    co = workloads.lengths_to_offsets(wl.cand_lengths)
+    cache = OracleCache(np.zeros((L, B, cap, D)), np.zeros((L, B, cap, D)), np.array([1, 0]),
+                        np.zeros(B, dtype=np.int64))
+    ptok, poff = _packed(wl, "bf16", prefix=True)
+    _, _, filled = oracle.encode(ptok, poff, np.zeros((0, D)), np.zeros(B + 1, np.int64), wl.params,
+                                 heads=2, max_len=64, mode="bf16", cache=cache)
+    assert filled.cached_len.tolist() == [5 * f, 0]
+    tok, off = _packed(wl, "bf16")
+    u_s, c_s, _ = oracle.encode(tok, off, wl.cand, co, wl.params, heads=2, max_len=64, mode="bf16",
+                                cache=filled)
+    eo_p = workloads.lengths_to_offsets(wl.cached_lengths)
+    eo_n = workloads.lengths_to_offsets(wl.uih_lengths)
+    ctx = np.concatenate([np.concatenate([wl.prefix[eo_p[b]:eo_p[b + 1]], wl.uih[eo_n[b]:eo_n[b + 1]]])
+                          for b in range(B)])
+    act = np.concatenate([np.concatenate([wl.prefix_action[eo_p[b]:eo_p[b + 1]],
+                                          wl.action[eo_n[b]:eo_n[b + 1]]]) for b in range(B)])
+    all_len = wl.cached_lengths + wl.uih_lengths
+    ftok, foff = oracle.pack_uih(ctx, act, workloads.lengths_to_offsets(all_len), packing, bf16=True)
+    fu, fc, _ = oracle.encode(ftok, foff, wl.cand, co, wl.params, heads=2, max_len=64, mode="bf16")
+    new_rows = np.concatenate([fu[foff[b] + f * wl.cached_lengths[b]:foff[b + 1]] for b in range(B)])
+    assert np.array_equal(u_s, new_rows) and np.array_equal(c_s, fc)
+
+
 # --------------------------------------------------------------------------- FLOP counting
 
 def test_counter_matches_closed_forms_and_page_formula():

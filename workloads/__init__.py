@@ -17,11 +17,14 @@ time order. That dataset is not available here; the workloads below stand in for
   "Time/position encoding" paragraph) draw instead, or as well, a relative bias
   table R [heads, max_len] ~ N(0, std 0.02 unless stated) over pos_i - pos_j;
 * UIH lengths follow each workload's distribution; the streaming workload draws a
-  cached prefix plus newly appended events per user.
+  cached prefix plus newly appended events per user;
+* workloads with a packing step (the page's action-embedding paragraph, same
+  section) draw per history event a context embedding and an action embedding,
+  both N(0, 1); the encoder's tokens are made from them by that step.
 
 Values are drawn in float32 from ``numpy.random.Generator(PCG64(seed))`` in a fixed
-order (lengths; per user UIH then candidate embeddings; per layer W1, W2, then P and/or
-R).
+order (lengths; per user UIH (context) embeddings, action embeddings when packing,
+then candidate embeddings; per layer W1, W2, then P and/or R).
 For bfloat16 workloads every drawn value is then stored once as the nearest
 bfloat16 (round to nearest even), so both sides consume identical bits.
 """
@@ -51,6 +54,9 @@ class WorkloadSpec:
     heads: int
     max_len: int          # rows of the position-bias table = UIH bound + 1 candidate slot
     position: str = "absolute"   # "absolute" (P on V, Q, K), "relative" (R on the weights) or "both"
+    packing: str = "none"        # "none": the history holds tokens; "sum" / "interleave": it holds
+                                 # per-event context and action embeddings, merged into tokens by
+                                 # the pack step (uih_dist and cached then count events)
 
 
 # The five workloads. The headline one is "d512_uih2k_c2k" (D=512, UIH ~2K, 2K candidates).
@@ -66,6 +72,10 @@ WORKLOADS: Dict[str, WorkloadSpec] = {
         # form: relative position bias only
         WorkloadSpec("d512_uih2k_c2k_rel", 3, 8, "bf16", 16, ("lognormal", 2000, 0.5, 512, 4096), 0, 2048,
                      512, 4, 4097, "relative"),
+        # the headline workload's users and event counts in the original HSTU input form:
+        # each event's context and action embeddings interleaved, two tokens per event
+        WorkloadSpec("d512_uih2k_c2k_interleaved", 3, 8, "bf16", 16, ("lognormal", 2000, 0.5, 512, 4096), 0,
+                     2048, 512, 4, 8193, "absolute", "interleave"),
     ]
 }
 
@@ -94,13 +104,16 @@ class Workload:
     d_model: int
     heads: int
     max_len: int
-    uih_lengths: np.ndarray      # [B] int64, new UIH tokens per user
+    uih_lengths: np.ndarray      # [B] int64, new UIH tokens (events, if packing) per user
     cand_lengths: np.ndarray     # [B] int64
-    cached_lengths: np.ndarray   # [B] int64, prefix tokens to be cached first (streaming)
-    prefix: np.ndarray           # [sum cached, D] float32 prefix tokens (empty if none)
-    uih: np.ndarray              # [sum uih_lengths, D] float32
+    cached_lengths: np.ndarray   # [B] int64, prefix tokens (events, if packing) to be cached first
+    prefix: np.ndarray           # [sum cached, D] float32 prefix tokens or context embeddings
+    uih: np.ndarray              # [sum uih_lengths, D] float32 tokens or context embeddings
     cand: np.ndarray             # [sum cand_lengths, D] float32
     params: List[LayerParams]
+    packing: str = "none"        # "none", "sum" or "interleave" (see WorkloadSpec)
+    prefix_action: Optional[np.ndarray] = None   # [sum cached, D] action embeddings (packing only)
+    action: Optional[np.ndarray] = None          # [sum uih_lengths, D] action embeddings (packing only)
 
     @property
     def users(self) -> int:
@@ -152,7 +165,7 @@ def _finish(spec_dtype, arrays):
 
 def make_custom(*, seed: int, dtype: str, layers: int, d_model: int, heads: int, max_len: int,
                 uih_lengths, cand_lengths, cached_lengths=None, name: str = "custom",
-                position: str = "absolute", rel_std: float = 0.02) -> Workload:
+                position: str = "absolute", rel_std: float = 0.02, packing: str = "none") -> Workload:
     """A workload with explicit lengths (tests: ragged tails, empty users, tiny shapes)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     uih_lengths = np.asarray(uih_lengths, dtype=np.int64)
@@ -161,19 +174,25 @@ def make_custom(*, seed: int, dtype: str, layers: int, d_model: int, heads: int,
     cached_lengths = (np.zeros(B, dtype=np.int64) if cached_lengths is None
                       else np.asarray(cached_lengths, dtype=np.int64))
     return _draw_rest(rng, name, dtype, layers, d_model, heads, max_len,
-                      uih_lengths, cand_lengths, cached_lengths, position, rel_std)
+                      uih_lengths, cand_lengths, cached_lengths, position, rel_std, packing)
 
 
 def _draw_rest(rng, name, dtype, layers, D, H, max_len, uih_lengths, cand_lengths, cached_lengths,
-               position="absolute", rel_std=0.02):
+               position="absolute", rel_std=0.02, packing="none"):
     if position not in ("absolute", "relative", "both"):
         raise ValueError(position)
-    prefix_parts, uih_parts, cand_parts = [], [], []
+    if packing not in ("none", "sum", "interleave"):
+        raise ValueError(packing)
+    prefix_parts, uih_parts, cand_parts, pact_parts, act_parts = [], [], [], [], []
     for b in range(uih_lengths.shape[0]):
         m, n, c = int(cached_lengths[b]), int(uih_lengths[b]), int(cand_lengths[b])
         hist = _normal(rng, (m + n, D), 1.0)        # the user's whole history, oldest first
         prefix_parts.append(hist[:m])
         uih_parts.append(hist[m:])
+        if packing != "none":                       # one action embedding per history event
+            act = _normal(rng, (m + n, D), 1.0)
+            pact_parts.append(act[:m])
+            act_parts.append(act[m:])
         cand_parts.append(_normal(rng, (c, D), 1.0))
     params = []
     for _ in range(layers):
@@ -188,9 +207,13 @@ def _draw_rest(rng, name, dtype, layers, D, H, max_len, uih_lengths, cand_length
         params.append(LayerParams(w1, w2, pos, rel))
     cat = lambda parts: (np.concatenate(parts, axis=0) if parts else np.zeros((0, D), np.float32))
     prefix, uih, cand = _finish(dtype, [cat(prefix_parts), cat(uih_parts), cat(cand_parts)])
+    prefix_action = action = None
+    if packing != "none":
+        prefix_action, action = _finish(dtype, [cat(pact_parts), cat(act_parts)])
     return Workload(name=name, dtype=dtype, layers=layers, d_model=D, heads=H, max_len=max_len,
                     uih_lengths=uih_lengths, cand_lengths=cand_lengths,
-                    cached_lengths=cached_lengths, prefix=prefix, uih=uih, cand=cand, params=params)
+                    cached_lengths=cached_lengths, prefix=prefix, uih=uih, cand=cand, params=params,
+                    packing=packing, prefix_action=prefix_action, action=action)
 
 
 def make_workload(name: str, *, users: Optional[int] = None, layers: Optional[int] = None) -> Workload:
@@ -208,4 +231,4 @@ def make_workload(name: str, *, users: Optional[int] = None, layers: Optional[in
     cands = np.full(B, spec.cands, dtype=np.int64)
     cached = np.full(B, spec.cached, dtype=np.int64)
     return _draw_rest(rng, spec.name, spec.dtype, L, spec.d_model, spec.heads, spec.max_len,
-                      lengths, cands, cached, spec.position)
+                      lengths, cands, cached, spec.position, packing=spec.packing)
