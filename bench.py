@@ -2,7 +2,9 @@
 
 One step = one hstu_encode call over the whole batch through every layer (row
 statistics, uvqk projection, target-aware SiLU attention, gated output GEMM), on
-seeded synthetic inputs already resident in HBM. The default workload is
+seeded synthetic inputs already resident in HBM; for a workload given as per-event
+context and action embeddings, the hstu_pack_uih call that makes the tokens is part
+of the step. The default workload is
 "d512_uih2k_c2k": 16 users, UIH lengths lognormal (median 2000, sigma 0.5, clipped
 to [512, 4096]), 2048 candidates per user, D=512, 4 heads, 8 layers, bfloat16.
 
@@ -37,16 +39,22 @@ KERNEL_SOURCES = {
 }
 
 
+def token_lengths(wl) -> np.ndarray:
+    """History tokens per user as the encoder sees them: a packing workload's event counts
+    become two tokens per event when interleaved and one when merged."""
+    return wl.uih_lengths.astype(np.int64) * (2 if wl.packing == "interleave" else 1)
+
+
 def kernel_flops_per_launch(wl) -> dict:
     """Algorithmic flops of one launch (one layer) of each kernel, from the lengths."""
     D = wl.d_model
-    n = wl.uih_lengths.astype(np.int64)
+    n = token_lengths(wl)
     c = wl.cand_lengths.astype(np.int64)
     m = np.zeros_like(n) if wl.cached_lengths is None else wl.cached_lengths.astype(np.int64)
     T = int((n + c).sum())
     pairs = int((n * m + n * (n + 1) // 2 + c * (m + n + 1)).sum())
     return {"uvqk": 2 * T * D * 4 * D, "attention": 4 * D * pairs, "out": 2 * T * 3 * D * D,
-            "norm": 0, "plan": 0}
+            "norm": 0, "plan": 0, "pack": 0}
 
 
 def source_hash(path: str) -> str:
@@ -84,18 +92,27 @@ def cpu_baseline(wl, min_seconds: float = 10.0):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
-    med = float(np.median(wl.uih_lengths))
-    order = sorted(range(wl.users), key=lambda b: (abs(float(wl.uih_lengths[b]) - med), b))
+    tl = token_lengths(wl)
+    med = float(np.median(tl))
+    order = sorted(range(wl.users), key=lambda b: (abs(float(tl[b]) - med), b))
     uo = workloads.lengths_to_offsets(wl.uih_lengths)
     co = workloads.lengths_to_offsets(wl.cand_lengths)
     D, L = wl.d_model, wl.layers
+    mode = "bf16" if wl.dtype == "bf16" else "f64"
     done, flops, dt = [], 0, 0.0
     for b in order:
         t0 = time.perf_counter()
-        oracle.encode(wl.uih, uo, wl.cand, co, wl.params, heads=wl.heads, max_len=wl.max_len,
-                      mode="bf16" if wl.dtype == "bf16" else "f64", users=[b])
+        if wl.packing == "none":
+            oracle.encode(wl.uih, uo, wl.cand, co, wl.params, heads=wl.heads, max_len=wl.max_len,
+                          mode=mode, users=[b])
+        else:                             # this user's events packed, then encoded on their own
+            ev = slice(int(uo[b]), int(uo[b + 1]))
+            tok, toff = oracle.pack_uih(wl.uih[ev], wl.action[ev], [0, uo[b + 1] - uo[b]], wl.packing,
+                                        bf16=(mode == "bf16"))
+            oracle.encode(tok, toff, wl.cand[co[b]:co[b + 1]], [0, co[b + 1] - co[b]], wl.params,
+                          heads=wl.heads, max_len=wl.max_len, mode=mode)
         dt += time.perf_counter() - t0
-        n, c = int(wl.uih_lengths[b]), int(wl.cand_lengths[b])
+        n, c = int(tl[b]), int(wl.cand_lengths[b])
         flops += L * (14 * (n + c) * D * D + 4 * D * (n * (n + 1) // 2 + c * (n + 1)))
         done.append(b)
         if dt >= min_seconds:
@@ -147,10 +164,16 @@ def main():
         sys.exit(1)
     model = hsa.Model(wl.params, d_model=wl.d_model, heads=wl.heads, max_len=wl.max_len,
                       dtype=wl.dtype, device=dev)
-    uih = torch.from_numpy(wl.uih).to(device=dev, dtype=torch.bfloat16)
-    cand = torch.from_numpy(wl.cand).to(device=dev, dtype=torch.bfloat16)
-    uo = workloads.lengths_to_offsets(wl.uih_lengths)
+    bf = lambda a: torch.from_numpy(a).to(device=dev, dtype=torch.bfloat16)
+    cand = bf(wl.cand)
+    eo = workloads.lengths_to_offsets(wl.uih_lengths)
+    uo = workloads.lengths_to_offsets(token_lengths(wl))
     co = workloads.lengths_to_offsets(wl.cand_lengths)
+    if wl.packing == "none":
+        uih = bf(wl.uih)
+    else:                                 # per-event context and action embeddings
+        ctx, act = bf(wl.uih), bf(wl.action)
+        uih = torch.empty((int(uo[-1]), wl.d_model), dtype=torch.bfloat16, device=dev)
     out = (torch.empty_like(uih), torch.empty_like(cand))
     ws = torch.empty(hsa.workspace_bytes(model, uo, co), dtype=torch.uint8, device=dev)
     st, alg_flops, formula_flops = hsa.hstu_flops(model.dims(), wl.users, uo, co, None)
@@ -158,6 +181,8 @@ def main():
     stream = torch.cuda.current_stream(dev).cuda_stream
 
     def step():
+        if wl.packing != "none":
+            hsa.pack_uih(model, ctx, act, eo, wl.packing, out=uih, stream=stream)
         hsa.encode(model, uih, uo, cand, co, out=out, workspace=ws, stream=stream)
 
     t_w = time.perf_counter()
@@ -205,10 +230,14 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded: lognormal UIH lengths, N(0,1) tokens, N(0,1/D) weights, "
-                "N(0,0.02) position bias)",
+                "N(0,0.02) position bias)" + ("" if wl.packing == "none" else
+                                              "; N(0,1) context and action embeddings per event"),
         "config": {"workload": args.workload, "users": wl.users, "layers": wl.layers,
                    "d_model": wl.d_model, "heads": wl.heads, "cands_per_user": int(wl.cand_lengths[0]),
-                   "uih_mean": float(wl.uih_lengths.mean()), "rows": int(wl.uih_lengths.sum() + wl.cand_lengths.sum())},
+                   "uih_mean": float(token_lengths(wl).mean()),
+                   "rows": int(token_lengths(wl).sum() + wl.cand_lengths.sum()),
+                   **({} if wl.packing == "none" else
+                      {"packing": wl.packing, "events_mean": float(wl.uih_lengths.mean())})},
         "users_per_s": round(wl.users / sec, 2),
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "formula_tflops": round(formula_flops / sec / 1e12, 3),

@@ -4,9 +4,9 @@ Argument marshalling only: PyTorch supplies device memory and the current stream
 and every step of the encoder runs in the library's HIP kernels. There is no
 fallback: if the library is missing or fails to load, every call raises.
 
-Low-level functions carry the C names (``hstu_encode``, ``hstu_workspace_size``,
-``hstu_flops``, ``hstu_abi_version``, ``hstu_status_string``). ``Model``,
-``KVCache`` and ``encode`` wrap them for torch tensors.
+Low-level functions carry the C names (``hstu_encode``, ``hstu_pack_uih``,
+``hstu_workspace_size``, ``hstu_flops``, ``hstu_abi_version``, ``hstu_status_string``).
+``Model``, ``KVCache``, ``encode`` and ``pack_uih`` wrap them for torch tensors.
 """
 from __future__ import annotations
 
@@ -18,12 +18,14 @@ import numpy as np
 
 __all__ = ["HSTU_F32", "HSTU_BF16", "HstuError", "load_library", "library_path",
            "hstu_abi_version", "hstu_status_string", "hstu_workspace_size", "hstu_flops",
-           "hstu_encode", "hstu_timing_enable", "hstu_timing_read", "KERNEL_KINDS", "Model", "KVCache", "encode", "HstuDims", "HstuLayerWeights",
+           "hstu_encode", "hstu_pack_uih", "hstu_timing_enable", "hstu_timing_read", "KERNEL_KINDS",
+           "PACK_MODES", "Model", "KVCache", "encode", "pack_uih", "HstuDims", "HstuLayerWeights",
            "HstuKvCache"]
 
 HSTU_F32, HSTU_BF16 = 0, 1
 HSTU_OK = 0
-KERNEL_KINDS = ("plan", "uvqk", "attention", "out", "norm")
+KERNEL_KINDS = ("plan", "uvqk", "attention", "out", "norm", "pack")
+PACK_MODES = {"sum": 0, "interleave": 1}
 
 
 class HstuDims(ctypes.Structure):
@@ -83,6 +85,9 @@ def load_library() -> ctypes.CDLL:
     lib.hstu_encode.argtypes = [P(HstuDims), ctypes.c_int32, i32p, i32p, ctypes.c_void_p, ctypes.c_void_p,
                                 P(HstuLayerWeights), P(HstuKvCache), ctypes.c_void_p, ctypes.c_void_p,
                                 ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.hstu_pack_uih.restype = ctypes.c_int32
+    lib.hstu_pack_uih.argtypes = [P(HstuDims), ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     _lib = lib
     return lib
 
@@ -135,6 +140,13 @@ def hstu_encode(dims: HstuDims, B: int, uih_offsets, cand_offsets, uih_ptr: int,
     return int(load_library().hstu_encode(ctypes.byref(dims), B, uo, co, uih_ptr, cand_ptr, warr,
                                           ctypes.byref(kv) if kv is not None else None,
                                           uih_out_ptr, cand_out_ptr, workspace_ptr, workspace_bytes, stream))
+
+
+def hstu_pack_uih(dims: HstuDims, events: int, mode: int, context_ptr: int, action_ptr: int,
+                  uih_ptr: int, stream: int) -> int:
+    """Raw call with integer device pointers. Returns the status."""
+    return int(load_library().hstu_pack_uih(ctypes.byref(dims), events, mode, context_ptr, action_ptr,
+                                            uih_ptr, stream))
 
 
 def hstu_timing_enable(enable: bool) -> int:
@@ -235,3 +247,28 @@ def encode(model: Model, uih, uih_offsets, cand, cand_offsets, *, cache: Optiona
     if st != HSTU_OK:
         raise HstuError(st, "hstu_encode")
     return out
+
+
+def pack_uih(model: Model, context, action, event_offsets, mode: str, *, out=None, stream=None):
+    """Run hstu_pack_uih on the current (or given) stream.
+
+    context/action: device tensors [E, D] in the model's dtype, every user's events in the
+    order of ``event_offsets`` (host [B+1]). Returns (tokens, token offsets): tokens is a
+    device tensor [E, D] ("sum") or [2E, D] ("interleave"), and the token offsets (host
+    int32 [B+1]) are the event offsets, doubled for "interleave".
+    """
+    torch = _torch()
+    if mode not in PACK_MODES:
+        raise ValueError(mode)
+    E = int(context.shape[0])
+    f = 2 if mode == "interleave" else 1
+    if out is None:
+        out = torch.empty((f * E, model.d_model), dtype=context.dtype, device=context.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(context.device).cuda_stream
+    ptr = lambda t: t.data_ptr() if t.numel() else None
+    st = hstu_pack_uih(model.dims(), E, PACK_MODES[mode], ptr(context), ptr(action), ptr(out), stream)
+    if st != HSTU_OK:
+        raise HstuError(st, "hstu_pack_uih")
+    offsets = np.asarray(event_offsets, dtype=np.int64) * f
+    return out, offsets.astype(np.int32)

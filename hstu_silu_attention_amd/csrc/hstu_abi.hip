@@ -497,4 +497,24 @@ hstu_status hstu_encode(const hstu_dims* d, int32_t B, const int32_t* uih_offset
   return HSTU_OK;
 }
 
+hstu_status hstu_pack_uih(const hstu_dims* d, int32_t events, int32_t mode, const void* context,
+                          const void* action, void* uih, void* stream) {
+  hstu_status st = check_dims(d);
+  if (st != HSTU_OK) return st;
+  if (events < 0 || (mode != HSTU_PACK_SUM && mode != HSTU_PACK_INTERLEAVE)) return HSTU_ERR_SHAPE;
+  const int64_t esize = d->dtype == HSTU_BF16 ? 2 : 4;
+  const int64_t cpr = d->d_model * esize / 16;   // D is a multiple of 64, so rows are whole chunks
+  const int64_t rows = mode == HSTU_PACK_INTERLEAVE ? 2 * (int64_t)events : events;
+  if (rows * cpr >= ((int64_t)1 << 31)) return HSTU_ERR_SHAPE;
+  if (events == 0) return HSTU_OK;
+  if (!context || !action || !uih) return HSTU_ERR_NULL;
+  if (!aligned16(context) || !aligned16(action) || !aligned16(uih)) return HSTU_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  const hstu::PackArgs pa{context, action, uih, (int32_t)(rows * cpr), (int32_t)cpr,
+                          mode == HSTU_PACK_INTERLEAVE, d->dtype == HSTU_BF16};
+  if (timed_launch(HSTU_KERNEL_PACK, s, [&] { return hstu::launch_pack(pa, s); }) != hipSuccess)
+    return HSTU_ERR_HIP;
+  return HSTU_OK;
+}
+
 }  // extern "C"

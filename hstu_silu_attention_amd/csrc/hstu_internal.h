@@ -125,7 +125,17 @@ struct OutArgs {
 // Query rows per attention work item for a dtype.
 int attn_block_rows(int dtype);
 
+// History packing: the output is `chunks` 16-byte chunks, `cpr` per row.
+struct PackArgs {
+  const void* ctx;
+  const void* act;
+  void* out;
+  int32_t chunks, cpr;
+  bool interleave, bf16;
+};
+
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+hipError_t launch_pack(const PackArgs& a, hipStream_t s);
 hipError_t launch_norm(int dtype, const NormArgs& a, hipStream_t s);
 hipError_t launch_colsum(const ColsumArgs& a, hipStream_t s);   // bfloat16 weights
 // st[row][g] of the rows [0, Nu) of x_lo and [Nu, T) of x_hi (bfloat16)

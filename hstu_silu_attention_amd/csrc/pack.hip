@@ -1,0 +1,77 @@
+// History tokens from per-event context and action embeddings (the two input forms of
+// the DLRMv3 page's action-embedding paragraph, section "Model selection").
+//
+// Both forms are pure streaming passes: every 16-byte chunk of the output is made
+// from one or two 16-byte chunks of the inputs, one thread per output chunk, so
+// consecutive lanes read and write consecutive 16 bytes of one row. The interleaved
+// form moves bytes unchanged; the merged form adds in float32 and rounds once to
+// the storage type.
+#include <hip/hip_runtime.h>
+
+#include "hstu.h"
+#include "bf16_common.h"
+#include "hstu_internal.h"
+
+namespace hstu {
+namespace {
+
+constexpr int kPackThreads = 256;
+
+// Output row r of the interleaved history is row r / 2 of the context (r even) or of
+// the action (r odd). `cpr` is the row length in 16-byte chunks.
+__global__ __launch_bounds__(kPackThreads) void pack_interleave_kernel(
+    const uint4* __restrict__ ctx, const uint4* __restrict__ act, uint4* __restrict__ out,
+    int chunks, int cpr) {
+  const int q = blockIdx.x * kPackThreads + threadIdx.x;
+  if (q >= chunks) return;
+  const int r = q / cpr, c = q - r * cpr;
+  const uint4* src = (r & 1) ? act : ctx;
+  out[q] = src[(r >> 1) * cpr + c];
+}
+
+// Two bfloat16 pairs -> their sums, each rounded once to bfloat16 (nearest even). The
+// float32 sum of two bfloat16 values is exact unless their exponents differ by more
+// than 16; then the smaller one is below half a bfloat16 unit of the larger one and
+// both roundings give the larger value.
+__device__ __forceinline__ uint32_t add_bf16x2(uint32_t x, uint32_t y) {
+  return pack2(bf2f_lo(x) + bf2f_lo(y), bf2f_hi(x) + bf2f_hi(y));
+}
+
+__global__ __launch_bounds__(kPackThreads) void pack_sum_bf16_kernel(
+    const uint4* __restrict__ ctx, const uint4* __restrict__ act, uint4* __restrict__ out,
+    int chunks) {
+  const int q = blockIdx.x * kPackThreads + threadIdx.x;
+  if (q >= chunks) return;
+  const uint4 x = ctx[q], y = act[q];
+  out[q] = make_uint4(add_bf16x2(x.x, y.x), add_bf16x2(x.y, y.y), add_bf16x2(x.z, y.z),
+                      add_bf16x2(x.w, y.w));
+}
+
+__global__ __launch_bounds__(kPackThreads) void pack_sum_f32_kernel(
+    const float4* __restrict__ ctx, const float4* __restrict__ act, float4* __restrict__ out,
+    int chunks) {
+  const int q = blockIdx.x * kPackThreads + threadIdx.x;
+  if (q >= chunks) return;
+  const float4 x = ctx[q], y = act[q];
+  out[q] = make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w);
+}
+
+}  // namespace
+
+// `chunks` counts 16-byte chunks of the output (< 2^31, checked by the caller).
+hipError_t launch_pack(const PackArgs& a, hipStream_t s) {
+  if (a.chunks == 0) return hipSuccess;
+  const int grid = (a.chunks + kPackThreads - 1) / kPackThreads;
+  if (a.interleave)
+    pack_interleave_kernel<<<grid, kPackThreads, 0, s>>>((const uint4*)a.ctx, (const uint4*)a.act,
+                                                         (uint4*)a.out, a.chunks, a.cpr);
+  else if (a.bf16)
+    pack_sum_bf16_kernel<<<grid, kPackThreads, 0, s>>>((const uint4*)a.ctx, (const uint4*)a.act,
+                                                       (uint4*)a.out, a.chunks);
+  else
+    pack_sum_f32_kernel<<<grid, kPackThreads, 0, s>>>((const float4*)a.ctx, (const float4*)a.act,
+                                                      (float4*)a.out, a.chunks);
+  return hipGetLastError();
+}
+
+}  // namespace hstu

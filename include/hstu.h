@@ -28,8 +28,10 @@
  * The new history rows' K, V (after bias) are appended to the cache.
  *
  * bfloat16 mode: storage is bfloat16, accumulation float32; results are rounded
- * to bfloat16 (nearest, ties to even) at Xn; at U,V,Q,K; at each attention weight
- * SiLU(q.k); at each attention output; at the gate U*O; and at X + Z.
+ * to bfloat16 (nearest, ties to even) at U,V,Q,K; at each attention weight SiLU(q.k)
+ * (plus the relative bias, when there is one); at each attention output; at the gate
+ * U*O; and at X + Z. The normalisation is applied to the projection's float32 product,
+ * so Xn is never rounded.
  * float32 mode: float32 storage and arithmetic throughout.
  *
  * Conventions for every entry point:
@@ -57,7 +59,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 2
+#define HSTU_ABI_VERSION 3
 
 /* Element type of every device tensor of a call. */
 enum hstu_dtype { HSTU_F32 = 0, HSTU_BF16 = 1 };
@@ -172,9 +174,33 @@ hstu_status hstu_encode(const hstu_dims* d, int32_t B, const int32_t* uih_offset
                         const hstu_layer_weights* w, hstu_kv_cache* kv, void* uih_out,
                         void* cand_out, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Measurement aid: device time of each kernel that hstu_encode launches, taken with
- * HIP events recorded on the caller's stream immediately before and after every
- * launch while timing is enabled (calls on one device at a time).
+/* History tokens from per-event context and action embeddings: the two input forms
+ * of the DLRMv3 page's action-embedding paragraph (section "Model selection"). The
+ * original HSTU weaves each event's context features and its action into the
+ * sequence as two tokens, doubling its length; DLRMv3 merges the two embeddings of
+ * an event into one token instead (read here as their sum).
+ *  events   E >= 0: rows of context and action, every user's events concatenated in
+ *           the jagged order of the history offsets
+ *  mode     HSTU_PACK_SUM: uih [E][D], row e = context[e] + action[e], added in float32
+ *             and rounded once to the dtype (nearest, ties to even)
+ *           HSTU_PACK_INTERLEAVE: uih [2E][D], rows 2e and 2e+1 = context[e] and
+ *             action[e]; user b's tokens are rows 2*o[b] .. 2*o[b+1]-1 for event offsets
+ *             o, so hstu_encode takes the offsets 2*o (and a user with m cached events
+ *             has 2m cached tokens)
+ *  context, action  device [E][D] in the dims' dtype; uih device output, which must
+ *           not overlap them. All three 16-byte aligned.
+ * Only d_model and dtype matter, but the dims are checked as for hstu_encode.
+ * Errors: HSTU_ERR_SHAPE (dims, E < 0, unknown mode, or an output of 2^31 or more
+ * 16-byte chunks), HSTU_ERR_NULL (a device pointer is NULL while E > 0),
+ * HSTU_ERR_ALIGN, HSTU_ERR_HIP (the launch failed). E = 0 launches nothing.
+ * Enqueued on `stream` like hstu_encode; the two can share a stream. */
+enum hstu_pack_mode { HSTU_PACK_SUM = 0, HSTU_PACK_INTERLEAVE = 1 };
+hstu_status hstu_pack_uih(const hstu_dims* d, int32_t events, int32_t mode, const void* context,
+                          const void* action, void* uih, void* stream);
+
+/* Measurement aid: device time of each kernel that hstu_encode and hstu_pack_uih
+ * launch, taken with HIP events recorded on the caller's stream immediately before
+ * and after every launch while timing is enabled (calls on one device at a time).
  *  hstu_timing_enable(1) discards earlier records and starts recording;
  *  hstu_timing_enable(0) stops recording (records are kept).
  *  hstu_timing_read waits for the recorded events, then writes, per kernel kind k <
@@ -189,7 +215,8 @@ enum hstu_kernel_kind {
                               /* layer's input rows; bfloat16 models run two passes  */
                               /* per call (W1 column sums, first-layer row sums) and */
                               /* normalise inside the projection                     */
-  HSTU_KERNEL_KINDS = 5
+  HSTU_KERNEL_PACK = 5,       /* hstu_pack_uih                           */
+  HSTU_KERNEL_KINDS = 6
 };
 hstu_status hstu_timing_enable(int32_t enable);
 hstu_status hstu_timing_read(double* total_ms, int64_t* launches, int32_t kinds);

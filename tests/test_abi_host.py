@@ -217,3 +217,34 @@ def test_encode_empty_batches_are_ok_without_device_work():
     assert a.call(kv=kv, ws=0, ws_bytes=0) == OK and cl.tolist() == [3, 4]
     a = FakeArgs()
     assert hsa.hstu_encode(a.d, a.B, [0, 5, 4], a.co, 1, 1, a.w, None, 1, 1, 1, 1, 0) == ERR_OFFSETS
+
+
+# --------------------------------------------------------------------------- hstu_pack_uih
+
+SUM, INTERLEAVE = 0, 1
+
+
+@pytest.mark.parametrize("args,want", [
+    ((None, 4, SUM, 16, 16, 16), ERR_NULL),                           # no dims
+    ((dims(D=192, H=3), 4, SUM, 16, 16, 16), ERR_SHAPE),              # dims checked as for encode
+    ((dims(), -1, SUM, 16, 16, 16), ERR_SHAPE),                       # negative event count
+    ((dims(), 4, 2, 16, 16, 16), ERR_SHAPE),                          # unknown mode
+    ((dims(), 0, SUM, None, None, None), OK),                         # nothing to pack: no launch
+    ((dims(), 0, INTERLEAVE, None, None, None), OK),
+    ((dims(), 4, SUM, None, 16, 16), ERR_NULL),
+    ((dims(), 4, INTERLEAVE, 16, None, 16), ERR_NULL),
+    ((dims(), 4, SUM, 16, 16, None), ERR_NULL),
+    ((dims(), 4, SUM, 24, 16, 16), ERR_ALIGN),
+    ((dims(), 4, INTERLEAVE, 16, 16, 8), ERR_ALIGN),
+    # bf16, D = 256: 32 chunks per row; 2^26 events interleave to 2^27 rows = 2^32 chunks
+    ((dims(), 1 << 26, INTERLEAVE, 16, 16, 16), ERR_SHAPE),
+    ((dims(), (1 << 26) - 1, SUM, None, 16, 16), ERR_NULL),           # 2^31 - 32 chunks: size ok
+    ((dims(), 1 << 26, SUM, None, 16, 16), ERR_SHAPE),                # 2^31 chunks
+    ((dims(), 1 << 25, INTERLEAVE, None, 16, 16), ERR_SHAPE),         # 2^26 rows = 2^31 chunks
+])
+def test_pack_validation(args, want):
+    """Every rejected case returns before anything is enqueued (no GPU here)."""
+    d, events, mode, c, a, o = args
+    lib = hsa.load_library()
+    st = lib.hstu_pack_uih(ctypes.byref(d) if d is not None else None, events, mode, c, a, o, None)
+    assert st == want

@@ -49,6 +49,35 @@ def test_relative_bias_workload_sampled_users():
     compare_users(wl, gu, gc, [int(order[0]), int(order[len(order) // 2])])
 
 
+def test_interleaved_workload_sampled_users():
+    """The headline workload's users in the original HSTU input form: each event's context
+    and action embeddings interleaved by hstu_pack_uih on the GPU (about 3.7K tokens per
+    user, up to 8192), the whole batch encoded in one call as the benchmark does; the
+    shortest and the median-length user are packed and recomputed by the oracle."""
+    torch = torch_cuda()
+    wl = workloads.make_workload("d512_uih2k_c2k_interleaved")
+    model = make_model(torch, wl)
+    eo = workloads.lengths_to_offsets(wl.uih_lengths)
+    tok, to = hsa.pack_uih(model, to_dev(torch, wl.uih, "bf16"), to_dev(torch, wl.action, "bf16"), eo,
+                           "interleave")
+    tl = np.diff(to.astype(np.int64))
+    assert tl.tolist() == (2 * wl.uih_lengths).tolist()
+    gu, gc = gpu_encode(wl, model=model, uih=tok, uih_lengths=tl)
+    assert np.all(np.isfinite(gu)) and np.all(np.isfinite(gc))
+    order = np.argsort(wl.uih_lengths)
+    users = [int(order[0]), int(order[len(order) // 2])]
+    rtok, _ = oracle.pack_uih(wl.uih, wl.action, eo, "interleave", bf16=True)
+    ru, rc, _ = oracle_encode(wl, "bf16", users=users, uih=rtok, uih_lengths=tl)
+    worst = 0.0
+    for b in users:
+        eu = normwise_per_user(select_users(gu, tl, [b]), select_users(ru, tl, [b]), [tl[b]])
+        ec = normwise_per_user(select_users(gc, wl.cand_lengths, [b]), select_users(rc, wl.cand_lengths, [b]),
+                               [wl.cand_lengths[b]])
+        say(f"  user {b} ({tl[b]} tokens, {wl.cand_lengths[b]} cand): uih {eu:.3e} cand {ec:.3e}")
+        worst = max(worst, eu, ec)
+    assert worst <= BF16_TOL
+
+
 def test_d256_workload_all_users():
     """D=256, 4 layers, 32 users, UIH uniform [256, 1024], 64 candidates: every user checked."""
     wl = workloads.make_workload("d256_uih1k_c64")
