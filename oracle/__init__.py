@@ -6,5 +6,6 @@ definition of the layer stack; ``brute`` re-derives it with scalar Python loops
 for tiny inputs.
 """
 from .hstu_oracle import (MacCounter, OracleCache, attention_user, count_macs, encode,  # noqa: F401
-                          jagged_offsets, layer_user, normalize_rows, pack_uih, round_bf16, silu,
+                          jagged_offsets, layer_user, normalize_rows, pack_uih, round_bf16, score_head,
+                          sigmoid, silu,
                           user_positions, NORM_EPS)

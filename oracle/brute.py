@@ -161,3 +161,27 @@ def pack_brute(context, action, event_offsets, mode: str, *, bf16: bool):
                 raise ValueError(mode)
         offsets.append(len(tokens))
     return tokens, offsets
+
+
+def score_brute(x, layers, *, bf16: bool):
+    """Candidate probabilities with scalar loops: per row, each layer's outputs as explicit
+    sums over its inputs plus the bias, ReLU between layers (hidden values rounded to
+    bfloat16 when ``bf16``), and the logistic function of the last layer's outputs.
+    x: list of rows; layers: list of (weight [out][in], bias [out]) nested lists."""
+    rnd = bf16_round if bf16 else (lambda v: v)
+    out = []
+    for row in x:
+        h = [float(v) for v in row]
+        for li, (w, b) in enumerate(layers):
+            z = []
+            for o in range(len(w)):
+                acc = 0.0
+                for k in range(len(h)):
+                    acc += h[k] * w[o][k]
+                z.append(acc + b[o])
+            if li == len(layers) - 1:
+                h = [1.0 / (1.0 + math.exp(-v)) if v >= 0 else math.exp(v) / (1.0 + math.exp(v)) for v in z]
+            else:
+                h = [rnd(v if v > 0.0 else 0.0) for v in z]
+        out.append(h)
+    return out

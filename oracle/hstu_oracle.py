@@ -28,6 +28,11 @@ HSTU weaves each event's context features and its action into the sequence as tw
 tokens, doubling the sequence length, while DLRMv3 merges the two embeddings of an
 event into one token. ``pack_uih`` builds either form from per-event embeddings.
 
+``score_head`` turns candidate rows into probabilities: the same section keeps a
+top-layer MLP for the final prediction, and the TorchRec tutorial page (section 1.1,
+the combination and final output) takes the probability as the sigmoid of the top
+MLP's output.
+
 Readings adopted where the pages are silent (each listed in the design notes):
 the 3*D*D GEMM consumes [U | O | U*O]; the residual is X + Z; each layer
 normalises its input rows (zero mean, unit variance over D, eps 1e-6, no learned
@@ -60,7 +65,8 @@ from typing import Dict, List, Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = ["round_bf16", "silu", "normalize_rows", "NORM_EPS", "jagged_offsets", "MacCounter", "OracleCache",
-           "encode", "layer_user", "attention_user", "user_positions", "count_macs", "pack_uih"]
+           "encode", "layer_user", "attention_user", "user_positions", "count_macs", "pack_uih",
+           "sigmoid", "score_head"]
 
 _BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
 _BF16_MIN_QUANTUM_EXP = -133          # smallest bfloat16 subnormal is 2**-133
@@ -367,6 +373,36 @@ def pack_uih(context, action, event_offsets, mode: str, *, bf16: bool = False):
         lengths.append(t.shape[0])
     tokens = np.concatenate(parts, axis=0) if parts else np.zeros((0, D))
     return tokens, jagged_offsets(lengths)
+
+
+def sigmoid(z) -> np.ndarray:
+    """The logistic function 1 / (1 + exp(-z)) in float64, evaluated as exp(z) / (1 + exp(z))
+    for negative z so that neither branch overflows."""
+    z = np.asarray(z, dtype=np.float64)
+    e = np.exp(-np.abs(z))
+    return np.where(z >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
+def score_head(x, layers, *, bf16: bool = False):
+    """Probabilities of the predicted outcomes for each candidate row.
+
+    x: [rows, D] candidate rows (the encoder's final outputs). layers: sequence of
+    (weight [out, in], bias [out]). Readings where the pages are silent: every layer is
+    affine, h W^T + b; a ReLU follows every layer but the last; the last layer's outputs
+    are one logit per outcome and each probability is the sigmoid of its logit. In
+    ``bf16`` mode the hidden activations are rounded to bfloat16 (a pipeline stores them);
+    logits and probabilities are not.
+    Returns [rows, outcomes] float64.
+    """
+    h = np.asarray(x, dtype=np.float64)
+    for i, (w, b) in enumerate(layers):
+        z = h @ np.asarray(w, dtype=np.float64).T + np.asarray(b, dtype=np.float64)
+        if i == len(layers) - 1:
+            return sigmoid(z)
+        h = np.maximum(z, 0.0)
+        if bf16:
+            h = round_bf16(h)
+    raise ValueError("the head needs at least one layer")
 
 
 def count_macs(D: int, layers: int, n: int, c: int, m: int) -> Dict[str, int]:

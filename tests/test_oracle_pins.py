@@ -623,6 +623,56 @@ def test_packed_streaming_equals_one_shot(packing):
     assert np.array_equal(u_s, new_rows) and np.array_equal(c_s, fc)
 
 
+# --------------------------------------------------------------------------- scoring head
+
+def test_sigmoid_closed_forms_and_library():
+    """Pin: sigmoid(0) = 1/2, sigmoid(ln 3) = 3/4, sigmoid(z) + sigmoid(-z) = 1, the limits
+    0 and 1 without overflow, and scipy's expit over a sweep."""
+    from scipy.special import expit
+    assert oracle.sigmoid(0.0) == 0.5
+    assert abs(oracle.sigmoid(math.log(3.0)) - 0.75) <= 1e-15
+    z = np.linspace(-40.0, 40.0, 2001)
+    assert np.max(np.abs(oracle.sigmoid(z) + oracle.sigmoid(-z) - 1.0)) <= 1e-15
+    assert np.max(np.abs(oracle.sigmoid(z) - expit(z))) <= 1e-15
+    with np.errstate(over="raise", invalid="raise"):
+        assert oracle.sigmoid(-1000.0) == 0.0 and oracle.sigmoid(1000.0) == 1.0
+
+
+def test_score_head_single_layer_is_logistic_regression():
+    """Pin (special case): one layer is a logistic regression, p = sigmoid(x . w + b); with w
+    a unit vector the probability reads one feature."""
+    x = np.array([[0.5, -2.0, 1.0], [0.0, 0.0, 0.0]])
+    w = np.array([[0.0, 1.0, 0.0], [1.0, 1.0, 1.0]])
+    b = np.array([0.0, math.log(3.0)])
+    p = oracle.score_head(x, [(w, b)])
+    assert abs(p[0, 0] - 1.0 / (1.0 + math.exp(2.0))) <= 1e-15
+    assert abs(p[0, 1] - 1.0 / (1.0 + math.exp(-(-0.5 + math.log(3.0))))) <= 1e-15
+    assert p[1, 0] == 0.5 and abs(p[1, 1] - 0.75) <= 1e-15
+
+
+def test_score_head_relu_between_layers():
+    """Pin (ReLU placement): a hidden unit with a negative pre-activation contributes nothing
+    (the output is the sigmoid of the last bias alone); a positive one passes unchanged."""
+    x = np.array([[1.0, 2.0]])
+    hidden = (np.array([[-1.0, -1.0], [1.0, 0.0]]), np.array([0.0, 0.0]))   # pre-activations -3, 1
+    last = (np.array([[5.0, 0.0]]), np.array([0.25]))
+    assert oracle.score_head(x, [hidden, last])[0, 0] == oracle.sigmoid(0.25)
+    last2 = (np.array([[0.0, 2.0]]), np.array([0.25]))
+    assert oracle.score_head(x, [hidden, last2])[0, 0] == oracle.sigmoid(2.25)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_score_head_matches_brute_force(bf16):
+    """Pin: three layers (16 -> 8 -> 4 -> 3 outcomes) re-derived with scalar loops."""
+    wl = workloads.make_custom(seed=101, dtype="bf16" if bf16 else "f32", layers=1, d_model=16, heads=2,
+                               max_len=8, uih_lengths=[0], cand_lengths=[5], head=(8, 4, 3))
+    got = oracle.score_head(wl.cand, wl.head, bf16=bf16)
+    layers = [(w.astype(np.float64).tolist(), b.astype(np.float64).tolist()) for w, b in wl.head]
+    want = brute.score_brute(wl.cand.astype(np.float64).tolist(), layers, bf16=bf16)
+    assert got.shape == (5, 3)
+    assert np.max(np.abs(got - np.array(want))) <= 1e-14
+
+
 # --------------------------------------------------------------------------- FLOP counting
 
 def test_counter_matches_closed_forms_and_page_formula():

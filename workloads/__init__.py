@@ -24,7 +24,8 @@ time order. That dataset is not available here; the workloads below stand in for
 
 Values are drawn in float32 from ``numpy.random.Generator(PCG64(seed))`` in a fixed
 order (lengths; per user UIH (context) embeddings, action embeddings when packing,
-then candidate embeddings; per layer W1, W2, then P and/or R).
+then candidate embeddings; per layer W1, W2, then P and/or R; then, for a scoring head,
+per head layer its weight [out, in] ~ N(0, var 1/in) and bias ~ N(0, std 0.1)).
 For bfloat16 workloads every drawn value is then stored once as the nearest
 bfloat16 (round to nearest even), so both sides consume identical bits.
 """
@@ -57,6 +58,7 @@ class WorkloadSpec:
     packing: str = "none"        # "none": the history holds tokens; "sum" / "interleave": it holds
                                  # per-event context and action embeddings, merged into tokens by
                                  # the pack step (uih_dist and cached then count events)
+    head: Tuple[int, ...] = ()   # scoring head: output widths of its layers (last = outcomes)
 
 
 # The five workloads. The headline one is "d512_uih2k_c2k" (D=512, UIH ~2K, 2K candidates).
@@ -76,6 +78,9 @@ WORKLOADS: Dict[str, WorkloadSpec] = {
         # each event's context and action embeddings interleaved, two tokens per event
         WorkloadSpec("d512_uih2k_c2k_interleaved", 3, 8, "bf16", 16, ("lognormal", 2000, 0.5, 512, 4096), 0,
                      2048, 512, 4, 8193, "absolute", "interleave"),
+        # the headline workload followed by a candidate scoring head D -> 512 -> 256 -> 1
+        WorkloadSpec("d512_uih2k_c2k_scored", 3, 8, "bf16", 16, ("lognormal", 2000, 0.5, 512, 4096), 0, 2048,
+                     512, 4, 4097, head=(512, 256, 1)),
     ]
 }
 
@@ -114,6 +119,8 @@ class Workload:
     packing: str = "none"        # "none", "sum" or "interleave" (see WorkloadSpec)
     prefix_action: Optional[np.ndarray] = None   # [sum cached, D] action embeddings (packing only)
     action: Optional[np.ndarray] = None          # [sum uih_lengths, D] action embeddings (packing only)
+    head: List[Tuple[np.ndarray, np.ndarray]] = dataclasses.field(default_factory=list)
+    # scoring head layers (weight [out, in], bias [out]); empty when there is none
 
     @property
     def users(self) -> int:
@@ -165,7 +172,8 @@ def _finish(spec_dtype, arrays):
 
 def make_custom(*, seed: int, dtype: str, layers: int, d_model: int, heads: int, max_len: int,
                 uih_lengths, cand_lengths, cached_lengths=None, name: str = "custom",
-                position: str = "absolute", rel_std: float = 0.02, packing: str = "none") -> Workload:
+                position: str = "absolute", rel_std: float = 0.02, packing: str = "none",
+                head: Tuple[int, ...] = ()) -> Workload:
     """A workload with explicit lengths (tests: ragged tails, empty users, tiny shapes)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     uih_lengths = np.asarray(uih_lengths, dtype=np.int64)
@@ -174,11 +182,11 @@ def make_custom(*, seed: int, dtype: str, layers: int, d_model: int, heads: int,
     cached_lengths = (np.zeros(B, dtype=np.int64) if cached_lengths is None
                       else np.asarray(cached_lengths, dtype=np.int64))
     return _draw_rest(rng, name, dtype, layers, d_model, heads, max_len,
-                      uih_lengths, cand_lengths, cached_lengths, position, rel_std, packing)
+                      uih_lengths, cand_lengths, cached_lengths, position, rel_std, packing, head)
 
 
 def _draw_rest(rng, name, dtype, layers, D, H, max_len, uih_lengths, cand_lengths, cached_lengths,
-               position="absolute", rel_std=0.02, packing="none"):
+               position="absolute", rel_std=0.02, packing="none", head=()):
     if position not in ("absolute", "relative", "both"):
         raise ValueError(position)
     if packing not in ("none", "sum", "interleave"):
@@ -207,13 +215,19 @@ def _draw_rest(rng, name, dtype, layers, D, H, max_len, uih_lengths, cand_length
         params.append(LayerParams(w1, w2, pos, rel))
     cat = lambda parts: (np.concatenate(parts, axis=0) if parts else np.zeros((0, D), np.float32))
     prefix, uih, cand = _finish(dtype, [cat(prefix_parts), cat(uih_parts), cat(cand_parts)])
+    head_params, fan_in = [], D
+    for width in head:
+        w = _normal(rng, (width, fan_in), 1.0 / math.sqrt(fan_in))
+        b = _normal(rng, (width,), 0.1)
+        head_params.append(tuple(_finish(dtype, [w, b])))
+        fan_in = width
     prefix_action = action = None
     if packing != "none":
         prefix_action, action = _finish(dtype, [cat(pact_parts), cat(act_parts)])
     return Workload(name=name, dtype=dtype, layers=layers, d_model=D, heads=H, max_len=max_len,
                     uih_lengths=uih_lengths, cand_lengths=cand_lengths,
                     cached_lengths=cached_lengths, prefix=prefix, uih=uih, cand=cand, params=params,
-                    packing=packing, prefix_action=prefix_action, action=action)
+                    packing=packing, prefix_action=prefix_action, action=action, head=head_params)
 
 
 def make_workload(name: str, *, users: Optional[int] = None, layers: Optional[int] = None) -> Workload:
@@ -231,4 +245,4 @@ def make_workload(name: str, *, users: Optional[int] = None, layers: Optional[in
     cands = np.full(B, spec.cands, dtype=np.int64)
     cached = np.full(B, spec.cached, dtype=np.int64)
     return _draw_rest(rng, spec.name, spec.dtype, L, spec.d_model, spec.heads, spec.max_len,
-                      lengths, cands, cached, spec.position, packing=spec.packing)
+                      lengths, cands, cached, spec.position, packing=spec.packing, head=spec.head)
