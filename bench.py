@@ -4,7 +4,8 @@ One step = one hstu_encode call over the whole batch through every layer (row
 statistics, uvqk projection, target-aware SiLU attention, gated output GEMM), on
 seeded synthetic inputs already resident in HBM; for a workload given as per-event
 context and action embeddings, the hstu_pack_uih call that makes the tokens is part
-of the step. The default workload is
+of the step, and for a workload with a scoring head, the hstu_score call over every
+candidate's output (its flops are added to the encoder's). The default workload is
 "d512_uih2k_c2k": 16 users, UIH lengths lognormal (median 2000, sigma 0.5, clipped
 to [512, 4096]), 2048 candidates per user, D=512, 4 heads, 8 layers, bfloat16.
 
@@ -45,6 +46,11 @@ def token_lengths(wl) -> np.ndarray:
     return wl.uih_lengths.astype(np.int64) * (2 if wl.packing == "interleave" else 1)
 
 
+def head_flops(wl) -> int:
+    """Algorithmic flops of the scoring head over every candidate (2 per multiply-add)."""
+    return 2 * int(wl.cand_lengths.sum()) * sum(int(w.shape[0]) * int(w.shape[1]) for w, _ in wl.head)
+
+
 def kernel_flops_per_launch(wl) -> dict:
     """Algorithmic flops of one launch (one layer) of each kernel, from the lengths."""
     D = wl.d_model
@@ -54,7 +60,7 @@ def kernel_flops_per_launch(wl) -> dict:
     T = int((n + c).sum())
     pairs = int((n * m + n * (n + 1) // 2 + c * (m + n + 1)).sum())
     return {"uvqk": 2 * T * D * 4 * D, "attention": 4 * D * pairs, "out": 2 * T * 3 * D * D,
-            "norm": 0, "plan": 0, "pack": 0}
+            "norm": 0, "plan": 0, "pack": 0, "score": head_flops(wl)}
 
 
 def source_hash(path: str) -> str:
@@ -103,16 +109,20 @@ def cpu_baseline(wl, min_seconds: float = 10.0):
     for b in order:
         t0 = time.perf_counter()
         if wl.packing == "none":
-            oracle.encode(wl.uih, uo, wl.cand, co, wl.params, heads=wl.heads, max_len=wl.max_len,
-                          mode=mode, users=[b])
+            _, cand_out, _ = oracle.encode(wl.uih, uo, wl.cand, co, wl.params, heads=wl.heads,
+                                           max_len=wl.max_len, mode=mode, users=[b])
+            cand_out = cand_out[co[b]:co[b + 1]]
         else:                             # this user's events packed, then encoded on their own
             ev = slice(int(uo[b]), int(uo[b + 1]))
             tok, toff = oracle.pack_uih(wl.uih[ev], wl.action[ev], [0, uo[b + 1] - uo[b]], wl.packing,
                                         bf16=(mode == "bf16"))
-            oracle.encode(tok, toff, wl.cand[co[b]:co[b + 1]], [0, co[b + 1] - co[b]], wl.params,
-                          heads=wl.heads, max_len=wl.max_len, mode=mode)
-        dt += time.perf_counter() - t0
+            _, cand_out, _ = oracle.encode(tok, toff, wl.cand[co[b]:co[b + 1]], [0, co[b + 1] - co[b]],
+                                           wl.params, heads=wl.heads, max_len=wl.max_len, mode=mode)
         n, c = int(tl[b]), int(wl.cand_lengths[b])
+        if wl.head:                       # the user's encoded candidates scored
+            oracle.score_head(cand_out, wl.head, bf16=(mode == "bf16"))
+            flops += 2 * c * sum(int(w.shape[0]) * int(w.shape[1]) for w, _ in wl.head)
+        dt += time.perf_counter() - t0
         flops += L * (14 * (n + c) * D * D + 4 * D * (n * (n + 1) // 2 + c * (n + 1)))
         done.append(b)
         if dt >= min_seconds:
@@ -178,12 +188,18 @@ def main():
     ws = torch.empty(hsa.workspace_bytes(model, uo, co), dtype=torch.uint8, device=dev)
     st, alg_flops, formula_flops = hsa.hstu_flops(model.dims(), wl.users, uo, co, None)
     assert st == 0
+    alg_flops += head_flops(wl)
     stream = torch.cuda.current_stream(dev).cuda_stream
+    if wl.head:
+        head = hsa.ScoringHead(wl.head, dtype=wl.dtype, device=dev)
+        prob = torch.empty((int(co[-1]), head.outcomes), dtype=torch.float32, device=dev)
 
     def step():
         if wl.packing != "none":
             hsa.pack_uih(model, ctx, act, eo, wl.packing, out=uih, stream=stream)
         hsa.encode(model, uih, uo, cand, co, out=out, workspace=ws, stream=stream)
+        if wl.head:
+            hsa.score(model, head, out[1], out=prob, stream=stream)
 
     t_w = time.perf_counter()
     done = 0
@@ -203,6 +219,8 @@ def main():
     st, ktimes = hsa.hstu_timing_read()
     assert st == 0
     finite = bool(torch.isfinite(out[0].float()).all().item() and torch.isfinite(out[1].float()).all().item())
+    if wl.head:
+        finite = finite and bool(((prob >= 0) & (prob <= 1)).all().item())
 
     sec = (t1 - t0) / args.steps
     tflops = alg_flops / sec / 1e12
@@ -212,9 +230,10 @@ def main():
     dominant = max(("uvqk", "attention", "out"), key=lambda k: ktimes[k][0])
     avg_s = kernels[dominant]["avg_ms"] / 1e3
     achieved = per_launch[dominant] / avg_s / 1e12
-    for k in ("uvqk", "attention", "out"):
+    for k in ("uvqk", "attention", "out", "score"):
         a_ms = kernels[k]["avg_ms"]
-        kernels[k]["tflops"] = per_launch[k] / (a_ms / 1e3) / 1e12 if a_ms else 0.0
+        if a_ms:
+            kernels[k]["tflops"] = per_launch[k] / (a_ms / 1e3) / 1e12
     traffic = read_traffic(dominant, args.workload)
     result = {
         "metric": "HSTU encoder TFLOP/s (% bf16 MFMA peak) + users/s, D=512 UIH~2K, 2K cands",
@@ -237,7 +256,8 @@ def main():
                    "uih_mean": float(token_lengths(wl).mean()),
                    "rows": int(token_lengths(wl).sum() + wl.cand_lengths.sum()),
                    **({} if wl.packing == "none" else
-                      {"packing": wl.packing, "events_mean": float(wl.uih_lengths.mean())})},
+                      {"packing": wl.packing, "events_mean": float(wl.uih_lengths.mean())}),
+                   **({"head": [int(w.shape[0]) for w, _ in wl.head]} if wl.head else {})},
         "users_per_s": round(wl.users / sec, 2),
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "formula_tflops": round(formula_flops / sec / 1e12, 3),

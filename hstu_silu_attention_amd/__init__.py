@@ -5,8 +5,9 @@ and every step of the encoder runs in the library's HIP kernels. There is no
 fallback: if the library is missing or fails to load, every call raises.
 
 Low-level functions carry the C names (``hstu_encode``, ``hstu_pack_uih``,
-``hstu_workspace_size``, ``hstu_flops``, ``hstu_abi_version``, ``hstu_status_string``).
-``Model``, ``KVCache``, ``encode`` and ``pack_uih`` wrap them for torch tensors.
+``hstu_score``, ``hstu_workspace_size``, ``hstu_flops``, ``hstu_abi_version``,
+``hstu_status_string``). ``Model``, ``KVCache``, ``ScoringHead``, ``encode``,
+``pack_uih`` and ``score`` wrap them for torch tensors.
 """
 from __future__ import annotations
 
@@ -19,12 +20,12 @@ import numpy as np
 __all__ = ["HSTU_F32", "HSTU_BF16", "HstuError", "load_library", "library_path",
            "hstu_abi_version", "hstu_status_string", "hstu_workspace_size", "hstu_flops",
            "hstu_encode", "hstu_pack_uih", "hstu_timing_enable", "hstu_timing_read", "KERNEL_KINDS",
-           "PACK_MODES", "Model", "KVCache", "encode", "pack_uih", "HstuDims", "HstuLayerWeights",
-           "HstuKvCache"]
+           "PACK_MODES", "Model", "KVCache", "ScoringHead", "encode", "pack_uih", "score", "hstu_score",
+           "HstuDims", "HstuLayerWeights", "HstuKvCache", "HstuHeadLayer"]
 
 HSTU_F32, HSTU_BF16 = 0, 1
 HSTU_OK = 0
-KERNEL_KINDS = ("plan", "uvqk", "attention", "out", "norm", "pack")
+KERNEL_KINDS = ("plan", "uvqk", "attention", "out", "norm", "pack", "score")
 PACK_MODES = {"sum": 0, "interleave": 1}
 
 
@@ -42,6 +43,10 @@ class HstuKvCache(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("slots", ctypes.c_int32),
                 ("capacity", ctypes.c_int32), ("slot_of_user", ctypes.POINTER(ctypes.c_int32)),
                 ("cached_len", ctypes.POINTER(ctypes.c_int32))]
+
+
+class HstuHeadLayer(ctypes.Structure):
+    _fields_ = [("weight", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("out_features", ctypes.c_int32)]
 
 
 class HstuError(RuntimeError):
@@ -85,6 +90,9 @@ def load_library() -> ctypes.CDLL:
     lib.hstu_encode.argtypes = [P(HstuDims), ctypes.c_int32, i32p, i32p, ctypes.c_void_p, ctypes.c_void_p,
                                 P(HstuLayerWeights), P(HstuKvCache), ctypes.c_void_p, ctypes.c_void_p,
                                 ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.hstu_score.restype = ctypes.c_int32
+    lib.hstu_score.argtypes = [P(HstuDims), ctypes.c_int32, ctypes.c_void_p, P(HstuHeadLayer), ctypes.c_int32,
+                               ctypes.c_void_p, ctypes.c_void_p]
     lib.hstu_pack_uih.restype = ctypes.c_int32
     lib.hstu_pack_uih.argtypes = [P(HstuDims), ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
@@ -147,6 +155,13 @@ def hstu_pack_uih(dims: HstuDims, events: int, mode: int, context_ptr: int, acti
     """Raw call with integer device pointers. Returns the status."""
     return int(load_library().hstu_pack_uih(ctypes.byref(dims), events, mode, context_ptr, action_ptr,
                                             uih_ptr, stream))
+
+
+def hstu_score(dims: HstuDims, rows: int, x_ptr: int, head: Sequence[HstuHeadLayer], prob_ptr: int,
+               stream: int) -> int:
+    """Raw call with integer device pointers. Returns the status."""
+    harr = (HstuHeadLayer * max(len(head), 1))(*head)
+    return int(load_library().hstu_score(ctypes.byref(dims), rows, x_ptr, harr, len(head), prob_ptr, stream))
 
 
 def hstu_timing_enable(enable: bool) -> int:
@@ -272,3 +287,32 @@ def pack_uih(model: Model, context, action, event_offsets, mode: str, *, out=Non
         raise HstuError(st, "hstu_pack_uih")
     offsets = np.asarray(event_offsets, dtype=np.int64) * f
     return out, offsets.astype(np.int32)
+
+
+class ScoringHead:
+    """Device-resident candidate scoring head: per layer (weight [out, in], bias [out]) as
+    float32 numpy arrays, stored in the model's dtype."""
+
+    def __init__(self, layers, *, dtype: str, device="cuda"):
+        torch = _torch()
+        tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device=device, dtype=tdt)
+        self.tensors = [(dev(w), dev(b)) for w, b in layers]
+        self.layers = [HstuHeadLayer(w.data_ptr(), b.data_ptr(), int(w.shape[0])) for w, b in self.tensors]
+        self.outcomes = int(self.tensors[-1][0].shape[0]) if self.tensors else 0
+
+
+def score(model: Model, head: ScoringHead, x, *, out=None, stream=None):
+    """Run hstu_score on candidate rows x (device [rows, D] in the model's dtype) on the current
+    (or given) stream; returns the float32 probabilities [rows, outcomes]."""
+    torch = _torch()
+    rows = int(x.shape[0])
+    if out is None:
+        out = torch.empty((rows, head.outcomes), dtype=torch.float32, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    ptr = lambda t: t.data_ptr() if t.numel() else None
+    st = hstu_score(model.dims(), rows, ptr(x), head.layers, ptr(out), stream)
+    if st != HSTU_OK:
+        raise HstuError(st, "hstu_score")
+    return out

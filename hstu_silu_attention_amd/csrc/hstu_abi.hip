@@ -517,4 +517,42 @@ hstu_status hstu_pack_uih(const hstu_dims* d, int32_t events, int32_t mode, cons
   return HSTU_OK;
 }
 
+hstu_status hstu_score(const hstu_dims* d, int32_t rows, const void* x, const hstu_head_layer* head,
+                       int32_t head_layers, float* prob, void* stream) {
+  hstu_status st = check_dims(d);
+  if (st != HSTU_OK) return st;
+  if (!head) return HSTU_ERR_NULL;
+  if (head_layers < 1 || head_layers > hstu::kMaxHeadLayers || rows < 0) return HSTU_ERR_SHAPE;
+  if (d->d_model > hstu::kMaxHeadWidth) return HSTU_ERR_SHAPE;
+  for (int32_t l = 0; l + 1 < head_layers; ++l) {
+    const int32_t n = head[l].out_features;
+    if (n < 128 || n > hstu::kMaxHeadWidth || n % 128) return HSTU_ERR_SHAPE;
+  }
+  const int32_t outcomes = head[head_layers - 1].out_features;
+  if (outcomes < 1 || outcomes > hstu::kMaxOutcomes) return HSTU_ERR_SHAPE;
+  if (rows == 0) return HSTU_OK;
+  if (!x || !prob) return HSTU_ERR_NULL;
+  for (int32_t l = 0; l < head_layers; ++l)
+    if (!head[l].weight || !head[l].bias) return HSTU_ERR_NULL;
+  if (!aligned16(x) || !aligned16(prob)) return HSTU_ERR_ALIGN;
+  for (int32_t l = 0; l < head_layers; ++l)
+    if (!aligned16(head[l].weight) || !aligned16(head[l].bias)) return HSTU_ERR_ALIGN;
+  hstu::ScoreArgs sa{};
+  sa.x = x;
+  sa.prob = prob;
+  sa.rows = rows;
+  sa.D = d->d_model;
+  sa.layers = head_layers;
+  sa.outcomes = outcomes;
+  for (int32_t l = 0; l < head_layers; ++l) {
+    sa.w[l] = head[l].weight;
+    sa.b[l] = head[l].bias;
+    sa.width[l] = head[l].out_features;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  if (timed_launch(HSTU_KERNEL_SCORE, s, [&] { return hstu::launch_score(d->dtype, sa, s); }) != hipSuccess)
+    return HSTU_ERR_HIP;
+  return HSTU_OK;
+}
+
 }  // extern "C"

@@ -134,8 +134,21 @@ struct PackArgs {
   bool interleave, bf16;
 };
 
+// Candidate scoring head: `layers` affine layers over [rows][D] candidate rows, ReLU
+// between them; the last has `outcomes` outputs, each passed through the sigmoid.
+constexpr int kMaxHeadLayers = 8, kMaxHeadWidth = 512, kMaxOutcomes = 16;
+struct ScoreArgs {
+  const void* x;
+  float* prob;
+  int32_t rows, D, layers, outcomes;
+  const void* w[kMaxHeadLayers];      // [width][in] row-major
+  const void* b[kMaxHeadLayers];      // [width]
+  int32_t width[kMaxHeadLayers];      // output features of each layer (the last: outcomes)
+};
+
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_pack(const PackArgs& a, hipStream_t s);
+hipError_t launch_score(int dtype, const ScoreArgs& a, hipStream_t s);
 hipError_t launch_norm(int dtype, const NormArgs& a, hipStream_t s);
 hipError_t launch_colsum(const ColsumArgs& a, hipStream_t s);   // bfloat16 weights
 // st[row][g] of the rows [0, Nu) of x_lo and [Nu, T) of x_hi (bfloat16)

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 3
+#define HSTU_ABI_VERSION 4
 
 /* Element type of every device tensor of a call. */
 enum hstu_dtype { HSTU_F32 = 0, HSTU_BF16 = 1 };
@@ -198,9 +198,37 @@ enum hstu_pack_mode { HSTU_PACK_SUM = 0, HSTU_PACK_INTERLEAVE = 1 };
 hstu_status hstu_pack_uih(const hstu_dims* d, int32_t events, int32_t mode, const void* context,
                           const void* action, void* uih, void* stream);
 
-/* Measurement aid: device time of each kernel that hstu_encode and hstu_pack_uih
- * launch, taken with HIP events recorded on the caller's stream immediately before
- * and after every launch while timing is enabled (calls on one device at a time).
+/* Candidate scoring head: the probability of each predicted outcome for every
+ * candidate row. The DLRMv3 page keeps a top-layer MLP for the final prediction
+ * (section "Model selection"); the TorchRec tutorial page (section 1.1, the final
+ * output) takes the probability as the sigmoid of the top MLP's output.
+ *  x        device [rows][D] in the dims' dtype: candidate rows, e.g. hstu_encode's
+ *           cand_out
+ *  head     host array of head_layers (1..8) layers; layer l maps its input h (width
+ *           D for l = 0, else layer l-1's out_features) to h W^T + b, followed by
+ *           ReLU on every layer but the last:
+ *             weight  device [out_features][in] row-major, in the dtype
+ *             bias    device [out_features], in the dtype
+ *           hidden out_features: multiples of 128 in [128, 512]; the last layer's
+ *           out_features (the outcomes): 1..16; D <= 512
+ *  prob     device float32 [rows][outcomes]: sigmoid of the last layer's outputs
+ * bfloat16: products accumulate in float32; hidden activations are rounded to
+ * bfloat16 (nearest even) after ReLU; logits and probabilities are not rounded.
+ * float32: float32 throughout. All device pointers 16-byte aligned.
+ * Errors: HSTU_ERR_SHAPE (dims, widths, layer count, rows < 0), HSTU_ERR_NULL,
+ * HSTU_ERR_ALIGN, HSTU_ERR_HIP. rows = 0 launches nothing. Enqueued on `stream`. */
+typedef struct hstu_head_layer {
+  const void* weight;
+  const void* bias;
+  int32_t out_features;
+} hstu_head_layer;
+hstu_status hstu_score(const hstu_dims* d, int32_t rows, const void* x, const hstu_head_layer* head,
+                       int32_t head_layers, float* prob, void* stream);
+
+/* Measurement aid: device time of each kernel that hstu_encode, hstu_pack_uih and
+ * hstu_score launch, taken with HIP events recorded on the caller's stream
+ * immediately before and after every launch while timing is enabled (calls on one
+ * device at a time).
  *  hstu_timing_enable(1) discards earlier records and starts recording;
  *  hstu_timing_enable(0) stops recording (records are kept).
  *  hstu_timing_read waits for the recorded events, then writes, per kernel kind k <
@@ -216,7 +244,8 @@ enum hstu_kernel_kind {
                               /* per call (W1 column sums, first-layer row sums) and */
                               /* normalise inside the projection                     */
   HSTU_KERNEL_PACK = 5,       /* hstu_pack_uih                           */
-  HSTU_KERNEL_KINDS = 6
+  HSTU_KERNEL_SCORE = 6,      /* hstu_score                              */
+  HSTU_KERNEL_KINDS = 7
 };
 hstu_status hstu_timing_enable(int32_t enable);
 hstu_status hstu_timing_read(double* total_ms, int64_t* launches, int32_t kinds);

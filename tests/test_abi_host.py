@@ -248,3 +248,47 @@ def test_pack_validation(args, want):
     lib = hsa.load_library()
     st = lib.hstu_pack_uih(ctypes.byref(d) if d is not None else None, events, mode, c, a, o, None)
     assert st == want
+
+
+# --------------------------------------------------------------------------- hstu_score
+
+def _head(widths, ptr=16):
+    arr = (hsa.HstuHeadLayer * max(len(widths), 1))()
+    for i, w in enumerate(widths):
+        arr[i] = hsa.HstuHeadLayer(ptr, ptr, w)
+    return arr
+
+
+@pytest.mark.parametrize("d,rows,widths,x,prob,want", [
+    (None, 4, [1], 16, 16, ERR_NULL),
+    (dims(D=192, H=3), 4, [1], 16, 16, ERR_SHAPE),                 # dims checked as for encode
+    (dims(D=640, H=5), 4, [1], 16, 16, ERR_SHAPE),                 # input wider than 512
+    (dims(), -1, [1], 16, 16, ERR_SHAPE),
+    (dims(), 4, [], 16, 16, ERR_SHAPE),                            # no layer
+    (dims(), 4, [128] * 8 + [1], 16, 16, ERR_SHAPE),               # more than 8 layers
+    (dims(), 4, [100, 1], 16, 16, ERR_SHAPE),                      # hidden width not a multiple of 128
+    (dims(), 4, [640, 1], 16, 16, ERR_SHAPE),                      # hidden width above 512
+    (dims(), 4, [512, 0], 16, 16, ERR_SHAPE),                      # no outcome
+    (dims(), 4, [512, 17], 16, 16, ERR_SHAPE),                     # more than 16 outcomes
+    (dims(), 0, [512, 256, 1], None, None, OK),                    # nothing to score: no launch
+    (dims(), 4, [512, 256, 1], None, 16, ERR_NULL),
+    (dims(), 4, [512, 256, 1], 16, None, ERR_NULL),
+    (dims(), 4, [512, 256, 1], 8, 16, ERR_ALIGN),
+    (dims(), 4, [512, 256, 1], 16, 4, ERR_ALIGN),
+])
+def test_score_validation(d, rows, widths, x, prob, want):
+    """Every rejected case returns before anything is enqueued (no GPU here)."""
+    lib = hsa.load_library()
+    head = _head(widths)
+    st = lib.hstu_score(ctypes.byref(d) if d is not None else None, rows, x, head, len(widths), prob, None)
+    assert st == want
+
+
+def test_score_validation_layer_pointers():
+    lib = hsa.load_library()
+    head = _head([512, 1])
+    head[1] = hsa.HstuHeadLayer(16, None, 1)
+    assert lib.hstu_score(ctypes.byref(dims()), 4, 16, head, 2, 16, None) == ERR_NULL
+    head[1] = hsa.HstuHeadLayer(24, 16, 1)
+    assert lib.hstu_score(ctypes.byref(dims()), 4, 16, head, 2, 16, None) == ERR_ALIGN
+    assert lib.hstu_score(ctypes.byref(dims()), 4, 16, None, 2, 16, None) == ERR_NULL

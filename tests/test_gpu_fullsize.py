@@ -78,6 +78,34 @@ def test_interleaved_workload_sampled_users():
     assert worst <= BF16_TOL
 
 
+def test_scored_workload():
+    """The benchmark's users with the 512-256-1 scoring head, as the benchmark launches it:
+    one hstu_score over all 32 768 candidate rows. The head alone is checked on every row
+    (the oracle's head fed with the GPU's encoder outputs, to 4e-3), and the whole
+    prediction of the shortest and the median-length user against the oracle's encoder
+    and head (to 2e-2)."""
+    torch = torch_cuda()
+    wl = workloads.make_workload("d512_uih2k_c2k_scored")
+    model = make_model(torch, wl)
+    _, dc = gpu_encode(wl, model=model, keep_device=True)
+    head = hsa.ScoringHead(wl.head, dtype="bf16")
+    prob = hsa.score(model, head, dc)
+    torch.cuda.synchronize()
+    got = prob.cpu().numpy().astype(np.float64)
+    x = dc.float().cpu().numpy().astype(np.float64)
+    alone = float(np.max(np.abs(got - oracle.score_head(x, wl.head, bf16=True))))
+    say(f"  head alone, {got.shape[0]} rows: max |dp| = {alone:.3e}")
+    assert alone <= 4e-3
+    order = np.argsort(wl.uih_lengths)
+    users = [int(order[0]), int(order[len(order) // 2])]
+    _, rc, _ = oracle_encode(wl, "bf16", users=users)
+    for b in users:
+        want = oracle.score_head(select_users(rc, wl.cand_lengths, [b]), wl.head, bf16=True)
+        err = float(np.max(np.abs(select_users(got, wl.cand_lengths, [b]) - want)))
+        say(f"  user {b}: encode+score max |dp| = {err:.3e}")
+        assert err <= 2e-2
+
+
 def test_d256_workload_all_users():
     """D=256, 4 layers, 32 users, UIH uniform [256, 1024], 64 candidates: every user checked."""
     wl = workloads.make_workload("d256_uih1k_c64")
