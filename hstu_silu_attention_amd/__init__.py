@@ -21,12 +21,13 @@ __all__ = ["HSTU_F32", "HSTU_BF16", "HstuError", "load_library", "library_path",
            "hstu_abi_version", "hstu_status_string", "hstu_workspace_size", "hstu_flops",
            "hstu_encode", "hstu_pack_uih", "hstu_timing_enable", "hstu_timing_read", "KERNEL_KINDS",
            "PACK_MODES", "Model", "KVCache", "ScoringHead", "encode", "pack_uih", "score", "hstu_score",
-           "HstuDims", "HstuLayerWeights", "HstuKvCache", "HstuHeadLayer"]
+           "HstuDims", "HstuLayerWeights", "HstuKvCache", "HstuHeadLayer", "SlotPool", "POOL_STATS"]
 
 HSTU_F32, HSTU_BF16 = 0, 1
 HSTU_OK = 0
 KERNEL_KINDS = ("plan", "uvqk", "attention", "out", "norm", "pack", "score")
 PACK_MODES = {"sum": 0, "interleave": 1}
+POOL_STATS = ("hits", "rebuild_new", "rebuild_stale", "rebuild_full", "evictions")
 
 
 class HstuDims(ctypes.Structure):
@@ -90,6 +91,21 @@ def load_library() -> ctypes.CDLL:
     lib.hstu_encode.argtypes = [P(HstuDims), ctypes.c_int32, i32p, i32p, ctypes.c_void_p, ctypes.c_void_p,
                                 P(HstuLayerWeights), P(HstuKvCache), ctypes.c_void_p, ctypes.c_void_p,
                                 ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    i64p = P(ctypes.c_int64)
+    lib.hstu_pool_create.restype = ctypes.c_int32
+    lib.hstu_pool_create.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, P(ctypes.c_void_p)]
+    lib.hstu_pool_destroy.restype = None
+    lib.hstu_pool_destroy.argtypes = [ctypes.c_void_p]
+    lib.hstu_pool_assign.restype = ctypes.c_int32
+    lib.hstu_pool_assign.argtypes = [ctypes.c_void_p, ctypes.c_int32, i64p, i32p, ctypes.c_int64, i32p, i32p, i32p]
+    lib.hstu_pool_commit.restype = ctypes.c_int32
+    lib.hstu_pool_commit.argtypes = [ctypes.c_void_p, ctypes.c_int32, i64p, i32p, ctypes.c_int64]
+    lib.hstu_pool_abort.restype = ctypes.c_int32
+    lib.hstu_pool_abort.argtypes = [ctypes.c_void_p, ctypes.c_int32, i64p]
+    lib.hstu_pool_stats.restype = ctypes.c_int32
+    lib.hstu_pool_stats.argtypes = [ctypes.c_void_p, i64p, ctypes.c_int32]
+    lib.hstu_pool_lookup.restype = ctypes.c_int32
+    lib.hstu_pool_lookup.argtypes = [ctypes.c_void_p, ctypes.c_int64, i32p, i32p]
     lib.hstu_score.restype = ctypes.c_int32
     lib.hstu_score.argtypes = [P(HstuDims), ctypes.c_int32, ctypes.c_void_p, P(HstuHeadLayer), ctypes.c_int32,
                                ctypes.c_void_p, ctypes.c_void_p]
@@ -316,3 +332,72 @@ def score(model: Model, head: ScoringHead, x, *, out=None, stream=None):
     if st != HSTU_OK:
         raise HstuError(st, "hstu_score")
     return out
+
+
+class SlotPool:
+    """The library's host-side slot manager (hstu_pool_*): which cache slot each user of a
+    batch gets and whether its cached rows are extended or its history is sent again."""
+
+    def __init__(self, slots: int, capacity: int, ttl: int):
+        self._lib = load_library()
+        self._h = ctypes.c_void_p()
+        st = int(self._lib.hstu_pool_create(slots, capacity, ttl, ctypes.byref(self._h)))
+        if st != HSTU_OK:
+            raise HstuError(st, "hstu_pool_create")
+        self.slots, self.capacity, self.ttl = slots, capacity, ttl
+
+    def __del__(self):
+        if getattr(self, "_h", None) and self._h.value:
+            self._lib.hstu_pool_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    @staticmethod
+    def _i64(a):
+        arr = np.ascontiguousarray(np.asarray(a, dtype=np.int64))
+        return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+    def assign_raw(self, users, new_events, now: int):
+        """Returns (status, slot_of_user, cached_len, rebuild) as int32 arrays."""
+        B = len(users)
+        ua, up = self._i64(users)
+        na, np_ = _i32(new_events)
+        outs = [np.full(B, -7, dtype=np.int32) for _ in range(3)]
+        ptrs = [o.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) for o in outs]
+        st = int(self._lib.hstu_pool_assign(self._h, B, up if B else None, np_ if B else None, int(now), *ptrs))
+        return (st, *outs)
+
+    def assign(self, users, new_events, now: int):
+        st, slot, cached, rebuild = self.assign_raw(users, new_events, now)
+        if st != HSTU_OK:
+            raise HstuError(st, "hstu_pool_assign")
+        return slot, cached, rebuild
+
+    def commit_raw(self, users, total_len, now: int) -> int:
+        ua, up = self._i64(users)
+        ta, tp = _i32(total_len)
+        return int(self._lib.hstu_pool_commit(self._h, len(users), up, tp, int(now)))
+
+    def commit(self, users, total_len, now: int):
+        st = self.commit_raw(users, total_len, now)
+        if st != HSTU_OK:
+            raise HstuError(st, "hstu_pool_commit")
+
+    def abort(self, users):
+        ua, up = self._i64(users)
+        st = int(self._lib.hstu_pool_abort(self._h, len(users), up))
+        if st != HSTU_OK:
+            raise HstuError(st, "hstu_pool_abort")
+
+    def stats(self) -> dict:
+        out = (ctypes.c_int64 * len(POOL_STATS))()
+        st = int(self._lib.hstu_pool_stats(self._h, out, len(POOL_STATS)))
+        if st != HSTU_OK:
+            raise HstuError(st, "hstu_pool_stats")
+        return {k: int(out[i]) for i, k in enumerate(POOL_STATS)}
+
+    def lookup(self, user: int):
+        slot, n = ctypes.c_int32(0), ctypes.c_int32(0)
+        st = int(self._lib.hstu_pool_lookup(self._h, int(user), ctypes.byref(slot), ctypes.byref(n)))
+        if st != HSTU_OK:
+            raise HstuError(st, "hstu_pool_lookup")
+        return int(slot.value), int(n.value)

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 4
+#define HSTU_ABI_VERSION 5
 
 /* Element type of every device tensor of a call. */
 enum hstu_dtype { HSTU_F32 = 0, HSTU_BF16 = 1 };
@@ -224,6 +224,61 @@ typedef struct hstu_head_layer {
 } hstu_head_layer;
 hstu_status hstu_score(const hstu_dims* d, int32_t rows, const void* x, const hstu_head_layer* head,
                        int32_t head_layers, float* prob, void* stream);
+
+/* Streaming replay: a host-side manager of the cache's user slots. Requests are
+ * replayed in time order (the DLRMv3 page, section "Dataset selection") and a user's
+ * history keys/values are reused across its consecutive requests (section "Model
+ * selection"); cached state goes stale (the multi-stage sequence model page, its
+ * limitations section: invalidation and TTL design). Per request the pool decides
+ * whether the user's cached rows are extended or its history is encoded again, and
+ * which slot of an hstu_kv_cache the user gets. Host only: it launches nothing and
+ * touches no device memory.
+ *
+ * hstu_pool_create: `slots` (>= 1) user slots of `capacity` (>= 1) rows each, the
+ *   capacity of the hstu_kv_cache the pool manages (use min(capacity, max_len - 1)
+ *   so that a user's history also fits the position tables); `ttl` (>= 0): cached
+ *   rows last used more than ttl time units before a request are stale. Errors:
+ *   ERR_NULL, ERR_SHAPE, ERR_HIP (the host allocation failed).
+ * hstu_pool_assign: one batch of B (<= slots) requests from distinct users (ids >= 0)
+ *   at time `now`, user b bringing new_events[b] (0..capacity) new history rows. For
+ *   each user it writes slot_of_user[b] and cached_len[b] (ready for hstu_kv_cache)
+ *   and rebuild[b]:
+ *     0  the user's slot holds cached_len[b] fresh rows and has room for the new
+ *        events: send only the new events;
+ *     1  cached_len[b] = 0: send the user's history again (as many of its latest
+ *        events as the caller keeps, at most capacity), as new rows.
+ *   A user without a slot gets a free one, else the least recently committed slot
+ *   not held by this batch or an uncommitted one (its user is evicted). Every user
+ *   of the batch is pending until hstu_pool_commit or hstu_pool_abort; a pending
+ *   user may not be assigned again.
+ *   Errors (the pool and the output arrays unchanged): ERR_NULL, ERR_SHAPE (B < 0, an
+ *   id < 0, repeated or pending), ERR_CAPACITY (B > slots, new_events out of range,
+ *   or too few slots not held by uncommitted batches).
+ * hstu_pool_commit: after hstu_encode succeeded for the batch: user b's slot now
+ *   holds total_len[b] rows (cached_len + rows sent, <= capacity), last used at `now`.
+ *   Errors (nothing changed): ERR_SHAPE (a user not pending), ERR_CAPACITY (a length
+ *   below the cached length or above capacity).
+ * hstu_pool_abort: after a failed encode: the users' slots are freed.
+ * hstu_pool_stats: counters since creation, indexed by enum hstu_pool_stat.
+ * hstu_pool_lookup: a user's slot (-1 if none) and committed row count. */
+typedef struct hstu_slot_pool hstu_slot_pool;
+enum hstu_pool_stat {
+  HSTU_POOL_HITS = 0,            /* cached rows extended                          */
+  HSTU_POOL_REBUILD_NEW = 1,     /* user had no slot                              */
+  HSTU_POOL_REBUILD_STALE = 2,   /* cached rows older than ttl                    */
+  HSTU_POOL_REBUILD_FULL = 3,    /* no room for the new events                    */
+  HSTU_POOL_EVICTIONS = 4,       /* users whose slot was given to another user    */
+  HSTU_POOL_STATS = 5
+};
+hstu_status hstu_pool_create(int32_t slots, int32_t capacity, int64_t ttl, hstu_slot_pool** pool);
+void hstu_pool_destroy(hstu_slot_pool* pool);
+hstu_status hstu_pool_assign(hstu_slot_pool* pool, int32_t B, const int64_t* user, const int32_t* new_events,
+                             int64_t now, int32_t* slot_of_user, int32_t* cached_len, int32_t* rebuild);
+hstu_status hstu_pool_commit(hstu_slot_pool* pool, int32_t B, const int64_t* user, const int32_t* total_len,
+                             int64_t now);
+hstu_status hstu_pool_abort(hstu_slot_pool* pool, int32_t B, const int64_t* user);
+hstu_status hstu_pool_stats(const hstu_slot_pool* pool, int64_t* stats, int32_t n);
+hstu_status hstu_pool_lookup(const hstu_slot_pool* pool, int64_t user, int32_t* slot, int32_t* len);
 
 /* Measurement aid: device time of each kernel that hstu_encode, hstu_pack_uih and
  * hstu_score launch, taken with HIP events recorded on the caller's stream

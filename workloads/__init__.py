@@ -38,7 +38,7 @@ from typing import Dict, List, Optional, Tuple
 import numpy as np
 
 __all__ = ["WORKLOADS", "Workload", "LayerParams", "make_workload", "make_custom",
-           "to_bf16_values", "lengths_to_offsets"]
+           "to_bf16_values", "lengths_to_offsets", "ReplayStream", "make_replay"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -246,3 +246,48 @@ def make_workload(name: str, *, users: Optional[int] = None, layers: Optional[in
     cached = np.full(B, spec.cached, dtype=np.int64)
     return _draw_rest(rng, spec.name, spec.dtype, L, spec.d_model, spec.heads, spec.max_len,
                       lengths, cands, cached, spec.position, packing=spec.packing, head=spec.head)
+
+
+@dataclasses.dataclass
+class ReplayStream:
+    """A time-ordered request stream over many users (streaming replay).
+
+    history[u]: [events, D] the user's whole event history, oldest first; requests: list of
+    (time, user, events known at that time, candidates), in time order. A request's
+    candidate embeddings come from ``candidates(i)``, drawn on demand from their own seed.
+    """
+    model: Workload              # the encoder's parameters (its own users are empty)
+    history: Dict[int, np.ndarray]
+    requests: List[Tuple[int, int, int, int]]
+    seed: int
+    d_model: int
+
+    def candidates(self, i: int) -> np.ndarray:
+        c = self.requests[i][3]
+        rng = np.random.Generator(np.random.PCG64([self.seed, i]))
+        return to_bf16_values(_normal(rng, (c, self.d_model), 1.0))
+
+
+def make_replay(*, seed: int = 11, users: int = 192, requests: int = 2048, layers: int = 8, d_model: int = 512,
+                heads: int = 4, max_len: int = 4097, first=("lognormal", 2000, 0.5, 512, 3000),
+                new_events=(16, 128), cands: int = 2048, mean_gap: float = 1.0) -> ReplayStream:
+    """Users arrive with a lognormal history (as the benchmark workload) and come back with
+    uniformly many new events; request times have exponential gaps (mean ``mean_gap``); users
+    are drawn uniformly per request; each request has ``cands`` candidates, N(0, 1)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    model = make_custom(seed=seed + 1, dtype="bf16", layers=layers, d_model=d_model, heads=heads, max_len=max_len,
+                        uih_lengths=[0], cand_lengths=[0])
+    median, sigma, lo, hi = first[1:]
+    start = np.clip(np.rint(rng.lognormal(math.log(median), sigma, size=users)), lo, hi).astype(np.int64)
+    who = rng.integers(0, users, size=requests)
+    gaps = rng.exponential(mean_gap, size=requests)
+    seen = np.zeros(users, dtype=np.int64)
+    plan = []
+    t = 0.0
+    for r in range(requests):
+        u = int(who[r])
+        t += float(gaps[r])
+        seen[u] = start[u] if seen[u] == 0 else seen[u] + int(rng.integers(new_events[0], new_events[1] + 1))
+        plan.append((int(t), u, int(seen[u]), cands))
+    history = {u: to_bf16_values(_normal(rng, (int(seen[u]), d_model), 1.0)) for u in range(users) if seen[u] > 0}
+    return ReplayStream(model, history, plan, seed, d_model)
