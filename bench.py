@@ -11,8 +11,9 @@ to [512, 4096]), 2048 candidates per user, D=512, 4 heads, 8 layers, bfloat16.
 
 Prints one JSON line: algorithmic TFLOP/s of the whole job (``value``), users/s, the
 fraction of the bf16 MFMA peak, per-kernel device times (HIP events recorded by the
-library on the launch stream), the roofline of the dominant kernel and the CPU
-oracle timed on a bounded sample of the same workload.
+library on the launch stream around one group of kernel kinds per timed step, the
+groups in turn), the roofline of the dominant kernel and the CPU oracle timed on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -260,15 +261,24 @@ def main():
         if done >= args.warmup:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
+    # Every step is timed by the wall clock. Each step also brackets the launches of one
+    # group of kernel kinds with HIP events, the groups taken in turn: events cost device
+    # time between kernels, so timing every launch of every step would slow the step.
+    phases = [("attention",), ("uvqk",), ("out",), ("plan", "norm", "pack", "score")]
+    phase_steps = [0] * len(phases)
     hsa.hstu_timing_enable(True)
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        hsa.hstu_timing_select(phases[i % len(phases)])
+        phase_steps[i % len(phases)] += 1
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     hsa.hstu_timing_enable(False)
+    hsa.hstu_timing_select(None)
     st, ktimes = hsa.hstu_timing_read()
     assert st == 0
+    steps_of = {k: phase_steps[j] for j, ph in enumerate(phases) for k in ph}
     finite = bool(torch.isfinite(out[0].float()).all().item() and torch.isfinite(out[1].float()).all().item())
     if wl.head:
         finite = finite and bool(((prob >= 0) & (prob <= 1)).all().item())
@@ -276,9 +286,11 @@ def main():
     sec = (t1 - t0) / args.steps
     tflops = alg_flops / sec / 1e12
     per_launch = kernel_flops_per_launch(wl)
-    kernels = {k: {"avg_ms": (ms / n if n else 0.0), "launches": n, "share": ms / max(sum(v[0] for v in ktimes.values()), 1e-12)}
+    per_step = {k: (ms / steps_of[k] if steps_of.get(k) else 0.0) for k, (ms, n) in ktimes.items()}
+    kernels = {k: {"avg_ms": (ms / n if n else 0.0), "launches": n, "timed_steps": steps_of.get(k, 0),
+                   "share": per_step[k] / max(sum(per_step.values()), 1e-12)}
                for k, (ms, n) in ktimes.items()}
-    dominant = max(("uvqk", "attention", "out"), key=lambda k: ktimes[k][0])
+    dominant = max(("uvqk", "attention", "out"), key=lambda k: kernels[k]["avg_ms"])
     avg_s = kernels[dominant]["avg_ms"] / 1e3
     achieved = per_launch[dominant] / avg_s / 1e12
     for k in ("uvqk", "attention", "out", "score"):

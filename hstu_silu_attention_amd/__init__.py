@@ -19,7 +19,7 @@ import numpy as np
 
 __all__ = ["HSTU_F32", "HSTU_BF16", "HstuError", "load_library", "library_path",
            "hstu_abi_version", "hstu_status_string", "hstu_workspace_size", "hstu_flops",
-           "hstu_encode", "hstu_pack_uih", "hstu_timing_enable", "hstu_timing_read", "KERNEL_KINDS",
+           "hstu_encode", "hstu_pack_uih", "hstu_timing_enable", "hstu_timing_select", "hstu_timing_read", "KERNEL_KINDS",
            "PACK_MODES", "Model", "KVCache", "ScoringHead", "encode", "pack_uih", "score", "hstu_score",
            "HstuDims", "HstuLayerWeights", "HstuKvCache", "HstuHeadLayer", "SlotPool", "POOL_STATS"]
 
@@ -85,6 +85,8 @@ def load_library() -> ctypes.CDLL:
                                P(ctypes.c_uint64)]
     lib.hstu_timing_enable.restype = ctypes.c_int32
     lib.hstu_timing_enable.argtypes = [ctypes.c_int32]
+    lib.hstu_timing_select.restype = ctypes.c_int32
+    lib.hstu_timing_select.argtypes = [ctypes.c_uint32]
     lib.hstu_timing_read.restype = ctypes.c_int32
     lib.hstu_timing_read.argtypes = [P(ctypes.c_double), P(ctypes.c_int64), ctypes.c_int32]
     lib.hstu_encode.restype = ctypes.c_int32
@@ -182,6 +184,12 @@ def hstu_score(dims: HstuDims, rows: int, x_ptr: int, head: Sequence[HstuHeadLay
 
 def hstu_timing_enable(enable: bool) -> int:
     return int(load_library().hstu_timing_enable(1 if enable else 0))
+
+
+def hstu_timing_select(kinds=None) -> int:
+    """Time only the given kernel kinds (names from KERNEL_KINDS); None: all of them."""
+    mask = 0xFFFFFFFF if kinds is None else sum(1 << KERNEL_KINDS.index(k) for k in kinds)
+    return int(load_library().hstu_timing_select(mask))
 
 
 def hstu_timing_read():

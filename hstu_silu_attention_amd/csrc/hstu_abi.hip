@@ -146,6 +146,7 @@ hstu_status stage_and_copy(const void* src, size_t bytes, void* dst, hipStream_t
 struct Timing {
   std::mutex mu;
   bool on = false;
+  uint32_t mask = 0xffffffffu;   // kernel kinds that get events while timing is on
   struct Rec { int kind; hipEvent_t a, b; };
   std::vector<Rec> recs;
   std::vector<hipEvent_t> pool;
@@ -169,7 +170,7 @@ hipEvent_t timing_event() {
 template <typename F>
 hipError_t timed_launch(int kind, hipStream_t s, F&& f) {
   std::unique_lock<std::mutex> lock(g_timing.mu);
-  if (!g_timing.on) {
+  if (!g_timing.on || !((g_timing.mask >> kind) & 1u)) {
     lock.unlock();
     return f();
   }
@@ -204,6 +205,12 @@ hstu_status hstu_timing_enable(int32_t enable) {
     }
   }
   g_timing.on = enable != 0;
+  return HSTU_OK;
+}
+
+hstu_status hstu_timing_select(uint32_t kinds_mask) {
+  std::lock_guard<std::mutex> lock(g_timing.mu);
+  g_timing.mask = kinds_mask;
   return HSTU_OK;
 }
 

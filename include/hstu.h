@@ -286,6 +286,10 @@ hstu_status hstu_pool_lookup(const hstu_slot_pool* pool, int64_t user, int32_t* 
  * device at a time).
  *  hstu_timing_enable(1) discards earlier records and starts recording;
  *  hstu_timing_enable(0) stops recording (records are kept).
+ *  hstu_timing_select(mask) restricts the events to the kernel kinds k whose bit
+ *  (1 << k) is set (all kinds until called; kept across enable/disable). Each timed
+ *  launch adds two event records to the stream, and they cost device time between
+ *  kernels: timing a subset of kinds costs less.
  *  hstu_timing_read waits for the recorded events, then writes, per kernel kind k <
  *  kinds (enum hstu_kernel_kind), the summed milliseconds total_ms[k] and the number
  *  of launches[k] recorded since enabling; it consumes the records. */
@@ -303,6 +307,7 @@ enum hstu_kernel_kind {
   HSTU_KERNEL_KINDS = 7
 };
 hstu_status hstu_timing_enable(int32_t enable);
+hstu_status hstu_timing_select(uint32_t kinds_mask);
 hstu_status hstu_timing_read(double* total_ms, int64_t* launches, int32_t kinds);
 
 #ifdef __cplusplus

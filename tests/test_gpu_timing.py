@@ -53,3 +53,29 @@ def test_timing_counts_and_bounds(dtype):
     # a read consumes the records
     st, rec = hsa.hstu_timing_read()
     assert st == 0 and all(n == 0 and ms == 0.0 for ms, n in rec.values())
+
+
+def test_timing_select_limits_the_kinds():
+    """With a kind mask, only launches of those kinds are recorded; the mask is kept until
+    changed and None restores all kinds."""
+    torch = torch_cuda()
+    wl = _workload("bf16")
+    model = make_model(torch, wl)
+    uih = to_dev(torch, wl.uih.reshape(-1, wl.d_model), wl.dtype)
+    cand = to_dev(torch, wl.cand.reshape(-1, wl.d_model), wl.dtype)
+    try:
+        assert hsa.hstu_timing_select(("attention", "out")) == 0
+        assert hsa.hstu_timing_enable(True) == 0
+        gpu_encode(wl, model=model, uih=uih, cand=cand)
+        gpu_encode(wl, model=model, uih=uih, cand=cand)
+        assert hsa.hstu_timing_enable(False) == 0
+        st, rec = hsa.hstu_timing_read()
+        assert st == 0
+        L = wl.layers
+        assert rec["attention"][1] == 2 * L and rec["out"][1] == 2 * L
+        assert all(rec[k][1] == 0 for k in ("plan", "uvqk", "norm", "pack", "score"))
+        assert rec["attention"][0] > 0.0 and rec["out"][0] > 0.0
+    finally:
+        hsa.hstu_timing_select(None)
+        hsa.hstu_timing_enable(False)
+        hsa.hstu_timing_read()
