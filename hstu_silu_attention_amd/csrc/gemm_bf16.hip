@@ -347,16 +347,18 @@ void uvqk_kernel(UvqkArgs a) {
   const int slice = col0 / D;
   // The position-bias tile goes through the (now idle) LDS: every 32 consecutive
   // threads read one row's 256 bias values as whole lines (the row's position comes
-  // from the row table), then each lane picks up the values of its accumulators.
+  // from the row table). Each lane then reads the bias at the places of its
+  // accumulators and writes its results over them: every tile position belongs to one
+  // lane, which reads it before writing it, so no barrier is needed in between.
   constexpr int OLD = C::BN + 8;                     // LDS row stride of the staged tiles
   static_assert(C::BM * OLD <= SMEM, "a staged tile must fit the LDS stages");
   constexpr int CPR = C::BN / 8;                     // 16-byte chunks per tile row
-  uint2 bias[C::MI][C::NI][4];
   // Thread t moves the 16-byte chunk (t % CPR) of tile rows t / CPR + RSTEP_O * i.
   constexpr int RSTEP_O = C::NT / CPR;
   static_assert(C::NT % CPR == 0, "a thread keeps its chunk column");
   const int r_first = threadIdx.x / CPR, cc = (threadIdx.x % CPR) * 8;
-  if (slice > 0 && a.pos != nullptr) {
+  const bool has_bias = slice > 0 && a.pos != nullptr;   // uniform over the workgroup
+  if (has_bias) {
     // a position table has fewer than 2^31 elements (checked on the host), so a
     // position's element offset is a 24 x 24-bit product
     const u16* pos = (const u16*)a.pos + (slice - 1) * D + (col0 - slice * D) + cc;
@@ -368,23 +370,6 @@ void uvqk_kernel(UvqkArgs a) {
           *reinterpret_cast<const uint4*>(pos + __umul24((unsigned)q.y, 3u * (unsigned)D));
     }
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < C::MI; ++i) {
-      const int r = wm * C::TM + i * 32 + l32;
-#pragma unroll
-      for (int j = 0; j < C::NI; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          bias[i][j][g] = *reinterpret_cast<const uint2*>(smem + r * OLD + wn * C::TN + j * 32 + g * 8 + hi * 4);
-    }
-    __syncthreads();
-  } else {
-#pragma unroll
-    for (int i = 0; i < C::MI; ++i)
-#pragma unroll
-      for (int j = 0; j < C::NI; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) bias[i][j][g] = make_uint2(0, 0);
   }
   // The finished tile goes through the LDS too: each lane writes its rounded values
   // there, then every 32 consecutive threads store 512 contiguous bytes of one row, so
@@ -402,12 +387,13 @@ void uvqk_kernel(UvqkArgs a) {
     for (int j = 0; j < C::NI; ++j) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const float v0 = silu_n(acc[i][j][4 * g + 0], sc) + bf2f_lo(bias[i][j][g].x);
-        const float v1 = silu_n(acc[i][j][4 * g + 1], sc) + bf2f_hi(bias[i][j][g].x);
-        const float v2 = silu_n(acc[i][j][4 * g + 2], sc) + bf2f_lo(bias[i][j][g].y);
-        const float v3 = silu_n(acc[i][j][4 * g + 3], sc) + bf2f_hi(bias[i][j][g].y);
-        *reinterpret_cast<uint2*>(smem + r * OLD + wn * C::TN + j * 32 + g * 8 + hi * 4) =
-            make_uint2(pack2(v0, v1), pack2(v2, v3));
+        uint2* at = reinterpret_cast<uint2*>(smem + r * OLD + wn * C::TN + j * 32 + g * 8 + hi * 4);
+        const uint2 bias = has_bias ? *at : make_uint2(0, 0);
+        const float v0 = silu_n(acc[i][j][4 * g + 0], sc) + bf2f_lo(bias.x);
+        const float v1 = silu_n(acc[i][j][4 * g + 1], sc) + bf2f_hi(bias.x);
+        const float v2 = silu_n(acc[i][j][4 * g + 2], sc) + bf2f_lo(bias.y);
+        const float v3 = silu_n(acc[i][j][4 * g + 3], sc) + bf2f_hi(bias.y);
+        *at = make_uint2(pack2(v0, v1), pack2(v2, v3));
       }
     }
   }
