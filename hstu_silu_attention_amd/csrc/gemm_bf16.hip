@@ -515,7 +515,11 @@ long tiles_of(int T, int N) {
 hipError_t launch_uvqk_bf16(const UvqkArgs& a, hipStream_t s) {
   // A tile must lie inside one of the U, V, Q, K column blocks: D % BN == 0.
   const int N = 4 * a.D;
-  if (a.D % BigTile::BN == 0 && tiles_of<BigTile>(a.T, N) >= 256)
+  // Big tiles need whole D-wide column blocks and enough tiles that the last of the
+  // rounds of 256 (one per CU) is mostly full: 352 big tiles would run as a full round
+  // and a 38% one, where the same work in small tiles fills its rounds evenly.
+  const int tb = tiles_of<BigTile>(a.T, N), rounds = (tb + 255) / 256;
+  if (a.D % BigTile::BN == 0 && tb >= 256 && (rounds >= 4 || 4 * tb >= 3 * 256 * rounds))
     uvqk_kernel<BigTile><<<tiles_of<BigTile>(a.T, N), BigTile::NT, 0, s>>>(a);
   else
     uvqk_kernel<SmallTile><<<tiles_of<SmallTile>(a.T, N), SmallTile::NT, 0, s>>>(a);
