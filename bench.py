@@ -83,6 +83,20 @@ def kernel_bytes_per_launch(wl) -> dict:
             "out": 2 * (2 * T * D + 3 * D * D + T * D + T * D)}
 
 
+def gpu_sclk_mhz():
+    """The GPU's current shader clock from the driver's DPM table (the level marked with
+    '*'), or None where the file is not readable."""
+    import glob
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            for line in open(path):
+                if line.rstrip().endswith("*"):
+                    return int(float(line.split(":")[1].strip().rstrip("*").strip().lower().rstrip("mhz")))
+        except (OSError, ValueError, IndexError):
+            continue
+    return None
+
+
 def source_hash(path: str) -> str:
     with open(os.path.join(ROOT, path), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -313,14 +327,21 @@ def main():
     # time between kernels, so timing every launch of every step would slow the step.
     phases = [("attention",), ("uvqk",), ("out",), ("plan", "norm", "pack", "score")]
     phase_steps = [0] * len(phases)
+    # one event between consecutive steps on the launch stream gives each step's device
+    # time (median and minimum reported beside the mean)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     hsa.hstu_timing_enable(True)
     t0 = time.perf_counter()
+    marks[0].record()
     for i in range(args.steps):
         hsa.hstu_timing_select(phases[i % len(phases)])
         phase_steps[i % len(phases)] += 1
         step()
+        marks[i + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    step_ms = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
+    sclk = gpu_sclk_mhz()                 # read right after the timed steps
     hsa.hstu_timing_enable(False)
     hsa.hstu_timing_select(None)
     st, ktimes = hsa.hstu_timing_read()
@@ -366,6 +387,8 @@ def main():
         "warmup": args.warmup,
         "warmup_steps_run": done,
         "ms_per_step": round(sec * 1e3, 4),
+        "step_ms": {"median": round(float(np.median(step_ms)), 4), "min": round(float(np.min(step_ms)), 4)},
+        "sclk_mhz_after": sclk,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
