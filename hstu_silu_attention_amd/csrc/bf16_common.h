@@ -38,6 +38,19 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Sum over each group of 16 consecutive lanes, every lane of the group receiving it, by
+// DPP lane moves (no LDS round trip). Lanes pair as i ^ 1, then i ^ 2; after these every
+// lane of a quad holds the quad's sum, so the mirror within 8 (lane 7 - i) and within 16
+// (lane 15 - i) add the neighbouring quad, then the neighbouring 8: the additions group
+// the values exactly as the xor butterfly 1, 2, 4, 8 does. All 64 lanes must be active.
+__device__ __forceinline__ float sum16(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));    // quad_perm 1,0,3,2
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));    // quad_perm 2,3,0,1
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));   // row_half_mirror
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true));   // row_mirror
+  return v;
+}
+
 // Workgroup -> tile order that keeps neighbouring tiles on one XCD. Workgroups are
 // dealt to the 8 XCDs round-robin; giving each XCD a contiguous run of tiles keeps
 // tiles that share operand blocks inside one XCD's L2.

@@ -470,8 +470,8 @@ void out_kernel(OutArgs a) {
   }
   __syncthreads();
   // Also the next layer's row statistics: each 16 consecutive threads hold one row's
-  // 128-column group and add their {sum, sum of squares} in a fixed butterfly order
-  // (the same order as the first layer's row pass).
+  // 128-column group and add their {sum, sum of squares} with sum16 (the same grouping
+  // as the first layer's row pass).
   static_assert(CPR % 16 == 0, "whole 128-column groups per tile row");
 #pragma unroll
   for (int i = 0; i < C::BM * CPR / C::NT; ++i) {
@@ -487,11 +487,8 @@ void out_kernel(OutArgs a) {
         s1 += lo + hi;
         s2 = __builtin_fmaf(lo, lo, __builtin_fmaf(hi, hi, s2));
       }
-#pragma unroll
-      for (int m = 1; m < 16; m <<= 1) {
-        s1 += __shfl_xor(s1, m);
-        s2 += __shfl_xor(s2, m);
-      }
+      s1 = sum16(s1);
+      s2 = sum16(s2);
       if ((c & 15) == 0 && row < a.T) a.st[(size_t)row * (D / 128) + (col0 + cc) / 128] = make_float2(s1, s2);
     }
     if (row >= a.T) continue;

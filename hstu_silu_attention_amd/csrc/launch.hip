@@ -138,11 +138,8 @@ __global__ __launch_bounds__(256) void rowstats_kernel(const void* x_lo, const v
         s2 = __builtin_fmaf(v[2 * e], v[2 * e], __builtin_fmaf(v[2 * e + 1], v[2 * e + 1], s2));
       }
     }
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) {
-      s1 += __shfl_xor(s1, m);
-      s2 += __shfl_xor(s2, m);
-    }
+    s1 = sum16(s1);
+    s2 = sum16(s2);
     if ((lane & 15) == 0 && c < D / 8) st[(size_t)row * (D / 128) + c / 16] = make_float2(s1, s2);
   }
 }
