@@ -406,17 +406,27 @@ void uvqk_kernel(UvqkArgs a) {
                : slice == 1 ? (u16*)a.cache_v + ccol
                : slice == 3 ? (u16*)a.cache_k + ccol : nullptr;
   u16* const out0 = out + (size_t)(row0 + r_first) * 3 * D + cc;
+  // Cache rows of this thread's tile rows, looked up before the stores: all row-table
+  // reads in flight together, then all user-record reads (a lookup per store would wait
+  // for two dependent reads each time).
+  constexpr int NR = C::BM * CPR / C::NT;
+  const bool append = cache != nullptr && row0 < a.Nu;   // uniform over the workgroup
+  int crow[NR];
+  if (append) {
+    int2 q[NR];
 #pragma unroll
-  for (int i = 0; i < C::BM * CPR / C::NT; ++i) {
+    for (int i = 0; i < NR; ++i) q[i] = a.row_info[min(row0 + r_first + RSTEP_O * i, a.T - 1)];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) crow[i] = a.users[q[i].x].key_row + q[i].y;
+  }
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
     const int r = r_first + RSTEP_O * i;
     const int row = row0 + r;
     if (row >= a.T) continue;
     const uint4 v = *reinterpret_cast<const uint4*>(smem + r * OLD + cc);
     *reinterpret_cast<uint4*>(out0 + (size_t)i * RSTEP_O * 3 * D) = v;
-    if (cache != nullptr && row < a.Nu) {
-      const int2 q = a.row_info[row];
-      *reinterpret_cast<uint4*>(cache + ((size_t)a.users[q.x].key_row + q.y) * D + cc) = v;
-    }
+    if (append && row < a.Nu) *reinterpret_cast<uint4*>(cache + (size_t)crow[i] * D + cc) = v;
   }
 }
 
