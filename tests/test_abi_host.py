@@ -292,3 +292,24 @@ def test_score_validation_layer_pointers():
     head[1] = hsa.HstuHeadLayer(24, 16, 1)
     assert lib.hstu_score(ctypes.byref(dims()), 4, 16, head, 2, 16, None) == ERR_ALIGN
     assert lib.hstu_score(ctypes.byref(dims()), 4, 16, None, 2, 16, None) == ERR_NULL
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """No fallback: with the shared library absent every entry point raises instead of
+    computing anything some other way (run in a child process so this one keeps its
+    loaded library)."""
+    import subprocess
+    import sys
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "import hstu_silu_attention_amd as hsa\n"
+        "hsa.library_path = lambda: %r\n"
+        "try:\n"
+        "    hsa.hstu_abi_version()\n"
+        "except RuntimeError as e:\n"
+        "    print('raised:', e)\n"
+        "    sys.exit(0)\n"
+        "sys.exit(3)\n" % (ROOT, str(tmp_path / "absent" / "libhstu.so")))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "build the HIP library" in r.stdout
