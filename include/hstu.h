@@ -260,7 +260,9 @@ hstu_status hstu_score(const hstu_dims* d, int32_t rows, const void* x, const hs
  *   below the cached length or above capacity).
  * hstu_pool_abort: after a failed encode: the users' slots are freed.
  * hstu_pool_stats: counters since creation, indexed by enum hstu_pool_stat.
- * hstu_pool_lookup: a user's slot (-1 if none) and committed row count. */
+ * hstu_pool_lookup: a user's slot (-1 if none) and committed row count.
+ * A pool is not synchronised: calls on one pool from several threads need the
+ * caller's lock. */
 typedef struct hstu_slot_pool hstu_slot_pool;
 enum hstu_pool_stat {
   HSTU_POOL_HITS = 0,            /* cached rows extended                          */
