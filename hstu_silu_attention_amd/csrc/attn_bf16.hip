@@ -110,8 +110,11 @@ __device__ __forceinline__ float silu_bias(float x, float nlog2e, float bias) {
 constexpr int kTabPad = 64, kTabEntries = 8192;
 static_assert(kTabPad + ((kRelMaxLen + 32 + 7 + 7) / 8 + 63) / 64 * 512 <= kTabEntries, "table must fit");
 
+// dh = 64 fits three waves per SIMD (under 168 registers; 32 KB of K/V slots, 48 KB with
+// a relative table, per workgroup), which hides more of each wave's latency; dh = 128
+// needs two (233 registers, 64 KB).
 template <int DH, bool REL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DH == 64 ? 3 : 2, DH == 64 ? 3 : 2)))
 void attn_kernel(AttnArgs a) {
   using C = AttnTile<DH>;
   __shared__ __attribute__((aligned(16))) u16 ks0[C::SLOT], ks1[C::SLOT], vs0[C::SLOT], vs1[C::SLOT];
