@@ -365,6 +365,11 @@ def main():
         a_ms = kernels[k]["avg_ms"]
         if a_ms:
             kernels[k]["tflops"] = per_launch[k] / (a_ms / 1e3) / 1e12
+            # HBM rate from the committed counter summary of this kernel (when it was
+            # taken on the current source), over this run's average launch time
+            t = read_traffic(k, args.workload) if k in KERNEL_SOURCES else None
+            if t:
+                kernels[k]["hbm_gbs"] = t / (a_ms / 1e3) / 1e9
     traffic = read_traffic(dominant, args.workload)
     # the bound of the dominant kernel: its algorithmic flops per algorithmic byte against
     # the ridge point of the two peaks
