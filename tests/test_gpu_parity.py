@@ -37,11 +37,12 @@ def test_f32_ragged(D, H):
     check(wl, gu, gc, "f64", F32_TOL, label=f"f32 D={D} H={H}")
 
 
-@pytest.mark.parametrize("D,H", [(256, 4), (256, 2), (512, 8), (512, 4)])
+@pytest.mark.parametrize("D,H", [(256, 4), (256, 2), (512, 8), (512, 4), (640, 10), (768, 6), (1024, 8)])
 def test_bf16_ragged(D, H):
     """dh = 64 and 128; histories of 0, 1, 127, 129, 300 rows and candidate sets of 1, 0, 130,
     5, 64 rows cover empty users, single rows and ragged tails of 128-row query tiles and
-    64-key blocks."""
+    64-key blocks. Widths up to D = 1024, including ones whose projection column blocks are
+    not whole 256-wide tiles (640, 768)."""
     wl = workloads.make_custom(seed=200 + D + H, dtype="bf16", layers=2, d_model=D, heads=H, max_len=400,
                                uih_lengths=[0, 1, 127, 129, 300], cand_lengths=[1, 0, 130, 5, 64])
     gu, gc = gpu_encode(wl)
