@@ -25,7 +25,13 @@
  *                                        + SiLU(q_r . k_r) v_r)
  *        (per head h: the columns [h*dh, (h+1)*dh), dh = D / heads)
  *   X_{l+1} = X_l + [U | O | U*O] W2_l
- * The new history rows' K, V (after bias) are appended to the cache.
+ * The position bias P_l is optional; a layer may instead (or also) carry a relative
+ * table rel_l, and then every weight SiLU(q_i . k_j) gains rel_l[h][pos_i - pos_j]
+ * (see hstu_layer_weights). The new history rows' K, V (after bias) are appended to
+ * the cache. Entry points around the encoder: hstu_pack_uih builds the history
+ * tokens from per-event context and action embeddings, hstu_score turns candidate
+ * rows into outcome probabilities, and hstu_pool_* manage cache slots for
+ * time-ordered request replay.
  *
  * bfloat16 mode: storage is bfloat16, accumulation float32; results are rounded
  * to bfloat16 (nearest, ties to even) at U,V,Q,K; at each attention weight SiLU(q.k)
