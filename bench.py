@@ -253,7 +253,7 @@ def main():
         print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}), flush=True)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); users are "
+        print(f"bench.py: the benchmark runs on one GPU only (asked for --gpus {args.gpus}); users are "
               f"independent, so N GPUs would each run this one-GPU workload on their own users.",
               file=sys.stderr)
         sys.exit(2)
