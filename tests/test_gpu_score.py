@@ -91,3 +91,44 @@ def test_encode_then_score():
     err = float(np.max(np.abs(got - want)))
     say(f"  encode+score max |dp| = {err:.3e} (tol {END_TO_END_TOL})")
     assert err <= END_TO_END_TOL
+
+
+def test_everything_together():
+    """The features composed: both position tables, interleaved context/action events, a
+    cached prefix filled by an earlier call, then the scoring head on the candidates;
+    the oracle does the same steps."""
+    torch = torch_cuda()
+    D, H, L = 256, 2, 2
+    wl = workloads.make_custom(seed=611, dtype="bf16", layers=L, d_model=D, heads=H, max_len=500,
+                               uih_lengths=[30, 0, 55], cand_lengths=[12, 4, 20], cached_lengths=[60, 25, 0],
+                               position="both", rel_std=0.3, packing="interleave", head=(256, 128, 3))
+    B = wl.users
+    model = make_model(torch, wl)
+    cache = hsa.KVCache(model, slots=4, capacity=300)
+    cache.slot_of_user = np.array([3, 1, 0], dtype=np.int32)
+    cache.cached_len = np.zeros(B, dtype=np.int32)
+    empty = np.zeros((0, D), np.float32)
+    po = workloads.lengths_to_offsets(wl.cached_lengths)
+    ptok, pto = hsa.pack_uih(model, to_dev(torch, wl.prefix, "bf16"), to_dev(torch, wl.prefix_action, "bf16"), po,
+                             "interleave")
+    pl = np.diff(pto.astype(np.int64))
+    gpu_encode(wl, model=model, uih=ptok, uih_lengths=pl, cand=empty, cand_lengths=np.zeros(B, np.int64), cache=cache)
+    eo = workloads.lengths_to_offsets(wl.uih_lengths)
+    tok, to = hsa.pack_uih(model, to_dev(torch, wl.uih, "bf16"), to_dev(torch, wl.action, "bf16"), eo, "interleave")
+    tl = np.diff(to.astype(np.int64))
+    _, dc = gpu_encode(wl, model=model, uih=tok, uih_lengths=tl, cache=cache, keep_device=True)
+    head = hsa.ScoringHead(wl.head, dtype="bf16")
+    got = hsa.score(model, head, dc).cpu().numpy().astype(np.float64)
+    assert cache.cached_len.tolist() == (2 * (wl.cached_lengths + wl.uih_lengths)).tolist()
+
+    ocache = oracle.OracleCache(np.zeros((L, 4, 300, D)), np.zeros((L, 4, 300, D)),
+                                cache.slot_of_user.astype(np.int64), np.zeros(B, np.int64))
+    rpt, _ = oracle.pack_uih(wl.prefix, wl.prefix_action, po, "interleave", bf16=True)
+    _, _, ocache = oracle_encode(wl, "bf16", cache=ocache, uih=rpt, uih_lengths=pl, cand=empty,
+                                 cand_lengths=np.zeros(B, np.int64))
+    rt, _ = oracle.pack_uih(wl.uih, wl.action, eo, "interleave", bf16=True)
+    _, rc, _ = oracle_encode(wl, "bf16", cache=ocache, uih=rt, uih_lengths=tl)
+    want = oracle.score_head(rc, wl.head, bf16=True)
+    err = float(np.max(np.abs(got - want)))
+    say(f"  everything together: max |dp| = {err:.3e} (tol {END_TO_END_TOL})")
+    assert err <= END_TO_END_TOL
