@@ -51,6 +51,42 @@ __device__ __forceinline__ float sum16(float v) {
   return v;
 }
 
+// Statistics of one row's 128-column group held by 16 consecutive lanes, 8 bfloat16
+// values (one 16-byte chunk) each: {mean, M2} with M2 the sum of squared deviations
+// from that mean, both float32 and every lane receiving them. Two passes over the
+// values in registers: the deviations are taken from the group's own mean, so M2
+// carries no cancellation however large the mean is against the spread. All 64 lanes
+// must be active.
+__device__ __forceinline__ float2 group_stats(uint4 q) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  float s = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) s += bf2f_lo(w[e]) + bf2f_hi(w[e]);
+  const float mean = sum16(s) * (1.0f / 128.0f);
+  float d2 = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float a = bf2f_lo(w[e]) - mean, b = bf2f_hi(w[e]) - mean;
+    d2 = __builtin_fmaf(a, a, __builtin_fmaf(b, b, d2));
+  }
+  return make_float2(mean, sum16(d2));
+}
+
+// Mean and variance of a whole row from its groups' {mean, M2}: the groups are merged
+// one at a time by the pairwise update of Chan, Golub and LeVeque (1979): merging n
+// values (mean ma, M2 Ma) with 128 more (mb, Mb) gives mean ma + d * 128 / (n + 128) and
+// M2 Ma + Mb + d^2 * n * 128 / (n + 128), with d = mb - ma. Returns {mean, M2 / D}.
+__device__ __forceinline__ float2 merge_group_stats(const float2* g, int groups) {
+  float mean = g[0].x, m2 = g[0].y;
+  for (int i = 1; i < groups; ++i) {
+    const float2 b = g[i];
+    const float d = b.x - mean, f = 1.0f / (float)(i + 1);   // 128 / (n + 128) with n = 128 i
+    mean = __builtin_fmaf(d, f, mean);
+    m2 += b.y + d * d * (128.0f * (float)i * f);
+  }
+  return make_float2(mean, m2 / (float)(128 * groups));
+}
+
 // Workgroup -> tile order that keeps neighbouring tiles on one XCD. Workgroups are
 // dealt to the 8 XCDs round-robin; giving each XCD a contiguous run of tiles keeps
 // tiles that share operand blocks inside one XCD's L2.

@@ -302,18 +302,12 @@ void uvqk_kernel(UvqkArgs a) {
 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int wm = wv / C::WN, wn = wv % C::WN, l32 = lane & 31, hi = lane >> 5;
-  // Row statistics from the per-128-column partial sums, added in column order.
+  // Row mean and variance from the per-128-column group statistics, merged in column
+  // order.
   for (int r = threadIdx.x; r < C::BM; r += C::NT) {
-    const float2* sp = a.st + (size_t)min(row0 + r, a.T - 1) * (D / 128);
-    float s1 = 0.0f, s2 = 0.0f;
-    for (int g = 0; g < D / 128; ++g) {
-      const float2 v = sp[g];
-      s1 += v.x;
-      s2 += v.y;
-    }
-    const float mean = s1 / (float)D;
-    const float var = fmaxf(s2 / (float)D - mean * mean, 0.0f);
-    const float sigma = sqrtf(var + kNormEps);
+    const float2 mv = merge_group_stats(a.st + (size_t)min(row0 + r, a.T - 1) * (D / 128), D / 128);
+    const float mean = mv.x;
+    const float sigma = sqrtf(mv.y + kNormEps);
     row_mean[r] = mean;
     row_scale[r] = make_float2(-1.4426950408889634f / sigma, sigma);
   }
@@ -480,8 +474,8 @@ void out_kernel(OutArgs a) {
   }
   __syncthreads();
   // Also the next layer's row statistics: each 16 consecutive threads hold one row's
-  // 128-column group and add their {sum, sum of squares} with sum16 (the same grouping
-  // as the first layer's row pass).
+  // 128-column group, whose {mean, M2} group_stats forms exactly as the first layer's
+  // row pass does.
   static_assert(CPR % 16 == 0, "whole 128-column groups per tile row");
 #pragma unroll
   for (int i = 0; i < C::BM * CPR / C::NT; ++i) {
@@ -489,17 +483,8 @@ void out_kernel(OutArgs a) {
     const int row = row0 + r;
     const uint4 v = *reinterpret_cast<const uint4*>(smem + r * OLD + cc);
     if (a.st != nullptr) {
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-      float s1 = 0.0f, s2 = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float lo = bf2f_lo(w[e]), hi = bf2f_hi(w[e]);
-        s1 += lo + hi;
-        s2 = __builtin_fmaf(lo, lo, __builtin_fmaf(hi, hi, s2));
-      }
-      s1 = sum16(s1);
-      s2 = sum16(s2);
-      if ((c & 15) == 0 && row < a.T) a.st[(size_t)row * (D / 128) + (col0 + cc) / 128] = make_float2(s1, s2);
+      const float2 g = group_stats(v);
+      if ((c & 15) == 0 && row < a.T) a.st[(size_t)row * (D / 128) + (col0 + cc) / 128] = g;
     }
     if (row >= a.T) continue;
     u16* y = row < a.Nu ? (u16*)a.y_lo + (size_t)row * D : (u16*)a.y_hi + (size_t)(row - a.Nu) * D;

@@ -1,15 +1,18 @@
 // Host side of the C ABI declared in include/hstu.h: argument validation, the
-// jagged work planner, the pinned staging ring and the per-layer launch sequence.
+// jagged work planner, the plan's transfer to the device and the per-layer launch
+// sequence.
 //
 // Validation is complete before anything is enqueued, so every error except
-// HSTU_ERR_HIP leaves the device and every host array untouched.
+// HSTU_ERR_HIP leaves the device and every host array untouched. The planner works
+// in host memory its caller provides and the plan reaches the device inside kernel
+// arguments, so a call allocates no device or pinned memory and never waits for the
+// device.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cstring>
 #include <mutex>
 #include <numeric>
-#include <unordered_map>
 #include <vector>
 
 #include "hstu.h"
@@ -25,6 +28,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 hstu_status check_dims(const hstu_dims* d) {
   if (!d) return HSTU_ERR_NULL;
   if (d->layers < 1 || d->d_model <= 0 || d->heads <= 0 || d->max_len < 1) return HSTU_ERR_SHAPE;
+  if (d->heads > 127) return HSTU_ERR_SHAPE;   // the planner's item codes hold a head in 7 bits
   if (d->d_model % d->heads) return HSTU_ERR_SHAPE;
   // a position table holds fewer than 2^31 elements (the kernels index it in 32 bits)
   if ((int64_t)d->max_len * 3 * d->d_model >= ((int64_t)1 << 31)) return HSTU_ERR_SHAPE;
@@ -54,22 +58,27 @@ hstu_status check_offsets(int32_t B, const int32_t* uo, const int32_t* co) {
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct Layout {
-  int32_t Nu = 0, Nc = 0, T = 0;
-  int64_t ntiles = 0;
-  size_t users = 0, wptr = 0, items = 0, rows = 0, xn = 0, cs = 0, st = 0, vqk = 0, aout = 0, x = 0, total = 0;
-  size_t staged = 0;  // host-planned part: users table, W1 pointers, attention items (copied up to the grid)
+  int32_t B = 0, Nu = 0, Nc = 0, T = 0;
+  int64_t ntiles = 0, groups = 0;
+  size_t users = 0, wptr = 0, codes = 0, items = 0, rows = 0, xn = 0, cs = 0, st = 0, vqk = 0, aout = 0, x = 0,
+         total = 0;
+  size_t staged = 0;  // host-planned part: users table, W1 pointers, item codes (sent up to the grid)
 };
 
 Layout make_layout(const hstu_dims* d, int32_t B, const int32_t* uo, const int32_t* co) {
   Layout L;
+  L.B = B;
   if (B > 0) {
     L.Nu = uo[B];
     L.Nc = co[B];
   }
   L.T = L.Nu + L.Nc;
   const int bm = hstu::attn_block_rows(d->dtype);
-  for (int32_t b = 0; b < B; ++b)
-    L.ntiles += d->heads * (cdiv(uo[b + 1] - uo[b], bm) + cdiv(co[b + 1] - co[b], bm));
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t per_head = cdiv(uo[b + 1] - uo[b], bm) + cdiv(co[b + 1] - co[b], bm);
+    L.ntiles += d->heads * per_head;
+    L.groups += per_head > 0 ? d->heads : 0;
+  }
   const size_t es = d->dtype == HSTU_F32 ? 4 : 2;
   const size_t D = (size_t)d->d_model, T = (size_t)L.T;
   // GEMM operands (xn, vqk, aout) are padded to whole 256-row tiles.
@@ -78,8 +87,9 @@ Layout make_layout(const hstu_dims* d, int32_t B, const int32_t* uo, const int32
   L.users = off; off += align_up((size_t)B * sizeof(UserRec));
   L.wptr = off; off += align_up((size_t)d->layers * sizeof(void*));
   // one item per attention workgroup: kXcds bins of at most ntiles items each
-  L.items = off; off += align_up((size_t)hstu::kXcds * L.ntiles * sizeof(hstu::AttnItem));
+  L.codes = off; off += align_up((size_t)hstu::kXcds * L.ntiles * sizeof(hstu::ItemCode));
   L.staged = off;
+  L.items = off; off += align_up((size_t)hstu::kXcds * L.ntiles * sizeof(hstu::AttnItem));
   L.rows = off; off += align_up(T * 8);
   // float32 models normalise into xn; bfloat16 models normalise inside the projection
   // and need the column sums of W1 instead
@@ -95,51 +105,126 @@ Layout make_layout(const hstu_dims* d, int32_t B, const int32_t* uo, const int32
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
-// ---------------------------------------------------------------- pinned staging ring
-// The plan (users table + tile list) is written into pinned host memory and copied
-// asynchronously into the workspace. A ring slot is reused only after the copy that
-// last read it has completed (its event), so a call never waits for the device
-// unless more than kRing calls are in flight on the device.
-constexpr int kRing = 4;
-struct StageSlot {
-  void* host = nullptr;
-  size_t cap = 0;
-  hipEvent_t ev = nullptr;
-  bool pending = false;
+// ---------------------------------------------------------------- attention planner
+// Attention work items, grouped per (user, head). Each group goes whole to one of the
+// kXcds bins (one bin per XCD), so a user's keys and values are read into one L2 only;
+// groups are placed largest first on the least loaded bin. Inside a bin the items run
+// longest first (workgroups take them in order as CUs free up), so the bin ends on
+// short items instead of one user's long tail. The order never changes any result:
+// each item writes its own rows, with a fixed key order inside.
+//
+// The planner allocates nothing: its caller provides the group and item records. Every
+// sort key is a total order (ties broken by a sequence number), so std::sort gives the
+// same order on every call.
+struct PlanItem {
+  int64_t cost;           // key blocks swept, plus a fixed per-item overhead
+  int32_t user, code;     // code as in hstu::ItemCode
+  int32_t seq, bin;       // push order inside the group, then append order inside the bin
 };
-struct DeviceStage {
-  StageSlot slot[kRing];
-  int next = 0;
+struct PlanGroup {
+  int64_t cost;
+  int32_t first, count;   // its items
+  int32_t index, pad;
 };
-std::mutex g_stage_mu;
-std::unordered_map<int, DeviceStage> g_stage;
 
-hstu_status stage_and_copy(const void* src, size_t bytes, void* dst, hipStream_t stream) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return HSTU_ERR_HIP;
-  std::lock_guard<std::mutex> lock(g_stage_mu);
-  DeviceStage& ds = g_stage[dev];
-  StageSlot& s = ds.slot[ds.next];
-  ds.next = (ds.next + 1) % kRing;
-  if (s.pending) {
-    if (hipEventSynchronize(s.ev) != hipSuccess) return HSTU_ERR_HIP;
-    s.pending = false;
+// Fills codes[0, grid) and returns grid, the attention's workgroup count: workgroup w
+// runs on XCD w % kXcds and takes position w / kXcds of that XCD's bin (user -1 past
+// the bin's end).
+int plan_attention(const UserRec* users, int32_t B, int32_t heads, int bm, PlanGroup* groups, PlanItem* items,
+                   hstu::ItemCode* codes) {
+  int32_t G = 0, N = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    const UserRec& u = users[b];
+    for (int32_t h = 0; h < heads; ++h) {
+      const int32_t first = N;
+      for (int32_t q0 = 0; q0 < u.n; q0 += bm) {
+        const int32_t nq = std::min(bm, u.n - q0);
+        items[N] = {cdiv((int64_t)u.m + q0 + nq, 64) + 2, b, ((q0 / bm) << 8) | (h << 1), N - first, -1};
+        ++N;
+      }
+      for (int32_t q0 = 0; q0 < u.c; q0 += bm) {
+        items[N] = {cdiv((int64_t)u.m + u.n, 64) + 2, b, ((q0 / bm) << 8) | (h << 1) | 1, N - first, -1};
+        ++N;
+      }
+      if (N == first) continue;
+      // the group's items, longest first (ties in push order)
+      std::sort(items + first, items + N, [](const PlanItem& x, const PlanItem& y) {
+        return x.cost != y.cost ? x.cost > y.cost : x.seq < y.seq;
+      });
+      int64_t cost = 0;
+      for (int32_t i = first; i < N; ++i) cost += items[i].cost;
+      groups[G] = {cost, first, N - first, G, 0};
+      ++G;
+    }
   }
-  if (s.cap < bytes) {
-    if (s.host && hipHostFree(s.host) != hipSuccess) return HSTU_ERR_HIP;
-    s.host = nullptr;
-    s.cap = 0;
-    size_t cap = std::max<size_t>(bytes, 64 * 1024);
-    if (hipHostMalloc(&s.host, cap, hipHostMallocDefault) != hipSuccess) return HSTU_ERR_HIP;
-    s.cap = cap;
+  std::sort(groups, groups + G, [](const PlanGroup& x, const PlanGroup& y) {
+    return x.cost != y.cost ? x.cost > y.cost : x.index < y.index;
+  });
+  int64_t bin_cost[hstu::kXcds] = {};
+  int32_t bin_n[hstu::kXcds] = {};
+  for (int32_t g = 0; g < G; ++g) {
+    const int x = (int)(std::min_element(bin_cost, bin_cost + hstu::kXcds) - bin_cost);
+    bin_cost[x] += groups[g].cost;
+    for (int32_t i = groups[g].first; i < groups[g].first + groups[g].count; ++i) {
+      items[i].bin = x;
+      items[i].seq = bin_n[x]++;
+    }
   }
-  if (!s.ev && hipEventCreateWithFlags(&s.ev, hipEventDisableTiming) != hipSuccess) return HSTU_ERR_HIP;
-  std::memcpy(s.host, src, bytes);
-  if (hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, stream) != hipSuccess)
-    return HSTU_ERR_HIP;
-  if (hipEventRecord(s.ev, stream) != hipSuccess) return HSTU_ERR_HIP;
-  s.pending = true;
-  return HSTU_OK;
+  std::sort(items, items + N, [](const PlanItem& x, const PlanItem& y) {
+    if (x.bin != y.bin) return x.bin < y.bin;
+    return x.cost != y.cost ? x.cost > y.cost : x.seq < y.seq;
+  });
+  int32_t start[hstu::kXcds] = {}, longest = 0;
+  for (int x = 0, acc = 0; x < hstu::kXcds; ++x) {
+    start[x] = acc;
+    acc += bin_n[x];
+    longest = std::max(longest, bin_n[x]);
+  }
+  const int grid = hstu::kXcds * longest;
+  for (int w = 0; w < grid; ++w) {
+    const int x = w % hstu::kXcds, j = w / hstu::kXcds;
+    codes[w] = j < bin_n[x] ? hstu::ItemCode{items[start[x] + j].user, items[start[x] + j].code}
+                            : hstu::ItemCode{-1, 0};
+  }
+  return grid;
+}
+
+// Host memory the planner of one call works in.
+struct PlanSpace {
+  PlanGroup* groups = nullptr;
+  PlanItem* items = nullptr;
+  unsigned char* image = nullptr;   // the upload image: users | W1 pointers | item codes
+  int32_t* keys = nullptr;          // validation scratch: one entry per user
+};
+
+// The calling thread's planner memory for a layout, grown when a larger plan comes
+// (host memory only; steady-state calls of one shape reuse it).
+PlanSpace thread_plan_space(const Layout& lay) {
+  thread_local std::vector<PlanGroup> groups;
+  thread_local std::vector<PlanItem> items;
+  thread_local std::vector<unsigned char> image;
+  thread_local std::vector<int32_t> keys;
+  if (groups.size() < (size_t)lay.groups) groups.resize((size_t)lay.groups);
+  if (items.size() < (size_t)lay.ntiles) items.resize((size_t)lay.ntiles);
+  if (image.size() < lay.staged) image.resize(lay.staged);
+  if (keys.size() < (size_t)lay.B) keys.resize((size_t)lay.B);
+  return PlanSpace{groups.data(), items.data(), image.data(), keys.data()};
+}
+
+// Copies `bytes` (a multiple of 4) from host memory to device memory dst on `stream`
+// inside the arguments of upload kernels.
+hipError_t upload(const unsigned char* src, size_t bytes, char* dst, hipStream_t stream) {
+  constexpr size_t kChunk = sizeof(uint32_t) * hstu::kUploadWords;
+  for (size_t off = 0; off < bytes; off += kChunk) {
+    hstu::UploadArgs ua;
+    ua.dst = reinterpret_cast<uint32_t*>(dst + off);
+    ua.words = (int32_t)(std::min(kChunk, bytes - off) / sizeof(uint32_t));
+    ua.pad = 0;
+    std::memcpy(ua.w, src + off, (size_t)ua.words * sizeof(uint32_t));
+    const hipError_t e = hstu::launch_upload(ua, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------- per-kernel timing
@@ -184,6 +269,185 @@ hipError_t timed_launch(int kind, hipStream_t s, F&& f) {
   if (e != hipSuccess) return e;
   g_timing.recs.push_back({kind, a, b});
   return hipSuccess;
+}
+
+// ---------------------------------------------------------------- hstu_encode's steps
+struct EncodeCall {
+  const hstu_dims* d;
+  int32_t B;
+  const int32_t* uo;
+  const int32_t* co;
+  const void* uih;
+  const void* cand;
+  const hstu_layer_weights* w;
+  hstu_kv_cache* kv;
+  void* uih_out;
+  void* cand_out;
+  Layout lay;
+};
+
+// Every argument but the workspace (host only; nothing is enqueued, nothing written
+// but `keys`, int32 scratch of at least B entries). c.lay must be make_layout's.
+hstu_status validate_encode(EncodeCall& c, int32_t* keys) {
+  const hstu_dims* d = c.d;
+  hstu_status st = check_dims(d);
+  if (st != HSTU_OK) return st;
+  st = check_offsets(c.B, c.uo, c.co);
+  if (st != HSTU_OK) return st;
+  if (!c.w) return HSTU_ERR_NULL;
+  if (c.lay.T == 0) return HSTU_OK;
+  for (int32_t l = 0; l < d->layers; ++l) {
+    const hstu_layer_weights& w = c.w[l];
+    if (!w.w_uvqk || !w.w_out) return HSTU_ERR_NULL;
+    if (!aligned16(w.w_uvqk) || !aligned16(w.w_out) || !aligned16(w.pos_bias) || !aligned16(w.rel_bias))
+      return HSTU_ERR_ALIGN;
+    if (w.rel_bias && d->dtype == HSTU_BF16 && d->max_len > hstu::kRelMaxLen) return HSTU_ERR_SHAPE;
+  }
+  const Layout& lay = c.lay;
+  if ((lay.Nu > 0 && (!c.uih || !c.uih_out)) || (lay.Nc > 0 && (!c.cand || !c.cand_out))) return HSTU_ERR_NULL;
+  if ((lay.Nu > 0 && (!aligned16(c.uih) || !aligned16(c.uih_out))) ||
+      (lay.Nc > 0 && (!aligned16(c.cand) || !aligned16(c.cand_out))))
+    return HSTU_ERR_ALIGN;
+  const hstu_kv_cache* kv = c.kv;
+  if (kv) {
+    if (!kv->k || !kv->v || !kv->slot_of_user || !kv->cached_len) return HSTU_ERR_NULL;
+    if (!aligned16(kv->k) || !aligned16(kv->v)) return HSTU_ERR_ALIGN;
+    if (kv->slots <= 0 || kv->capacity <= 0) return HSTU_ERR_CAPACITY;
+  }
+  for (int32_t b = 0; b < c.B; ++b) {
+    const int64_t n = c.uo[b + 1] - c.uo[b];
+    // the planner's item codes hold a query block index in 23 bits
+    if (n >= ((int64_t)1 << 30) || c.co[b + 1] - c.co[b] >= ((int64_t)1 << 30)) return HSTU_ERR_SHAPE;
+    int64_t m = 0;
+    if (kv) {
+      m = kv->cached_len[b];
+      const int32_t slot = kv->slot_of_user[b];
+      if (m < 0 || slot < 0 || slot >= kv->slots) return HSTU_ERR_CAPACITY;
+      if (m + n > kv->capacity) return HSTU_ERR_CAPACITY;
+    }
+    if (m + n + 1 > d->max_len) return HSTU_ERR_CAPACITY;
+    // the attention kernel addresses one user's key rows with 32-bit byte offsets
+    if ((m + n) * (int64_t)(kv ? d->d_model : 3 * d->d_model) * (d->dtype == HSTU_F32 ? 4 : 2) > INT32_MAX)
+      return HSTU_ERR_CAPACITY;
+  }
+  // distinct slots: no two users of the call may write the same cache rows
+  if (kv && c.B > 1) {
+    std::copy(kv->slot_of_user, kv->slot_of_user + c.B, keys);
+    std::sort(keys, keys + c.B);
+    if (std::adjacent_find(keys, keys + c.B) != keys + c.B) return HSTU_ERR_CAPACITY;
+  }
+  return HSTU_OK;
+}
+
+// Plans the call in `ps` and enqueues it on stream s with workspace ws (a validated call
+// with T > 0 and a workspace of c.lay.total bytes).
+hstu_status run_encode(const EncodeCall& c, const PlanSpace& ps, char* ws, hipStream_t s) {
+  const hstu_dims* d = c.d;
+  const Layout& lay = c.lay;
+  const hstu_kv_cache* kv = c.kv;
+  const int32_t B = c.B, L = d->layers, D = d->d_model;
+
+  // ------------------------------------------------------------ plan (host)
+  const int bm = hstu::attn_block_rows(d->dtype);
+  std::memset(ps.image, 0, lay.codes);
+  UserRec* users = reinterpret_cast<UserRec*>(ps.image + lay.users);
+  for (int32_t b = 0; b < B; ++b) {
+    UserRec& u = users[b];
+    u.uoff = c.uo[b];
+    u.n = c.uo[b + 1] - c.uo[b];
+    u.coff = c.co[b];
+    u.c = c.co[b + 1] - c.co[b];
+    u.m = kv ? kv->cached_len[b] : 0;
+    u.key_row = kv ? kv->slot_of_user[b] * kv->capacity : u.uoff;
+    u.pad0 = u.pad1 = 0;
+  }
+  const void** wptr = reinterpret_cast<const void**>(ps.image + lay.wptr);
+  for (int32_t l = 0; l < L; ++l) wptr[l] = c.w[l].w_uvqk;
+  hstu::ItemCode* codes = reinterpret_cast<hstu::ItemCode*>(ps.image + lay.codes);
+  const int attn_grid = plan_attention(users, B, d->heads, bm, ps.groups, ps.items, codes);
+
+  // ------------------------------------------------------------ enqueue
+  if (timed_launch(HSTU_KERNEL_PLAN, s, [&] {
+        return upload(ps.image, lay.codes + (size_t)attn_grid * sizeof(hstu::ItemCode), ws, s);
+      }) != hipSuccess)
+    return HSTU_ERR_HIP;
+  const UserRec* d_users = reinterpret_cast<const UserRec*>(ws + lay.users);
+  hstu::AttnItem* d_items = reinterpret_cast<hstu::AttnItem*>(ws + lay.items);
+  int2* d_rows = reinterpret_cast<int2*>(ws + lay.rows);
+  char* xn = ws + lay.xn;
+  float* cs = reinterpret_cast<float*>(ws + lay.cs);
+  float2* rstat = reinterpret_cast<float2*>(ws + lay.st);
+  const size_t es = d->dtype == HSTU_F32 ? 4 : 2;
+  char* vqk = ws + lay.vqk;
+  char* aout = ws + lay.aout;
+  char* xbuf = ws + lay.x;
+  const size_t nu_bytes = (size_t)lay.Nu * D * es;
+
+  hstu::PlanArgs pa{d_users, B, lay.Nu, lay.T, d_rows,
+                    reinterpret_cast<const hstu::ItemCode*>(ws + lay.codes), d_items, attn_grid, bm};
+  if (timed_launch(HSTU_KERNEL_PLAN, s, [&] { return hstu::launch_plan(pa, s); }) != hipSuccess)
+    return HSTU_ERR_HIP;
+
+  if (d->dtype != HSTU_F32) {
+    hstu::ColsumArgs ca{reinterpret_cast<const void* const*>(ws + lay.wptr), L, D, cs};
+    if (timed_launch(HSTU_KERNEL_NORM, s, [&] { return hstu::launch_colsum(ca, s); }) != hipSuccess)
+      return HSTU_ERR_HIP;
+    if (timed_launch(HSTU_KERNEL_NORM, s,
+                     [&] { return hstu::launch_rowstats(c.uih, c.cand, lay.Nu, lay.T, D, rstat, s); }) != hipSuccess)
+      return HSTU_ERR_HIP;
+  }
+
+  const int dh = D / d->heads;
+  const size_t layer_cache = kv ? (size_t)kv->slots * kv->capacity * D * es : 0;
+  for (int32_t l = 0; l < L; ++l) {
+    const void* x_lo = l == 0 ? c.uih : xbuf;
+    const void* x_hi = l == 0 ? c.cand : (const void*)(xbuf + nu_bytes);
+    void* y_lo = l == L - 1 ? c.uih_out : (void*)xbuf;
+    void* y_hi = l == L - 1 ? c.cand_out : (void*)(xbuf + nu_bytes);
+    void* ck = kv ? (void*)((char*)kv->k + l * layer_cache) : nullptr;
+    void* cv = kv ? (void*)((char*)kv->v + l * layer_cache) : nullptr;
+
+    if (d->dtype == HSTU_F32) {
+      hstu::NormArgs na{x_lo, x_hi, lay.Nu, lay.T, D, xn};
+      if (timed_launch(HSTU_KERNEL_NORM, s, [&] { return hstu::launch_norm(d->dtype, na, s); }) != hipSuccess)
+        return HSTU_ERR_HIP;
+    }
+    hstu::UvqkArgs ua{xn, x_lo, x_hi, cs + (size_t)l * 4 * D, rstat, lay.Nu, lay.T, D, c.w[l].w_uvqk,
+                      c.w[l].pos_bias, d_rows, d_users, vqk, aout, ck, cv};
+    if (timed_launch(HSTU_KERNEL_UVQK, s, [&] { return hstu::launch_uvqk(d->dtype, ua, s); }) != hipSuccess)
+      return HSTU_ERR_HIP;
+
+    hstu::AttnArgs aa{};
+    aa.items = d_items;
+    aa.Nu = lay.Nu;
+    aa.D = D;
+    aa.inv = 1.0f / (float)d->max_len;
+    aa.vqk = vqk;
+    if (kv) {
+      aa.kbase = ck;
+      aa.vbase = cv;
+      aa.ld = D;
+    } else {
+      aa.kbase = vqk + 2 * (size_t)D * es;
+      aa.vbase = vqk;
+      aa.ld = 3 * (int64_t)D;
+    }
+    aa.aout = aout;
+    aa.rel = c.w[l].rel_bias;
+    aa.max_len = d->max_len;
+    if (timed_launch(HSTU_KERNEL_ATTENTION, s,
+                     [&] { return hstu::launch_attn(d->dtype, dh, aa, attn_grid, s); }) != hipSuccess)
+      return HSTU_ERR_HIP;
+
+    // the output GEMM also leaves the next layer's row statistics (bfloat16 path)
+    hstu::OutArgs oa{aout, c.w[l].w_out, x_lo, x_hi, y_lo, y_hi,
+                     d->dtype == HSTU_F32 || l == L - 1 ? nullptr : rstat, lay.Nu, lay.T, D};
+    if (timed_launch(HSTU_KERNEL_OUT, s, [&] { return hstu::launch_out(d->dtype, oa, s); }) != hipSuccess)
+      return HSTU_ERR_HIP;
+  }
+  if (kv)
+    for (int32_t b = 0; b < B; ++b) kv->cached_len[b] += c.uo[b + 1] - c.uo[b];
+  return HSTU_OK;
 }
 
 }  // namespace
@@ -296,212 +560,18 @@ hstu_status hstu_encode(const hstu_dims* d, int32_t B, const int32_t* uih_offset
                         const int32_t* cand_offsets, const void* uih, const void* cand,
                         const hstu_layer_weights* w, hstu_kv_cache* kv, void* uih_out,
                         void* cand_out, void* workspace, size_t workspace_bytes, void* stream) {
-  // ------------------------------------------------------------ validation (host only)
   hstu_status st = check_dims(d);
   if (st != HSTU_OK) return st;
   st = check_offsets(B, uih_offsets, cand_offsets);
   if (st != HSTU_OK) return st;
-  if (!w) return HSTU_ERR_NULL;
-  const Layout lay = make_layout(d, B, uih_offsets, cand_offsets);
-  if (lay.T == 0) return HSTU_OK;  // nothing to encode; no history appended
-  const int32_t L = d->layers, D = d->d_model;
-  for (int32_t l = 0; l < L; ++l) {
-    if (!w[l].w_uvqk || !w[l].w_out) return HSTU_ERR_NULL;
-    if (!aligned16(w[l].w_uvqk) || !aligned16(w[l].w_out) || !aligned16(w[l].pos_bias) ||
-        !aligned16(w[l].rel_bias))
-      return HSTU_ERR_ALIGN;
-    if (w[l].rel_bias && d->dtype == HSTU_BF16 && d->max_len > hstu::kRelMaxLen) return HSTU_ERR_SHAPE;
-  }
-  if ((lay.Nu > 0 && (!uih || !uih_out)) || (lay.Nc > 0 && (!cand || !cand_out))) return HSTU_ERR_NULL;
-  if ((lay.Nu > 0 && (!aligned16(uih) || !aligned16(uih_out))) ||
-      (lay.Nc > 0 && (!aligned16(cand) || !aligned16(cand_out))))
-    return HSTU_ERR_ALIGN;
-  if (kv) {
-    if (!kv->k || !kv->v || !kv->slot_of_user || !kv->cached_len) return HSTU_ERR_NULL;
-    if (!aligned16(kv->k) || !aligned16(kv->v)) return HSTU_ERR_ALIGN;
-    if (kv->slots <= 0 || kv->capacity <= 0) return HSTU_ERR_CAPACITY;
-  }
-  std::vector<char> slot_used(kv ? (size_t)kv->slots : 0, 0);
-  for (int32_t b = 0; b < B; ++b) {
-    const int64_t n = uih_offsets[b + 1] - uih_offsets[b];
-    int64_t m = 0;
-    if (kv) {
-      m = kv->cached_len[b];
-      const int32_t slot = kv->slot_of_user[b];
-      if (m < 0 || slot < 0 || slot >= kv->slots || slot_used[slot]) return HSTU_ERR_CAPACITY;
-      slot_used[slot] = 1;
-      if (m + n > kv->capacity) return HSTU_ERR_CAPACITY;
-    }
-    if (m + n + 1 > d->max_len) return HSTU_ERR_CAPACITY;
-    // the attention kernel addresses one user's key rows with 32-bit byte offsets
-    if ((m + n) * (int64_t)(kv ? d->d_model : 3 * d->d_model) * (d->dtype == HSTU_F32 ? 4 : 2) > INT32_MAX)
-      return HSTU_ERR_CAPACITY;
-  }
-  if (!workspace || workspace_bytes < lay.total) return HSTU_ERR_WORKSPACE;
+  EncodeCall c{d, B, uih_offsets, cand_offsets, uih, cand, w, kv, uih_out, cand_out,
+               make_layout(d, B, uih_offsets, cand_offsets)};
+  const PlanSpace ps = thread_plan_space(c.lay);
+  st = validate_encode(c, ps.keys);
+  if (st != HSTU_OK || c.lay.T == 0) return st;   // T = 0: nothing to encode, no history appended
+  if (!workspace || workspace_bytes < c.lay.total) return HSTU_ERR_WORKSPACE;
   if (((uintptr_t)workspace & (kAlign - 1)) != 0) return HSTU_ERR_ALIGN;
-
-  // ------------------------------------------------------------ plan (host)
-  const int bm = hstu::attn_block_rows(d->dtype);
-  std::vector<char> staged(lay.staged, 0);
-  UserRec* users = reinterpret_cast<UserRec*>(staged.data() + lay.users);
-  for (int32_t b = 0; b < B; ++b) {
-    UserRec& u = users[b];
-    u.uoff = uih_offsets[b];
-    u.n = uih_offsets[b + 1] - uih_offsets[b];
-    u.coff = cand_offsets[b];
-    u.c = cand_offsets[b + 1] - cand_offsets[b];
-    u.m = kv ? kv->cached_len[b] : 0;
-    u.key_row = kv ? kv->slot_of_user[b] * kv->capacity : u.uoff;
-    u.pad0 = u.pad1 = 0;
-  }
-  // Attention work items, grouped per (user, head). Each group goes whole to one of
-  // the kXcds bins (one bin per XCD), so a user's keys and values are read into one
-  // L2 only; groups are placed largest first on the least loaded bin. The order never
-  // changes any result: each item writes its own rows, with a fixed key order inside.
-  struct Item { int32_t user, hk, q0, nq; int64_t cost; };
-  struct Group { std::vector<Item> items; int64_t cost = 0; };
-  std::vector<Group> groups;
-  groups.reserve((size_t)B * d->heads);
-  for (int32_t b = 0; b < B; ++b) {
-    const UserRec& u = users[b];
-    for (int32_t h = 0; h < d->heads; ++h) {
-      Group g;
-      // cost ~ key blocks swept, plus a fixed per-item overhead
-      for (int32_t q0 = 0; q0 < u.n; q0 += bm) {
-        const int32_t nq = std::min(bm, u.n - q0);
-        g.items.push_back({b, h << 1, q0, nq, cdiv((int64_t)u.m + q0 + nq, 64) + 2});
-      }
-      for (int32_t q0 = 0; q0 < u.c; q0 += bm)
-        g.items.push_back({b, (h << 1) | 1, q0, std::min(bm, u.c - q0), cdiv((int64_t)u.m + u.n, 64) + 2});
-      if (g.items.empty()) continue;
-      std::stable_sort(g.items.begin(), g.items.end(),
-                       [](const Item& x, const Item& y) { return x.cost > y.cost; });
-      for (const Item& it : g.items) g.cost += it.cost;
-      groups.push_back(std::move(g));
-    }
-  }
-  std::stable_sort(groups.begin(), groups.end(),
-                   [](const Group& x, const Group& y) { return x.cost > y.cost; });
-  std::vector<std::vector<const Item*>> bin_items(hstu::kXcds);
-  int64_t bin_cost[hstu::kXcds] = {};
-  for (const Group& g : groups) {
-    const int x = (int)(std::min_element(bin_cost, bin_cost + hstu::kXcds) - bin_cost);
-    bin_cost[x] += g.cost;
-    for (const Item& it : g.items) bin_items[x].push_back(&it);
-  }
-  // Inside a bin, items run longest first (workgroups take them in order as CUs free
-  // up), so the bin ends on short items instead of one user's long tail.
-  for (int x = 0; x < hstu::kXcds; ++x)
-    std::stable_sort(bin_items[x].begin(), bin_items[x].end(),
-                     [](const Item* p, const Item* q) { return p->cost > q->cost; });
-  size_t longest = 0;
-  for (int x = 0; x < hstu::kXcds; ++x) longest = std::max(longest, bin_items[x].size());
-  const int attn_grid = hstu::kXcds * (int)longest;
-  // workgroup w runs on XCD w % kXcds: it takes position w / kXcds of that XCD's bin
-  // (nq = 0 past the bin's end)
-  hstu::AttnItem* items = reinterpret_cast<hstu::AttnItem*>(staged.data() + lay.items);
-  for (int w = 0; w < attn_grid; ++w) {
-    const std::vector<const Item*>& bin = bin_items[w % hstu::kXcds];
-    const size_t j = (size_t)(w / hstu::kXcds);
-    hstu::AttnItem& a = items[w];
-    a = hstu::AttnItem{0, 0, 0, 0, 0, 0, 0, 0};
-    if (j >= bin.size()) continue;
-    const Item& it = *bin[j];
-    const UserRec& u = users[it.user];
-    const bool is_cand = (it.hk & 1) != 0;
-    a.hk = it.hk;
-    a.q0 = it.q0;
-    a.nq = it.nq;
-    a.m = u.m;
-    a.rbase = (is_cand ? lay.Nu + u.coff : u.uoff) + it.q0;
-    a.key_end = is_cand ? u.m + u.n : u.m + it.q0 + it.nq;
-    a.key_row = u.key_row;
-  }
-  const size_t staged_bytes = lay.items + (size_t)attn_grid * sizeof(hstu::AttnItem);
-  const void** wptr = reinterpret_cast<const void**>(staged.data() + lay.wptr);
-  for (int32_t l = 0; l < L; ++l) wptr[l] = w[l].w_uvqk;
-
-  // ------------------------------------------------------------ enqueue
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  st = stage_and_copy(staged.data(), staged_bytes, ws, s);
-  if (st != HSTU_OK) return st;
-  const UserRec* d_users = reinterpret_cast<const UserRec*>(ws + lay.users);
-  const hstu::AttnItem* d_items = reinterpret_cast<const hstu::AttnItem*>(ws + lay.items);
-  int2* d_rows = reinterpret_cast<int2*>(ws + lay.rows);
-  char* xn = ws + lay.xn;
-  float* cs = reinterpret_cast<float*>(ws + lay.cs);
-  float2* rstat = reinterpret_cast<float2*>(ws + lay.st);
-  const size_t es = d->dtype == HSTU_F32 ? 4 : 2;
-  char* vqk = ws + lay.vqk;
-  char* aout = ws + lay.aout;
-  char* xbuf = ws + lay.x;
-  const size_t nu_bytes = (size_t)lay.Nu * D * es;
-
-  hstu::PlanArgs pa{d_users, B, lay.Nu, lay.T, d_rows};
-  if (timed_launch(HSTU_KERNEL_PLAN, s, [&] { return hstu::launch_plan(pa, s); }) != hipSuccess)
-    return HSTU_ERR_HIP;
-
-  if (d->dtype != HSTU_F32) {
-    hstu::ColsumArgs ca{reinterpret_cast<const void* const*>(ws + lay.wptr), L, D, cs};
-    if (timed_launch(HSTU_KERNEL_NORM, s, [&] { return hstu::launch_colsum(ca, s); }) != hipSuccess)
-      return HSTU_ERR_HIP;
-    if (timed_launch(HSTU_KERNEL_NORM, s,
-                     [&] { return hstu::launch_rowstats(uih, cand, lay.Nu, lay.T, D, rstat, s); }) != hipSuccess)
-      return HSTU_ERR_HIP;
-  }
-
-  const int dh = D / d->heads;
-  const size_t layer_cache = kv ? (size_t)kv->slots * kv->capacity * D * es : 0;
-  for (int32_t l = 0; l < L; ++l) {
-    const void* x_lo = l == 0 ? uih : xbuf;
-    const void* x_hi = l == 0 ? cand : (const void*)(xbuf + nu_bytes);
-    void* y_lo = l == L - 1 ? uih_out : (void*)xbuf;
-    void* y_hi = l == L - 1 ? cand_out : (void*)(xbuf + nu_bytes);
-    void* ck = kv ? (void*)((char*)kv->k + l * layer_cache) : nullptr;
-    void* cv = kv ? (void*)((char*)kv->v + l * layer_cache) : nullptr;
-
-    if (d->dtype == HSTU_F32) {
-      hstu::NormArgs na{x_lo, x_hi, lay.Nu, lay.T, D, xn};
-      if (timed_launch(HSTU_KERNEL_NORM, s, [&] { return hstu::launch_norm(d->dtype, na, s); }) != hipSuccess)
-        return HSTU_ERR_HIP;
-    }
-    hstu::UvqkArgs ua{xn, x_lo, x_hi, cs + (size_t)l * 4 * D, rstat, lay.Nu, lay.T, D, w[l].w_uvqk, w[l].pos_bias, d_rows, d_users,
-                      vqk, aout, ck, cv};
-    if (timed_launch(HSTU_KERNEL_UVQK, s, [&] { return hstu::launch_uvqk(d->dtype, ua, s); }) != hipSuccess)
-      return HSTU_ERR_HIP;
-
-    hstu::AttnArgs aa{};
-    aa.items = d_items;
-    aa.Nu = lay.Nu;
-    aa.D = D;
-    aa.inv = 1.0f / (float)d->max_len;
-    aa.vqk = vqk;
-    if (kv) {
-      aa.kbase = ck;
-      aa.vbase = cv;
-      aa.ld = D;
-    } else {
-      aa.kbase = vqk + 2 * (size_t)D * es;
-      aa.vbase = vqk;
-      aa.ld = 3 * (int64_t)D;
-    }
-    aa.aout = aout;
-    aa.rel = w[l].rel_bias;
-    aa.max_len = d->max_len;
-    if (timed_launch(HSTU_KERNEL_ATTENTION, s,
-                     [&] { return hstu::launch_attn(d->dtype, dh, aa, attn_grid, s); }) != hipSuccess)
-      return HSTU_ERR_HIP;
-
-    // the output GEMM also leaves the next layer's row statistics (bfloat16 path)
-    hstu::OutArgs oa{aout, w[l].w_out, x_lo, x_hi, y_lo, y_hi,
-                     d->dtype == HSTU_F32 || l == L - 1 ? nullptr : rstat, lay.Nu, lay.T, D};
-    if (timed_launch(HSTU_KERNEL_OUT, s, [&] { return hstu::launch_out(d->dtype, oa, s); }) != hipSuccess)
-      return HSTU_ERR_HIP;
-  }
-  if (kv)
-    for (int32_t b = 0; b < B; ++b) kv->cached_len[b] += uih_offsets[b + 1] - uih_offsets[b];
-  return HSTU_OK;
+  return run_encode(c, ps, static_cast<char*>(workspace), reinterpret_cast<hipStream_t>(stream));
 }
 
 hstu_status hstu_pack_uih(const hstu_dims* d, int32_t events, int32_t mode, const void* context,

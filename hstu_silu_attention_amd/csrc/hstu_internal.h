@@ -37,10 +37,31 @@ struct AttnItem {
   int32_t hk, q0, nq, m, rbase, key_end, key_row, pad;
 };
 
+// Compact attention work item (8 bytes) as the host planner writes it: user -1 for no
+// work, else code = (query block << 8) | (head << 1) | is_candidate. The plan kernel
+// expands it into an AttnItem.
+struct ItemCode {
+  int32_t user, code;
+};
+
 struct PlanArgs {
   const UserRec* users;
   int32_t B, Nu, T;
   int2* row_info;        // [T] {user, position}
+  const ItemCode* codes; // [grid]
+  AttnItem* items;       // [grid] out
+  int32_t grid, bm;      // attention workgroups; query rows per work item
+};
+
+// Host -> device transfer through kernel arguments: `words` 32-bit words (at most
+// kUploadWords) copied to dst. Kernel arguments are captured by value when the launch
+// is enqueued, so the host source can be reused at once, nothing is allocated and the
+// host never waits for the device.
+constexpr int kUploadWords = 896;
+struct UploadArgs {
+  uint32_t* dst;
+  int32_t words, pad;
+  uint32_t w[kUploadWords];
 };
 
 // Workspace buffers of one layer (rows in the packed order: history rows of every
@@ -49,9 +70,10 @@ struct PlanArgs {
 //  xn   [T_pad][D]   normalised layer input, the float32 projection's A operand (the
 //                    bfloat16 projection normalises inside: no buffer)
 //  cs   [L][4D]      float32 column sums of each layer's W1 (bfloat16 only)
-//  st   [T][D/128]   float2 {sum, sum of squares} of each layer-input row over each
-//                    128-column group, in float32 (bfloat16 only): written by the
-//                    previous layer's output GEMM (the first layer's by a row pass)
+//  st   [T][D/128]   float2 {mean, sum of squared deviations from that mean} of each
+//                    layer-input row over each 128-column group, in float32 (bfloat16
+//                    only): written by the previous layer's output GEMM (the first
+//                    layer's by a row pass)
 //  vqk  [T_pad][3D]  V | Q | K after SiLU and position bias
 //  aout [T_pad][3D]  U | O | U*O: the output GEMM's A operand. The projection writes
 //                    U and the attention O; the float32 attention also writes the
@@ -147,6 +169,7 @@ struct ScoreArgs {
 };
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+hipError_t launch_upload(const UploadArgs& a, hipStream_t s);
 hipError_t launch_pack(const PackArgs& a, hipStream_t s);
 hipError_t launch_score(int dtype, const ScoreArgs& a, hipStream_t s);
 hipError_t launch_norm(int dtype, const NormArgs& a, hipStream_t s);

@@ -1,6 +1,8 @@
 // The jagged row planner kernel and the per-dtype launch dispatch.
 #include <hip/hip_runtime.h>
 
+#include <cstddef>
+
 #include "hstu.h"
 #include "bf16_common.h"
 #include "hstu_internal.h"
@@ -23,7 +25,31 @@ namespace {
 // [Nu, T) to the user whose candidate segment holds r - Nu, all at position m + n.
 // The user is the last one whose segment starts at or before r (segments of empty
 // users start where the next one does).
+//
+// The blocks past the rows' expand the planner's compact work items: workgroup w of
+// the attention gets item w.
 __global__ __launch_bounds__(256) void plan_rows_kernel(PlanArgs a) {
+  const int row_blocks = (a.T + 255) / 256;
+  if ((int)blockIdx.x >= row_blocks) {
+    const int w = ((int)blockIdx.x - row_blocks) * 256 + threadIdx.x;
+    if (w >= a.grid) return;
+    const ItemCode ic = a.codes[w];
+    AttnItem it{0, 0, 0, 0, 0, 0, 0, 0};
+    if (ic.user >= 0) {
+      const UserRec u = a.users[ic.user];
+      const bool cand = (ic.code & 1) != 0;
+      const int q0 = (ic.code >> 8) * a.bm;
+      it.hk = ic.code & 0xff;
+      it.q0 = q0;
+      it.nq = min(a.bm, (cand ? u.c : u.n) - q0);
+      it.m = u.m;
+      it.rbase = (cand ? a.Nu + u.coff : u.uoff) + q0;
+      it.key_end = cand ? u.m + u.n : u.m + q0 + it.nq;
+      it.key_row = u.key_row;
+    }
+    a.items[w] = it;
+    return;
+  }
   const int r = blockIdx.x * 256 + threadIdx.x;
   if (r >= a.T) return;
   const bool hist = r < a.Nu;
@@ -36,6 +62,13 @@ __global__ __launch_bounds__(256) void plan_rows_kernel(PlanArgs a) {
   }
   const UserRec u = a.users[lo];
   a.row_info[r] = make_int2(lo, hist ? u.m + (key - u.uoff) : u.m + u.n);
+}
+
+// The payload is read through the kernel-argument segment pointer, so indexing it by
+// thread never copies the argument block into private memory.
+__global__ __launch_bounds__(256) void upload_kernel(UploadArgs a) {
+  const uint32_t* w = (const uint32_t*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() + offsetof(UploadArgs, w));
+  for (int i = threadIdx.x; i < a.words; i += 256) a.dst[i] = w[i];
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -118,29 +151,21 @@ __global__ __launch_bounds__(256) void colsum_kernel(ColsumArgs a) {
   if (lane == 0) a.cs[row] = s;
 }
 
-// One wave per row: {sum, sum of squares} of each 128-column group (16 lanes of 8
-// values each, reduced in a fixed butterfly order). The order of every addition is the
-// one the output GEMM uses for the later layers' rows, so a row's statistics come out
-// bit-identical whichever kernel produced them.
+// One wave per row: {mean, sum of squared deviations from that mean} of each
+// 128-column group (group_stats: 16 lanes of 8 values each). The output GEMM computes
+// the later layers' rows with the same function on the same lane layout, so a row's
+// statistics come out bit-identical whichever kernel produced them.
 __global__ __launch_bounds__(256) void rowstats_kernel(const void* x_lo, const void* x_hi, int Nu, int T, int D, float2* st) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= T) return;
   const u16* x = row < Nu ? (const u16*)x_lo + (size_t)row * D : (const u16*)x_hi + (size_t)(row - Nu) * D;
   for (int c0 = 0; c0 < D / 8; c0 += 64) {          // 64 chunks = 4 groups per pass
     const int c = c0 + lane;
-    float s1 = 0.0f, s2 = 0.0f;
-    if (c < D / 8) {
-      float v[8];
-      load_chunk(x + c * 8, v);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        s1 += v[2 * e] + v[2 * e + 1];
-        s2 = __builtin_fmaf(v[2 * e], v[2 * e], __builtin_fmaf(v[2 * e + 1], v[2 * e + 1], s2));
-      }
-    }
-    s1 = sum16(s1);
-    s2 = sum16(s2);
-    if ((lane & 15) == 0 && c < D / 8) st[(size_t)row * (D / 128) + c / 16] = make_float2(s1, s2);
+    // D is a multiple of 128, so a 16-lane group is either wholly inside the row or
+    // wholly past it; the lanes past it feed zeros and their results are dropped
+    const uint4 q = c < D / 8 ? *reinterpret_cast<const uint4*>(x + c * 8) : make_uint4(0, 0, 0, 0);
+    const float2 g = group_stats(q);
+    if ((lane & 15) == 0 && c < D / 8) st[(size_t)row * (D / 128) + c / 16] = g;
   }
 }
 
@@ -172,8 +197,16 @@ hipError_t launch_norm(int dtype, const NormArgs& a, hipStream_t s) {
 int attn_block_rows(int dtype) { return dtype == HSTU_F32 ? attn_block_rows_f32() : attn_block_rows_bf16(); }
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
-  if (a.T <= 0) return hipSuccess;
-  plan_rows_kernel<<<(a.T + 255) / 256, 256, 0, s>>>(a);
+  const int blocks = (a.T + 255) / 256 + (a.grid + 255) / 256;
+  if (blocks <= 0) return hipSuccess;
+  plan_rows_kernel<<<blocks, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_upload(const UploadArgs& a, hipStream_t s) {
+  if (a.words <= 0) return hipSuccess;
+  if (a.words > kUploadWords) return hipErrorInvalidValue;
+  upload_kernel<<<1, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -43,12 +43,14 @@
  * Conventions for every entry point:
  *  - Host pointers are read during the call only. Device pointers must stay valid
  *    until the work enqueued on `stream` has completed.
- *  - Nothing is allocated on the device by the library; scratch memory is the
- *    caller's workspace. The library keeps a small pinned host staging ring per
- *    device (allocated on first use, grown when a larger plan is needed) from which
- *    the per-call work plan is copied into the workspace.
+ *  - Nothing is allocated on the device or in pinned host memory by the library;
+ *    scratch memory is the caller's workspace. The per-call work plan (a few bytes
+ *    per user and per attention work item) is computed on the host, in host memory
+ *    the calling thread keeps for its next calls, and reaches the workspace inside
+ *    the arguments of small copy kernels, which the runtime captures when they are
+ *    enqueued.
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null
- *    stream). There is no device synchronisation inside a call.
+ *    stream). There is no device or host synchronisation inside a call.
  *  - Every argument is validated on the host before anything is enqueued. On a
  *    validation error nothing is launched and no host array is modified.
  *  - Calls may run concurrently from several host threads if each uses its own
@@ -74,7 +76,8 @@ enum hstu_dtype { HSTU_F32 = 0, HSTU_BF16 = 1 };
 enum hstu_status_code {
   HSTU_OK = 0,
   HSTU_ERR_NULL = 1,       /* a required pointer is NULL                                  */
-  HSTU_ERR_SHAPE = 2,      /* unsupported dims/dtype (see hstu_dims), B < 0                */
+  HSTU_ERR_SHAPE = 2,      /* unsupported dims/dtype (see hstu_dims), B < 0, or a user   */
+                           /* with 2^30 or more history rows or candidates              */
   HSTU_ERR_OFFSETS = 3,    /* offsets do not start at 0 or decrease                        */
   HSTU_ERR_CAPACITY = 4,   /* m+n >= max_len, cache capacity < m+n, bad or repeated slot,   */
                            /* cached_len < 0, or one user's keys of one layer span 2 GiB or */
@@ -88,7 +91,7 @@ typedef int32_t hstu_status;
 
 /* Model dimensions, fixed for a model.
  *  layers  >= 1
- *  d_model  D; heads H with dh = D / H.
+ *  d_model  D; heads H (at most 127) with dh = D / H.
  *           float32:  D % 64 == 0 and dh in {32, 64, 128}
  *           bfloat16: D % 128 == 0 and dh in {64, 128}
  *  max_len  rows of each position-bias table; every user needs m + n + 1 <= max_len

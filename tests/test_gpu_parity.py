@@ -184,15 +184,81 @@ def test_uih_outputs_bit_identical_for_any_candidate_set():
 
 
 def test_zero_query_gives_zero_attention_on_gpu():
-    """Zero Q columns of W1 and the Q slice of the bias table: SiLU(0) = 0, so the attention
-    output vanishes and X1 = bf16(X0 + U W2[0:D]); compared with the oracle's bf16 mirror."""
+    """Zero Q columns of W1 and the Q slice of the bias table: SiLU(0) = 0, so every attention
+    weight and output is exactly 0 and X1 = bf16(X0 + U W2[0:D]). Checked three ways: against
+    the oracle's bf16 mirror; bit for bit against a second run whose W2 rows for O and U*O
+    (rows D..3D) are other random values (exact zeros times anything add nothing); and,
+    with all-zero input rows (then U = 0 too and X1 = bf16(O W2[D:2D])), every output
+    exactly zero."""
+    torch = torch_cuda()
     wl = workloads.make_custom(seed=601, dtype="bf16", layers=1, d_model=256, heads=4, max_len=300,
-                               uih_lengths=[200, 31], cand_lengths=[17, 2])
+                               uih_lengths=[200, 31, 0], cand_lengths=[17, 2, 5])
     D = 256
     wl.params[0].w1[:, 2 * D:3 * D] = 0.0
     wl.params[0].pos[:, D:2 * D] = 0.0
     gu, gc = gpu_encode(wl)
     check(wl, gu, gc, "bf16", BF16_TOL, label="zero-Q")
+    import copy
+    params2 = copy.deepcopy(wl.params)
+    rng = np.random.default_rng(602)
+    params2[0].w2[D:3 * D] = workloads.to_bf16_values(4.0 * rng.standard_normal((2 * D, D)).astype(np.float32))
+    gu2, gc2 = gpu_encode(wl, model=make_model(torch, wl, params2))
+    assert np.array_equal(gu, gu2) and np.array_equal(gc, gc2)
+    zu, zc = np.zeros_like(wl.uih), np.zeros_like(wl.cand)
+    gu0, gc0 = gpu_encode(wl, uih=zu, cand=zc)
+    assert not np.any(gu0) and not np.any(gc0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_large_row_offsets(dtype):
+    """Layer inputs whose rows carry a large common offset (rows of c + N(0, 1), c = 50, 300,
+    1000 and -300 for the four users): the row normalisation must not lose the rows' spread
+    to the offset. Each of two layers runs as a one-layer call on the GPU's own input to
+    that layer (the offset survives the residual, and in bfloat16 a row at 1000 has a
+    spacing of 4 against a spread near 1.5, so a single rounding flip of X + Z upstream
+    would change the next layer's normalised row: the oracle gets the same bits). The
+    cached keys and values of the call are the projection's outputs (normalised input
+    times W1, SiLU, position bias) and are compared with the oracle's; the outputs too
+    (their scale is the offset, so they pin less)."""
+    torch = torch_cuda()
+    import oracle
+    D, H, L = (512, 4, 2) if dtype == "bf16" else (128, 2, 2)
+    offsets = [50.0, 300.0, 1000.0, -300.0]
+    ul, cl = [300, 129, 64, 200], [17, 64, 1, 0]
+    wl = workloads.make_custom(seed=1201, dtype=dtype, layers=L, d_model=D, heads=H, max_len=400,
+                               uih_lengths=ul, cand_lengths=cl)
+    uo, co = workloads.lengths_to_offsets(ul), workloads.lengths_to_offsets(cl)
+    uih = wl.uih.copy()
+    cand = wl.cand.copy()
+    for b, c in enumerate(offsets):
+        uih[uo[b]:uo[b + 1]] += c
+        cand[co[b]:co[b + 1]] += c
+    if dtype == "bf16":
+        uih, cand = workloads.to_bf16_values(uih), workloads.to_bf16_values(cand)
+    mode = "bf16" if dtype == "bf16" else "f64"
+    tol = BF16_TOL if dtype == "bf16" else F32_TOL
+    x_u, x_c = uih.astype(np.float64), cand.astype(np.float64)
+    for l in range(L):
+        model = hsa.Model([wl.params[l]], d_model=D, heads=H, max_len=wl.max_len, dtype=dtype)
+        cache = hsa.KVCache(model, slots=4, capacity=384)
+        cache.cached_len = np.zeros(4, dtype=np.int32)
+        gu, gc = gpu_encode(wl, model=model, uih=x_u, cand=x_c, cache=cache)
+        ocache = oracle.OracleCache(np.zeros((1, 4, 384, D)), np.zeros((1, 4, 384, D)), np.arange(4),
+                                    np.zeros(4, np.int64))
+        ru, rc, ocache = oracle.encode(x_u, uo, x_c, co, [wl.params[l]], heads=H, max_len=wl.max_len, mode=mode,
+                                       cache=ocache)
+        gk, gv = to_np(cache.k), to_np(cache.v)
+        for b in range(4):
+            n = ul[b]
+            ek = float(np.max(np.abs(gk[0, b, :n] - ocache.k[0, b, :n])) / np.max(np.abs(ocache.k[0, b, :n])))
+            ev = float(np.max(np.abs(gv[0, b, :n] - ocache.v[0, b, :n])) / np.max(np.abs(ocache.v[0, b, :n])))
+            say(f"  large row offsets {dtype}, layer {l}, user {b} (offset {offsets[b]}): cached K {ek:.3e} V {ev:.3e}")
+            assert ek <= tol and ev <= tol
+        eu = normwise_per_user(gu, ru, ul)
+        ec = normwise_per_user(gc, rc, cl)
+        say(f"  large row offsets {dtype}, layer {l}: outputs uih {eu:.3e} cand {ec:.3e}")
+        assert eu <= tol and ec <= tol
+        x_u, x_c = gu, gc
 
 
 def test_two_runs_bitwise_identical():

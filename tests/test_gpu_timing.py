@@ -39,7 +39,8 @@ def test_timing_counts_and_bounds(dtype):
     assert st == 0
     L = wl.layers
     norm = 2 if dtype == "bf16" else L          # bf16: row and column sums once per call
-    expect = {"plan": 1, "uvqk": L, "attention": L, "out": L, "norm": norm}
+    # plan: the plan's transfer (its upload kernels, one record) and the plan kernel
+    expect = {"plan": 2, "uvqk": L, "attention": L, "out": L, "norm": norm}
     total = 0.0
     for kind, n in expect.items():
         ms, launches = rec[kind]
