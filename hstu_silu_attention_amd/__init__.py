@@ -19,12 +19,13 @@ import numpy as np
 
 __all__ = ["HSTU_F32", "HSTU_BF16", "HstuError", "load_library", "library_path",
            "hstu_abi_version", "hstu_status_string", "hstu_workspace_size", "hstu_flops",
-           "hstu_encode", "hstu_pack_uih", "hstu_timing_enable", "hstu_timing_select", "hstu_timing_read", "KERNEL_KINDS",
+           "hstu_encode", "hstu_encode_static", "encode_static", "HSTU_ERR_TOO_LARGE", "hstu_pack_uih", "hstu_timing_enable", "hstu_timing_select", "hstu_timing_read", "KERNEL_KINDS",
            "PACK_MODES", "Model", "KVCache", "ScoringHead", "encode", "pack_uih", "score", "hstu_score",
            "HstuDims", "HstuLayerWeights", "HstuKvCache", "HstuHeadLayer", "SlotPool", "POOL_STATS"]
 
 HSTU_F32, HSTU_BF16 = 0, 1
 HSTU_OK = 0
+HSTU_ERR_TOO_LARGE = 8
 KERNEL_KINDS = ("plan", "uvqk", "attention", "out", "norm", "pack", "score")
 PACK_MODES = {"sum": 0, "interleave": 1}
 POOL_STATS = ("hits", "rebuild_new", "rebuild_stale", "rebuild_full", "evictions")
@@ -93,6 +94,10 @@ def load_library() -> ctypes.CDLL:
     lib.hstu_encode.argtypes = [P(HstuDims), ctypes.c_int32, i32p, i32p, ctypes.c_void_p, ctypes.c_void_p,
                                 P(HstuLayerWeights), P(HstuKvCache), ctypes.c_void_p, ctypes.c_void_p,
                                 ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.hstu_encode_static.restype = ctypes.c_int32
+    lib.hstu_encode_static.argtypes = [P(HstuDims), ctypes.c_int32, i32p, i32p, ctypes.c_void_p, ctypes.c_void_p,
+                                       P(HstuLayerWeights), P(HstuKvCache), ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p]
     i64p = P(ctypes.c_int64)
     lib.hstu_pool_create.restype = ctypes.c_int32
     lib.hstu_pool_create.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, P(ctypes.c_void_p)]
@@ -166,6 +171,19 @@ def hstu_encode(dims: HstuDims, B: int, uih_offsets, cand_offsets, uih_ptr: int,
     return int(load_library().hstu_encode(ctypes.byref(dims), B, uo, co, uih_ptr, cand_ptr, warr,
                                           ctypes.byref(kv) if kv is not None else None,
                                           uih_out_ptr, cand_out_ptr, workspace_ptr, workspace_bytes, stream))
+
+
+def hstu_encode_static(dims: HstuDims, B: int, uih_offsets, cand_offsets, uih_ptr: int, cand_ptr: int,
+                       weights: Sequence[HstuLayerWeights], kv: Optional[HstuKvCache], uih_out_ptr: int,
+                       cand_out_ptr: int, stream: int) -> int:
+    """Raw call of the entry point that allocates nothing (its workspace is the library's fixed
+    device array). Returns the status."""
+    _, uo = _i32(uih_offsets)
+    _, co = _i32(cand_offsets)
+    warr = (HstuLayerWeights * max(len(weights), 1))(*weights)
+    return int(load_library().hstu_encode_static(ctypes.byref(dims), B, uo, co, uih_ptr, cand_ptr, warr,
+                                                 ctypes.byref(kv) if kv is not None else None,
+                                                 uih_out_ptr, cand_out_ptr, stream))
 
 
 def hstu_pack_uih(dims: HstuDims, events: int, mode: int, context_ptr: int, action_ptr: int,
@@ -285,6 +303,25 @@ def encode(model: Model, uih, uih_offsets, cand, cand_offsets, *, cache: Optiona
                      workspace.numel(), stream)
     if st != HSTU_OK:
         raise HstuError(st, "hstu_encode")
+    return out
+
+
+def encode_static(model: Model, uih, uih_offsets, cand, cand_offsets, *, cache: Optional[KVCache] = None,
+                  out: Optional[Tuple] = None, stream=None):
+    """Run hstu_encode_static (no workspace: the library's fixed device scratch, for callers that
+    cannot allocate) on the current (or given) stream; returns (uih_out, cand_out). Outputs are
+    allocated here unless ``out`` is given. Calls that overlap on one GPU race (one scratch)."""
+    torch = _torch()
+    B = len(uih_offsets) - 1
+    if out is None:
+        out = (torch.empty_like(uih), torch.empty_like(cand))
+    if stream is None:
+        stream = torch.cuda.current_stream(uih.device).cuda_stream
+    kv = cache.struct() if cache is not None else None
+    st = hstu_encode_static(model.dims(), B, uih_offsets, cand_offsets, uih.data_ptr(), cand.data_ptr(),
+                            model.weights, kv, out[0].data_ptr(), out[1].data_ptr(), stream)
+    if st != HSTU_OK:
+        raise HstuError(st, "hstu_encode_static")
     return out
 
 

@@ -340,8 +340,12 @@ hstu_status validate_encode(EncodeCall& c, int32_t* keys) {
 }
 
 // Plans the call in `ps` and enqueues it on stream s with workspace ws (a validated call
-// with T > 0 and a workspace of c.lay.total bytes).
-hstu_status run_encode(const EncodeCall& c, const PlanSpace& ps, char* ws, hipStream_t s) {
+// with T > 0 and a workspace of c.lay.total bytes). With `timed` false the timing aid is
+// bypassed (it creates events while it is on).
+hstu_status run_encode(const EncodeCall& c, const PlanSpace& ps, char* ws, hipStream_t s, bool timed = true) {
+  auto timed_launch = [timed](int kind, hipStream_t st, auto&& f) -> hipError_t {
+    return timed ? ::timed_launch(kind, st, f) : f();
+  };
   const hstu_dims* d = c.d;
   const Layout& lay = c.lay;
   const hstu_kv_cache* kv = c.kv;
@@ -450,6 +454,42 @@ hstu_status run_encode(const EncodeCall& c, const PlanSpace& ps, char* ws, hipSt
   return HSTU_OK;
 }
 
+// ---------------------------------------------------------------- no-allocation entry point
+// hstu_encode_static: hstu_encode with the workspace in a fixed device array and the
+// planner in fixed host arrays, for callers that cannot allocate. The array is a
+// file-scope device variable: each GPU that runs the entry point holds its own copy
+// until the process ends. Its device address on a device comes from
+// hipGetSymbolAddress, taken once per device with that device current; host code uses
+// only that address (the variable's name in host code is a host-side stand-in).
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+constexpr int32_t kStaticMaxUsers = 1024;
+constexpr int64_t kStaticMaxItems = 16384;       // attention work items (and so groups)
+constexpr size_t kStaticImageBytes = 256 * 1024 + (size_t)hstu::kXcds * kStaticMaxItems * sizeof(hstu::ItemCode);
+constexpr int kMaxDevices = 64;
+
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+std::mutex g_static_mu;                          // the host arrays below and g_scratch_ptr
+void* g_scratch_ptr[kMaxDevices] = {};
+PlanGroup g_static_groups[kStaticMaxItems];
+PlanItem g_static_items[kStaticMaxItems];
+alignas(256) unsigned char g_static_image[kStaticImageBytes];
+int32_t g_static_keys[kStaticMaxUsers];
+
+// The current device's copy of `scratch` (looked up on the device's first call).
+hstu_status static_scratch(char** ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return HSTU_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return HSTU_ERR_HIP;
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return HSTU_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = static_cast<char*>(g_scratch_ptr[dev]);
+  return HSTU_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -515,6 +555,7 @@ const char* hstu_status_string(hstu_status s) {
     case HSTU_ERR_WORKSPACE: return "workspace missing or smaller than hstu_workspace_size()";
     case HSTU_ERR_HIP: return "a HIP runtime call failed";
     case HSTU_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+    case HSTU_ERR_TOO_LARGE: return "batch too large for hstu_encode_static's fixed scratch (use hstu_encode)";
     default: return "unknown status";
   }
 }
@@ -572,6 +613,29 @@ hstu_status hstu_encode(const hstu_dims* d, int32_t B, const int32_t* uih_offset
   if (!workspace || workspace_bytes < c.lay.total) return HSTU_ERR_WORKSPACE;
   if (((uintptr_t)workspace & (kAlign - 1)) != 0) return HSTU_ERR_ALIGN;
   return run_encode(c, ps, static_cast<char*>(workspace), reinterpret_cast<hipStream_t>(stream));
+}
+
+hstu_status hstu_encode_static(const hstu_dims* d, int32_t B, const int32_t* uih_offsets,
+                               const int32_t* cand_offsets, const void* uih, const void* cand,
+                               const hstu_layer_weights* w, hstu_kv_cache* kv, void* uih_out, void* cand_out,
+                               void* stream) {
+  hstu_status st = check_dims(d);
+  if (st != HSTU_OK) return st;
+  st = check_offsets(B, uih_offsets, cand_offsets);
+  if (st != HSTU_OK) return st;
+  EncodeCall c{d, B, uih_offsets, cand_offsets, uih, cand, w, kv, uih_out, cand_out,
+               make_layout(d, B, uih_offsets, cand_offsets)};
+  if (B > kStaticMaxUsers || c.lay.ntiles > kStaticMaxItems || c.lay.staged > kStaticImageBytes ||
+      c.lay.total > kStaticScratchBytes)
+    return HSTU_ERR_TOO_LARGE;
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  st = validate_encode(c, g_static_keys);
+  if (st != HSTU_OK || c.lay.T == 0) return st;
+  char* ws = nullptr;
+  st = static_scratch(&ws);
+  if (st != HSTU_OK) return st;
+  return run_encode(c, PlanSpace{g_static_groups, g_static_items, g_static_image, g_static_keys}, ws,
+                    reinterpret_cast<hipStream_t>(stream), false);
 }
 
 hstu_status hstu_pack_uih(const hstu_dims* d, int32_t events, int32_t mode, const void* context,

@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 5
+#define HSTU_ABI_VERSION 6
 
 /* Element type of every device tensor of a call. */
 enum hstu_dtype { HSTU_F32 = 0, HSTU_BF16 = 1 };
@@ -85,7 +85,8 @@ enum hstu_status_code {
                            /* a cache, 3D without)                                          */
   HSTU_ERR_WORKSPACE = 5,  /* workspace NULL or smaller than hstu_workspace_size()          */
   HSTU_ERR_HIP = 6,        /* a HIP runtime call failed; outputs and cache are undefined    */
-  HSTU_ERR_ALIGN = 7       /* a device pointer is not 16-byte aligned                       */
+  HSTU_ERR_ALIGN = 7,      /* a device pointer is not 16-byte aligned                       */
+  HSTU_ERR_TOO_LARGE = 8   /* hstu_encode_static: the batch exceeds its fixed scratch       */
 };
 typedef int32_t hstu_status;
 
@@ -182,6 +183,29 @@ hstu_status hstu_encode(const hstu_dims* d, int32_t B, const int32_t* uih_offset
                         const int32_t* cand_offsets, const void* uih, const void* cand,
                         const hstu_layer_weights* w, hstu_kv_cache* kv, void* uih_out,
                         void* cand_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* hstu_encode for callers that cannot allocate (code under HIP graph capture, serving
+ * loops, harnesses that forbid allocation): the same arguments without the workspace,
+ * the same plan, kernels and results (bit for bit). It calls no hipMalloc, hipFree or
+ * other allocating routine, on the device or the host, and never records timing events.
+ *  - Its workspace is a fixed device array of 64 MiB in the library (file-scope, one copy
+ *    per GPU, held from the GPU's first call until the process ends); the planner works
+ *    in fixed host arrays. Batches whose workspace (hstu_workspace_size) exceeds 64 MiB,
+ *    with more than 1024 users or more than 16384 attention work items (per head,
+ *    ceil(n_b/128) + ceil(c_b/128) summed over users, bfloat16; 64-row items in float32)
+ *    are rejected with HSTU_ERR_TOO_LARGE before anything is enqueued. 64 MiB holds about
+ *    9000 rows (history plus candidates) at D = 512 in bfloat16.
+ *  - Every call on one GPU shares that GPU's array, and a later call overwrites what an
+ *    earlier one left there: calls that overlap on one GPU (concurrent streams, or host
+ *    threads with different streams) race, so the caller orders them (e.g. one stream).
+ *    Host threads are serialised around the planning inside the call.
+ *  - The stream must belong to the current device. Errors as hstu_encode, plus
+ *    HSTU_ERR_TOO_LARGE; HSTU_ERR_HIP also when the array's device address cannot be
+ *    looked up. */
+hstu_status hstu_encode_static(const hstu_dims* d, int32_t B, const int32_t* uih_offsets,
+                               const int32_t* cand_offsets, const void* uih, const void* cand,
+                               const hstu_layer_weights* w, hstu_kv_cache* kv, void* uih_out, void* cand_out,
+                               void* stream);
 
 /* History tokens from per-event context and action embeddings: the two input forms
  * of the DLRMv3 page's action-embedding paragraph (section "Model selection"). The

@@ -16,7 +16,7 @@ import workloads
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "hstu.h")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_OFFSETS, ERR_CAPACITY, ERR_WORKSPACE, ERR_HIP, ERR_ALIGN = range(8)
+OK, ERR_NULL, ERR_SHAPE, ERR_OFFSETS, ERR_CAPACITY, ERR_WORKSPACE, ERR_HIP, ERR_ALIGN, ERR_TOO_LARGE = range(9)
 
 
 def header_functions():
@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     assert {"hstu_abi_version", "hstu_status_string", "hstu_workspace_size", "hstu_flops", "hstu_encode",
             "hstu_pack_uih", "hstu_score", "hstu_pool_create", "hstu_pool_destroy", "hstu_pool_assign",
             "hstu_pool_commit", "hstu_pool_abort", "hstu_pool_stats", "hstu_pool_lookup", "hstu_timing_enable",
-            "hstu_timing_select", "hstu_timing_read"} <= set(names)
+            "hstu_timing_select", "hstu_timing_read", "hstu_encode_static"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
     version = int(re.search(r"#define HSTU_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     seen = set()
-    for s in range(8):
+    for s in range(9):
         msg = hsa.hstu_status_string(s)
         assert msg and msg not in seen
         seen.add(msg)
@@ -315,3 +315,22 @@ def test_missing_library_fails_loudly(tmp_path):
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "build the HIP library" in r.stdout
+
+
+def test_static_entry_rejects_batches_beyond_its_scratch():
+    """hstu_encode_static (no workspace argument, a fixed device scratch) refuses, before
+    touching the GPU, batches whose workspace exceeds its 64 MiB or whose plan exceeds its
+    fixed host arrays (1024 users, 16384 attention work items); validation errors come
+    first, as in hstu_encode."""
+    fake = 1 << 20                      # never dereferenced: the call returns before any launch
+    d = dims(L=1, D=512, H=4, max_len=20000)
+    w = (hsa.HstuLayerWeights * 1)(hsa.HstuLayerWeights(fake, fake, None, None))
+
+    def call(uo, co, d=d):
+        return hsa.hstu_encode_static(d, len(uo) - 1, uo, co, fake, fake, w, None, fake, fake, 0)
+
+    assert call([0, 16000], [0, 2048]) == ERR_TOO_LARGE                   # 18K rows at D = 512
+    many = list(range(0, 1026))                                           # 1025 users of one row
+    assert call(many, [0] * 1026, d=dims(L=1, D=128, H=2, max_len=20000)) == ERR_TOO_LARGE
+    assert call([3, 5], [0, 2]) == ERR_OFFSETS
+    assert hsa.hstu_encode_static(d, 0, None, None, None, None, w, None, None, None, 0) == OK
