@@ -293,10 +293,15 @@ def encode(model: Model, uih, uih_offsets, cand, cand_offsets, *, cache: Optiona
     if out is None:
         out = (torch.empty_like(uih), torch.empty_like(cand))
     nbytes = workspace_bytes(model, uih_offsets, cand_offsets)
-    if workspace is None or workspace.numel() < nbytes:
+    own_workspace = workspace is None or workspace.numel() < nbytes
+    if own_workspace:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=uih.device)
     if stream is None:
         stream = torch.cuda.current_stream(uih.device).cuda_stream
+    elif own_workspace and stream != torch.cuda.current_stream(uih.device).cuda_stream:
+        # the workspace was allocated on the current stream but is used on `stream`: keep
+        # the caching allocator from handing it out again before that stream's work ends
+        workspace.record_stream(torch.cuda.ExternalStream(stream, device=uih.device))
     kv = cache.struct() if cache is not None else None
     st = hstu_encode(model.dims(), B, uih_offsets, cand_offsets, uih.data_ptr(), cand.data_ptr(),
                      model.weights, kv, out[0].data_ptr(), out[1].data_ptr(), workspace.data_ptr(),
