@@ -180,13 +180,15 @@ def cpu_baseline(wl, min_seconds: float = 10.0):
                       f"float64 with bf16-mirror rounding; {dt:.1f} s; {len(done) / dt:.4f} users/s on this host"}
 
 
-def replay_bench(args, slots=160, capacity=4096, ttl=300, window=3072, batch_users=16, cand_sets=16):
+def replay_bench(args, pages=10240, max_rows=4096, ttl=300, window=3072, batch_users=16, cand_sets=16):
     """Streaming replay: 2048 requests from 192 drawn users in time order (first visit with a
     lognormal history, then 16-128 new events per visit, 2048 candidates per request), served
-    in batches of up to 16 distinct users through the slot pool and a 160-slot cache of
-    4096 rows (fewer slots than users: the least recently served are evicted). Histories are host bf16 rows (a request's new events, or its latest 3072
-    events when the pool says to encode again, cross PCIe per batch); candidate rows come
-    from 16 device-resident sets reused in turn. One untimed pass over the first 64
+    in batches of up to 16 distinct users through the page pool and a paged cache of 10240
+    pages of 64 rows (655K rows, the memory of 160 users at 4096 rows; a user holds
+    ceil(rows / 64) pages, at most 4096 rows; when pages run out the least recently served
+    users are evicted). Histories are host bf16 rows (a request's new events, or its latest
+    3072 events when the pool says to encode again, cross PCIe per batch); candidate rows
+    come from 16 device-resident sets reused in turn. One untimed pass over the first 64
     requests warms up; the timed pass replays all requests from an empty pool."""
     import torch
     from hstu_silu_attention_amd.replay import Replayer, Request
@@ -197,10 +199,11 @@ def replay_bench(args, slots=160, capacity=4096, ttl=300, window=3072, batch_use
     hist = {u: torch.from_numpy(h).to(torch.bfloat16) for u, h in rs.history.items()}
     sets = [torch.from_numpy(rs.candidates(i)).to(device=dev, dtype=torch.bfloat16) for i in range(cand_sets)]
     reqs = [Request(t, u, e, sets[i % cand_sets]) for i, (t, u, e, _) in enumerate(rs.requests)]
-    cache = hsa.KVCache(model, slots=slots, capacity=capacity, device=dev)
+    ppu = (max_rows + hsa.PAGE_ROWS - 1) // hsa.PAGE_ROWS
+    cache = hsa.PagedKVCache(model, pages=pages, pages_per_user=ppu, max_users=batch_users, device=dev)
 
     def run(requests):
-        pool = hsa.SlotPool(slots, capacity, ttl)
+        pool = hsa.KvPool(pages, max_rows, ttl)
         rep = Replayer(model, cache, pool, hist, window=window, device=dev, keep_outputs=False)
         for b in rep.batches_of(requests, batch_users):
             rep.serve(b)
@@ -213,15 +216,20 @@ def replay_bench(args, slots=160, capacity=4096, ttl=300, window=3072, batch_use
     rep, pool = run(reqs)
     dt = time.perf_counter() - t0
     stats = pool.stats()
+    held = [pool.lookup(u) for u in rs.history]
+    held_rows, held_pages = sum(n for n, _ in held), sum(p for _, p in held)
     print(json.dumps({
         "metric": "HSTU streaming replay requests/s (2K candidates per request)",
         "value": round(len(reqs) / dt, 2), "unit": "requests/s", "n_gpus": 1, "higher_is_better": True,
         "dtype": "bf16", "data": "synthetic (seeded replay stream)",
         "config": {"workload": "replay_192u_2048r_c2k", "users": len(rs.history), "requests": len(reqs),
-                   "batch_users": batch_users, "slots": slots, "capacity": capacity, "ttl": ttl, "window": window,
+                   "batch_users": batch_users, "pages": pages, "page_rows": hsa.PAGE_ROWS, "max_rows": max_rows,
+                   "ttl": ttl, "window": window,
                    "layers": wl.layers, "d_model": wl.d_model, "heads": wl.heads},
         "seconds": round(dt, 3), "batches": rep.batches, "tflops": round(rep.flops / dt / 1e12, 3),
         "history_rows_sent": rep.rows_sent, "history_rows_without_cache": rep.rows_no_cache, "pool": stats,
+        "rows_held_end": held_rows, "pages_held_end": held_pages,
+        "page_fill_end": round(held_rows / max(held_pages * hsa.PAGE_ROWS, 1), 4),
         "flops_saved_by_cache": round(1.0 - rep.flops / max(rep.flops_no_cache, 1), 4),
     }), flush=True)
 
@@ -237,7 +245,11 @@ def main():
     ap.add_argument("--workload", default="d512_uih2k_c2k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--replay", action="store_true",
-                    help="time-ordered streaming replay (slot pool + cache) instead of the batch encode")
+                    help="time-ordered streaming replay (page pool + paged cache) instead of the batch encode")
+    ap.add_argument("--paged", choices=("shuffled", "ordered"), default=None,
+                    help="workloads with a cached prefix: keep it in a paged cache of 64-row pages instead "
+                         "of one slot per user, the page ids a random permutation of the pool (shuffled) "
+                         "or each user's pages consecutive (ordered)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (to scale the HBM "
                          "byte counters of a profiler run) and exit")
@@ -292,7 +304,15 @@ def main():
         # candidates); every step then encodes the new events and the candidates against
         # it, with the cached lengths reset first, so each step rewrites the same rows
         cap = int((wl.cached_lengths + wl.uih_lengths).max())
-        cache = hsa.KVCache(model, slots=wl.users, capacity=cap, device=dev)
+        if args.paged:
+            ppu = (cap + hsa.PAGE_ROWS - 1) // hsa.PAGE_ROWS
+            cache = hsa.PagedKVCache(model, pages=wl.users * ppu, pages_per_user=ppu, max_users=wl.users, device=dev)
+            ids = np.arange(wl.users * ppu).reshape(wl.users, ppu)
+            if args.paged == "shuffled":
+                ids = np.random.default_rng(0).permutation(wl.users * ppu).reshape(wl.users, ppu)
+            cache.set_table(ids)
+        else:
+            cache = hsa.KVCache(model, slots=wl.users, capacity=cap, device=dev)
         po = workloads.lengths_to_offsets(wl.cached_lengths)
         hsa.encode(model, bf(wl.prefix), po, cand[:0], np.zeros(wl.users + 1, np.int32), cache=cache)
         torch.cuda.synchronize()
@@ -402,7 +422,9 @@ def main():
                 "N(0,0.02) position bias)" + ("" if wl.packing == "none" else
                                               "; N(0,1) context and action embeddings per event"),
         "config": {"workload": args.workload, "users": wl.users, "layers": wl.layers,
-                   **({"cached_per_user": int(wl.cached_lengths[0])} if cache is not None else {}),
+                   **({"cached_per_user": int(wl.cached_lengths[0]),
+                       "cache_layout": f"paged (64-row pages, {args.paged} ids)" if args.paged else "slot"}
+                    if cache is not None else {}),
                    "d_model": wl.d_model, "heads": wl.heads, "cands_per_user": int(wl.cand_lengths[0]),
                    "uih_mean": float(token_lengths(wl).mean()),
                    "rows": int(token_lengths(wl).sum() + wl.cand_lengths.sum()),

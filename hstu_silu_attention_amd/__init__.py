@@ -6,8 +6,9 @@ fallback: if the library is missing or fails to load, every call raises.
 
 Low-level functions carry the C names (``hstu_encode``, ``hstu_pack_uih``,
 ``hstu_score``, ``hstu_workspace_size``, ``hstu_flops``, ``hstu_abi_version``,
-``hstu_status_string``). ``Model``, ``KVCache``, ``ScoringHead``, ``encode``,
-``pack_uih`` and ``score`` wrap them for torch tensors.
+``hstu_status_string``). ``Model``, ``KVCache`` (slot layout), ``PagedKVCache``,
+``ScoringHead``, ``encode``, ``encode_static``, ``pack_uih`` and ``score`` wrap them for
+torch tensors; ``KvPool`` wraps the host-side page manager (hstu_pool_*).
 """
 from __future__ import annotations
 
@@ -21,14 +22,16 @@ __all__ = ["HSTU_F32", "HSTU_BF16", "HstuError", "load_library", "library_path",
            "hstu_abi_version", "hstu_status_string", "hstu_workspace_size", "hstu_flops",
            "hstu_encode", "hstu_encode_static", "encode_static", "HSTU_ERR_TOO_LARGE", "hstu_pack_uih", "hstu_timing_enable", "hstu_timing_select", "hstu_timing_read", "KERNEL_KINDS",
            "PACK_MODES", "Model", "KVCache", "ScoringHead", "encode", "pack_uih", "score", "hstu_score",
-           "HstuDims", "HstuLayerWeights", "HstuKvCache", "HstuHeadLayer", "SlotPool", "POOL_STATS"]
+           "HstuDims", "HstuLayerWeights", "HstuKvCache", "HstuHeadLayer", "KvPool", "PagedKVCache", "POOL_STATS",
+           "PAGE_ROWS"]
 
 HSTU_F32, HSTU_BF16 = 0, 1
 HSTU_OK = 0
 HSTU_ERR_TOO_LARGE = 8
 KERNEL_KINDS = ("plan", "uvqk", "attention", "out", "norm", "pack", "score")
 PACK_MODES = {"sum": 0, "interleave": 1}
-POOL_STATS = ("hits", "rebuild_new", "rebuild_stale", "rebuild_full", "evictions")
+POOL_STATS = ("hits", "rebuild_new", "rebuild_stale", "rebuild_full", "evictions", "pages_in_use", "pages_peak")
+PAGE_ROWS = 64
 
 
 class HstuDims(ctypes.Structure):
@@ -44,7 +47,8 @@ class HstuLayerWeights(ctypes.Structure):
 class HstuKvCache(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("slots", ctypes.c_int32),
                 ("capacity", ctypes.c_int32), ("slot_of_user", ctypes.POINTER(ctypes.c_int32)),
-                ("cached_len", ctypes.POINTER(ctypes.c_int32))]
+                ("cached_len", ctypes.POINTER(ctypes.c_int32)), ("page_rows", ctypes.c_int32),
+                ("pages", ctypes.c_int32), ("pages_per_user", ctypes.c_int32), ("page_table", ctypes.c_void_p)]
 
 
 class HstuHeadLayer(ctypes.Structure):
@@ -104,7 +108,8 @@ def load_library() -> ctypes.CDLL:
     lib.hstu_pool_destroy.restype = None
     lib.hstu_pool_destroy.argtypes = [ctypes.c_void_p]
     lib.hstu_pool_assign.restype = ctypes.c_int32
-    lib.hstu_pool_assign.argtypes = [ctypes.c_void_p, ctypes.c_int32, i64p, i32p, ctypes.c_int64, i32p, i32p, i32p]
+    lib.hstu_pool_assign.argtypes = [ctypes.c_void_p, ctypes.c_int32, i64p, i32p, i32p, ctypes.c_int64, ctypes.c_int32,
+                                     i32p, i32p, i32p]
     lib.hstu_pool_commit.restype = ctypes.c_int32
     lib.hstu_pool_commit.argtypes = [ctypes.c_void_p, ctypes.c_int32, i64p, i32p, ctypes.c_int64]
     lib.hstu_pool_abort.restype = ctypes.c_int32
@@ -270,7 +275,37 @@ class KVCache:
         self.cached_len = np.ascontiguousarray(self.cached_len, dtype=np.int32)
         return HstuKvCache(self.k.data_ptr(), self.v.data_ptr(), self.slots, self.capacity,
                            self.slot_of_user.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
-                           self.cached_len.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+                           self.cached_len.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 0, 0, 0, None)
+
+
+class PagedKVCache:
+    """Caller-owned paged cache: k, v [layers][pages][64][D] on the device, the device page
+    table [max_users][pages_per_user] int32 (row b: user b of the next call) and host int32
+    ``cached_len`` per user of the next call. ``set_table`` copies host rows into the device
+    table on the current stream."""
+
+    def __init__(self, model: Model, pages: int, pages_per_user: int, max_users: int, device="cuda"):
+        torch = _torch()
+        L, D = len(model.layers), model.d_model
+        self.k = torch.zeros((L, pages, PAGE_ROWS, D), dtype=model.torch_dtype, device=device)
+        self.v = torch.zeros((L, pages, PAGE_ROWS, D), dtype=model.torch_dtype, device=device)
+        self.pages, self.pages_per_user, self.max_users = pages, pages_per_user, max_users
+        self.table = torch.full((max_users, pages_per_user), -1, dtype=torch.int32, device=device)
+        self.cached_len = np.zeros(max_users, dtype=np.int32)
+
+    def set_table(self, rows) -> None:
+        """Rows 0..B-1 of the device page table from a host int array [B][pages_per_user]."""
+        torch = _torch()
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
+        if rows.ndim != 2 or rows.shape[1] != self.pages_per_user or rows.shape[0] > self.max_users:
+            raise ValueError("page table rows must be [B <= max_users][pages_per_user]")
+        self.table[:rows.shape[0]].copy_(torch.from_numpy(rows), non_blocking=False)
+
+    def struct(self) -> HstuKvCache:
+        self.cached_len = np.ascontiguousarray(self.cached_len, dtype=np.int32)
+        return HstuKvCache(self.k.data_ptr(), self.v.data_ptr(), 0, 0, None,
+                           self.cached_len.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), PAGE_ROWS,
+                           self.pages, self.pages_per_user, self.table.data_ptr())
 
 
 def workspace_bytes(model: Model, uih_offsets, cand_offsets) -> int:
@@ -384,17 +419,18 @@ def score(model: Model, head: ScoringHead, x, *, out=None, stream=None):
     return out
 
 
-class SlotPool:
-    """The library's host-side slot manager (hstu_pool_*): which cache slot each user of a
-    batch gets and whether its cached rows are extended or its history is sent again."""
+class KvPool:
+    """The library's host-side page manager of a paged cache (hstu_pool_*): per request whether
+    a user's cached rows are extended or its history is sent again, and which pages hold the
+    user's rows."""
 
-    def __init__(self, slots: int, capacity: int, ttl: int):
+    def __init__(self, pages: int, max_rows: int, ttl: int):
         self._lib = load_library()
         self._h = ctypes.c_void_p()
-        st = int(self._lib.hstu_pool_create(slots, capacity, ttl, ctypes.byref(self._h)))
+        st = int(self._lib.hstu_pool_create(pages, max_rows, ttl, ctypes.byref(self._h)))
         if st != HSTU_OK:
             raise HstuError(st, "hstu_pool_create")
-        self.slots, self.capacity, self.ttl = slots, capacity, ttl
+        self.pages, self.max_rows, self.ttl = pages, max_rows, ttl
 
     def __del__(self):
         if getattr(self, "_h", None) and self._h.value:
@@ -406,21 +442,25 @@ class SlotPool:
         arr = np.ascontiguousarray(np.asarray(a, dtype=np.int64))
         return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
 
-    def assign_raw(self, users, new_events, now: int):
-        """Returns (status, slot_of_user, cached_len, rebuild) as int32 arrays."""
+    def assign_raw(self, users, new_events, window, now: int, pages_per_user: int):
+        """Returns (status, page_table [B][pages_per_user], cached_len, rebuild) as int32 arrays."""
         B = len(users)
         ua, up = self._i64(users)
         na, np_ = _i32(new_events)
-        outs = [np.full(B, -7, dtype=np.int32) for _ in range(3)]
-        ptrs = [o.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) for o in outs]
-        st = int(self._lib.hstu_pool_assign(self._h, B, up if B else None, np_ if B else None, int(now), *ptrs))
-        return (st, *outs)
+        wa, wp = _i32(window)
+        table = np.full((B, max(pages_per_user, 1)), -7, dtype=np.int32)
+        outs = [np.full(B, -7, dtype=np.int32) for _ in range(2)]
+        ptr = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        st = int(self._lib.hstu_pool_assign(self._h, B, up if B else None, np_ if B else None, wp if B else None,
+                                            int(now), int(pages_per_user), ptr(table), ptr(outs[0]),
+                                            ptr(outs[1])))
+        return (st, table, *outs)
 
-    def assign(self, users, new_events, now: int):
-        st, slot, cached, rebuild = self.assign_raw(users, new_events, now)
+    def assign(self, users, new_events, window, now: int, pages_per_user: int):
+        st, table, cached, rebuild = self.assign_raw(users, new_events, window, now, pages_per_user)
         if st != HSTU_OK:
             raise HstuError(st, "hstu_pool_assign")
-        return slot, cached, rebuild
+        return table, cached, rebuild
 
     def commit_raw(self, users, total_len, now: int) -> int:
         ua, up = self._i64(users)
@@ -446,8 +486,9 @@ class SlotPool:
         return {k: int(out[i]) for i, k in enumerate(POOL_STATS)}
 
     def lookup(self, user: int):
-        slot, n = ctypes.c_int32(0), ctypes.c_int32(0)
-        st = int(self._lib.hstu_pool_lookup(self._h, int(user), ctypes.byref(slot), ctypes.byref(n)))
+        """(committed rows, pages held) of a user; (0, 0) if absent."""
+        n, pages = ctypes.c_int32(0), ctypes.c_int32(0)
+        st = int(self._lib.hstu_pool_lookup(self._h, int(user), ctypes.byref(n), ctypes.byref(pages)))
         if st != HSTU_OK:
             raise HstuError(st, "hstu_pool_lookup")
-        return int(slot.value), int(n.value)
+        return int(n.value), int(pages.value)

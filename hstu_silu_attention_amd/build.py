@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libhstu.so")
-SOURCES = ["hstu_abi.hip", "launch.hip", "gemm_bf16.hip", "attn_bf16.hip", "kernels_f32.hip", "pack.hip", "score.hip", "slot_pool.cpp"]
+SOURCES = ["hstu_abi.hip", "launch.hip", "gemm_bf16.hip", "attn_bf16.hip", "kernels_f32.hip", "pack.hip", "score.hip", "kv_pool.cpp"]
 ARCH = "gfx950"
 
 

@@ -66,6 +66,7 @@ struct AttnTile {
 constexpr uint32_t kBufferWord3 = 0x00020000u;   // raw buffer, 32-bit data format
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(4))) int32_t const_i32;
 
 // Raw buffer descriptor: base address, no stride, num_records bytes (loads at or past
 // it return zero).
@@ -113,7 +114,13 @@ static_assert(kTabPad + ((kRelMaxLen + 32 + 7 + 7) / 8 + 63) / 64 * 512 <= kTabE
 // dh = 64 fits three waves per SIMD (under 168 registers; 32 KB of K/V slots, 48 KB with
 // a relative table, per workgroup), which hides more of each wave's latency; dh = 128
 // needs two (233 registers, 64 KB).
-template <int DH, bool REL>
+//
+// Paged cache (PAGED): key r of the user lives in row r % 64 of page pages[key_row + r / 64]
+// of the layer's pool. The buffer range is then the whole pool, and each DMA lane takes its
+// row's page from the pair of page ids that a block of 64 consecutive keys can touch; the
+// pair is read (wave-uniform) one block ahead. A key outside [0, key_end), or an id
+// outside the pool, gets an offset past the range and reads as zero.
+template <int DH, bool REL, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DH == 64 ? 3 : 2, DH == 64 ? 3 : 2)))
 void attn_kernel(AttnArgs a) {
   using C = AttnTile<DH>;
@@ -160,9 +167,24 @@ void attn_kernel(AttnArgs a) {
   // key row r of this user and head at byte offset 2 * (r * ld + col) of the resource;
   // rows outside [0, key_end) read as zero
   const int ld = (int)a.ld;
-  const int nbytes = key_end * ld * 2;
-  const i32x4 rk_src = buffer_desc((const u16*)a.kbase + (size_t)it.key_row * a.ld + head * DH, nbytes);
-  const i32x4 rv_src = buffer_desc((const u16*)a.vbase + (size_t)it.key_row * a.ld + head * DH, nbytes);
+  const int nbytes = PAGED ? a.npages * kPageRows * ld * 2 : key_end * ld * 2;
+  const size_t row0 = PAGED ? 0 : (size_t)it.key_row;
+  const i32x4 rk_src = buffer_desc((const u16*)a.kbase + row0 * a.ld + head * DH, nbytes);
+  const i32x4 rv_src = buffer_desc((const u16*)a.vbase + row0 * a.ld + head * DH, nbytes);
+  // PAGED: the ids of the pages holding keys key0 .. key0 + 63 (the 64-row chunks
+  // floor(key0 / 64) and the next, clamped to the user's npg pages). Branch-free: a user
+  // with no keys reads entry 0 of its table row (in bounds; every key is masked anyway).
+  // The table is read through the constant address space: wave-uniform addresses there
+  // become scalar loads, which count on lgkmcnt. (Vector loads would count on vmcnt, and
+  // the wait for them would also wait for the K/V loads meant to stay in flight until
+  // the block's barrier.)
+  const int last_pg = max((key_end + kPageRows - 1) / kPageRows - 1, 0);
+  const const_i32* tbl = (const const_i32*)(a.pages + it.key_row);
+  auto page_pair = [&](int key0) -> int2 {
+    if (!PAGED) return make_int2(-1, -1);
+    const int c0 = key0 >> 6;
+    return make_int2(tbl[min(max(c0, 0), last_pg)], tbl[min(max(c0 + 1, 0), last_pg)]);
+  };
   // relative bias table of this head, read from the 16-byte-aligned address at or before it
   int mis = 0, tab_chunks = 0;
   i32x4 rel_src = {0, 0, 0, 0};
@@ -178,20 +200,32 @@ void attn_kernel(AttnArgs a) {
 
   // 64-lane LDS loads: load j of a region covers rows RPI*j.. of it; lane i brings the
   // global chunk that belongs at row RPI*j + i/CPR, slot i%CPR
-  auto lds_rows = [&](const i32x4& src, u16* dst, int key0, int j, bool is_v) {
+  auto lds_rows = [&](const i32x4& src, u16* dst, int key0, int j, bool is_v, int2 pp) {
     const int r = C::RPI * j + lane / C::CPR, slot = lane % C::CPR;
     const int chunk = slot ^ (is_v ? v_swz<DH>(r) : k_swz<DH>(r));
     const uint32_t addr = (uint32_t)(uintptr_t)(lds_void*)(dst + j * 512);
-    lds_load16(src, __builtin_amdgcn_readfirstlane(addr), ((key0 + r) * ld + chunk * 8) * 2);
+    int voff = ((key0 + r) * ld + chunk * 8) * 2;
+    if (PAGED) {
+      // branch-free (a branch here would split the loop body): unsigned arithmetic, and a
+      // mask instead of a short-circuit test; an invalid key or page gets offset 2^31,
+      // past any pool of under 2 GiB
+      const int key = key0 + r;
+      const unsigned pg = (unsigned)((key >> 6) == (key0 >> 6) ? pp.x : pp.y);
+      const unsigned ok = (unsigned)((unsigned)key < (unsigned)key_end) & (unsigned)(pg < (unsigned)a.npages);
+      const unsigned off = ((pg * kPageRows + ((unsigned)key & (kPageRows - 1))) * (unsigned)ld + chunk * 8u) * 2u;
+      voff = (int)((off & (0u - ok)) | ((ok ^ 1u) << 31));
+    }
+    lds_load16(src, __builtin_amdgcn_readfirstlane(addr), voff);
   };
-  auto load_k = [&](u16* slot, int blk) {
+  auto load_k = [&](u16* slot, int blk, int2 pp) {
 #pragma unroll
-    for (int i = 0; i < C::IPW; ++i) lds_rows(rk_src, slot, blk * C::KB - shift, wv + C::WAVES * i, false);
+    for (int i = 0; i < C::IPW; ++i) lds_rows(rk_src, slot, blk * C::KB - shift, wv + C::WAVES * i, false, pp);
   };
-  auto load_v = [&](u16* slot, int blk) {
+  auto load_v = [&](u16* slot, int blk, int2 pp) {
 #pragma unroll
-    for (int i = 0; i < C::IPW; ++i) lds_rows(rv_src, slot, blk * C::KB - shift, wv + C::WAVES * i, true);
+    for (int i = 0; i < C::IPW; ++i) lds_rows(rv_src, slot, blk * C::KB - shift, wv + C::WAVES * i, true, pp);
   };
+  auto block_pages = [&](int blk) { return page_pair(blk * C::KB - shift); };
   // every LDS load of this wave has landed
   auto wait_loads = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
@@ -300,9 +334,12 @@ void attn_kernel(AttnArgs a) {
   // the first step: make them finite
   for (int i = tid; i < 32 * DH / 8; i += C::NT)
     *reinterpret_cast<uint4*>(vs1 + 32 * DH + 8 * i) = make_uint4(0, 0, 0, 0);
-  load_k(ks0, 0);
-  load_k(ks1, 1);
-  load_v(vs0, 0);
+  {
+    const int2 p0 = block_pages(0), p1 = block_pages(1);
+    load_k(ks0, 0, p0);
+    load_k(ks1, 1, p1);
+    load_v(vs0, 0, p0);
+  }
   if (REL) {
     if (tid < kTabPad / 8) *reinterpret_cast<uint4*>(tab + 8 * tid) = make_uint4(0, 0, 0, 0);
     const uint32_t tab_lds = (uint32_t)(uintptr_t)(lds_void*)(tab + kTabPad);
@@ -325,12 +362,13 @@ void attn_kernel(AttnArgs a) {
   // Block b with its K in kb (the other K slot holds block b + 1) and its V in vb (the
   // other V slot holds block b - 1).
   auto block = [&](int b, u16* kb, u16* kn, u16* vb, u16* vp) {
+    const int2 pk = block_pages(b + 2), pv = block_pages(b + 1);   // read here, used after the wait
     body(2 * b, kb + 32 * DH, vp + 32 * DH, sA, wA, sB, wB, [] {});   // K rows of half 2b+1, V of half 2b-1
     wait_loads();                      // this wave's K(b + 1) and V(b) have landed
     __syncthreads();                   // ... everyone's; K(b) and V(b - 1) are no longer read
     body(2 * b + 1, kn, vb, sB, wB, sA, wA, [&] {                  // K rows of half 2b+2, V of half 2b
-      load_k(kb, b + 2);               // past the last block these rows read as zero
-      load_v(vp, b + 1);
+      load_k(kb, b + 2, pk);           // past the last block these rows read as zero
+      load_v(vp, b + 1, pv);
     });
   };
   int b = 0;
@@ -359,10 +397,11 @@ void attn_kernel(AttnArgs a) {
       wait_loads();
       __syncthreads();   // the slots (or the previous block's area) are free
       const int k0 = wf + 32 * qb - shift;   // key of the half's first row
+      const int2 pp = page_pair(k0);
 #pragma unroll
       for (int j = 0; j < 32 / C::RPI; ++j) {
-        lds_rows(rk_src, dk, k0, j, false);
-        lds_rows(rv_src, dv, k0, j, true);
+        lds_rows(rk_src, dk, k0, j, false, pp);
+        lds_rows(rv_src, dv, k0, j, true, pp);
       }
       wait_loads();
       __syncthreads();
@@ -436,18 +475,21 @@ void attn_kernel(AttnArgs a) {
 
 hipError_t launch_attn_bf16(int dh, const AttnArgs& a, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  const bool rel = a.rel != nullptr;
-  if (dh == 64 && !rel)
-    attn_kernel<64, false><<<grid, AttnTile<64>::NT, 0, s>>>(a);
-  else if (dh == 64)
-    attn_kernel<64, true><<<grid, AttnTile<64>::NT, 0, s>>>(a);
-  else if (dh == 128 && !rel)
-    attn_kernel<128, false><<<grid, AttnTile<128>::NT, 0, s>>>(a);
-  else if (dh == 128)
-    attn_kernel<128, true><<<grid, AttnTile<128>::NT, 0, s>>>(a);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  const bool rel = a.rel != nullptr, paged = a.pages != nullptr;
+  constexpr int NT = AttnTile<64>::NT;
+  static_assert(AttnTile<128>::NT == NT, "one block size");
+#define HSTU_ATTN_CASE(DH, REL, PAGED) \
+  if (dh == DH && rel == REL && paged == PAGED) { attn_kernel<DH, REL, PAGED><<<grid, NT, 0, s>>>(a); return hipGetLastError(); }
+  HSTU_ATTN_CASE(64, false, false)
+  HSTU_ATTN_CASE(64, true, false)
+  HSTU_ATTN_CASE(128, false, false)
+  HSTU_ATTN_CASE(128, true, false)
+  HSTU_ATTN_CASE(64, false, true)
+  HSTU_ATTN_CASE(64, true, true)
+  HSTU_ATTN_CASE(128, false, true)
+  HSTU_ATTN_CASE(128, true, true)
+#undef HSTU_ATTN_CASE
+  return hipErrorInvalidValue;
 }
 
 int attn_block_rows_bf16() { return AttnTile<128>::BM; }

@@ -400,9 +400,11 @@ void uvqk_kernel(UvqkArgs a) {
                : slice == 1 ? (u16*)a.cache_v + ccol
                : slice == 3 ? (u16*)a.cache_k + ccol : nullptr;
   u16* const out0 = out + (size_t)(row0 + r_first) * 3 * D + cc;
-  // Cache rows of this thread's tile rows, looked up before the stores: all row-table
-  // reads in flight together, then all user-record reads (a lookup per store would wait
-  // for two dependent reads each time).
+  // Cache rows of this thread's history rows (-1: none), looked up before the stores: all
+  // row-table reads in flight together, then all user-record reads, then (paged cache)
+  // all page-table reads (a lookup per store would wait for dependent reads each time).
+  // A paged row goes to row pos % 64 of page table[key_row + pos / 64]; an id outside
+  // the pool is skipped.
   constexpr int NR = C::BM * CPR / C::NT;
   const bool append = cache != nullptr && row0 < a.Nu;   // uniform over the workgroup
   int crow[NR];
@@ -411,7 +413,17 @@ void uvqk_kernel(UvqkArgs a) {
 #pragma unroll
     for (int i = 0; i < NR; ++i) q[i] = a.row_info[min(row0 + r_first + RSTEP_O * i, a.T - 1)];
 #pragma unroll
-    for (int i = 0; i < NR; ++i) crow[i] = a.users[q[i].x].key_row + q[i].y;
+    for (int i = 0; i < NR; ++i) crow[i] = row0 + r_first + RSTEP_O * i < a.Nu ? a.users[q[i].x].key_row : -1;
+    if (a.pages != nullptr) {
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        const int pg = crow[i] >= 0 ? a.pages[crow[i] + (q[i].y >> 6)] : -1;
+        crow[i] = (unsigned)pg < (unsigned)a.npages ? pg * kPageRows + (q[i].y & (kPageRows - 1)) : -1;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NR; ++i) crow[i] = crow[i] >= 0 ? crow[i] + q[i].y : -1;
+    }
   }
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
@@ -420,7 +432,7 @@ void uvqk_kernel(UvqkArgs a) {
     if (row >= a.T) continue;
     const uint4 v = *reinterpret_cast<const uint4*>(smem + r * OLD + cc);
     *reinterpret_cast<uint4*>(out0 + (size_t)i * RSTEP_O * 3 * D) = v;
-    if (append && row < a.Nu) *reinterpret_cast<uint4*>(cache + (size_t)crow[i] * D + cc) = v;
+    if (append && crow[i] >= 0) *reinterpret_cast<uint4*>(cache + (size_t)crow[i] * D + cc) = v;
   }
 }
 

@@ -309,10 +309,23 @@ hstu_status validate_encode(EncodeCall& c, int32_t* keys) {
       (lay.Nc > 0 && (!aligned16(c.cand) || !aligned16(c.cand_out))))
     return HSTU_ERR_ALIGN;
   const hstu_kv_cache* kv = c.kv;
+  const int64_t es = d->dtype == HSTU_F32 ? 4 : 2;
+  const bool paged = kv && kv->page_rows != 0;
   if (kv) {
-    if (!kv->k || !kv->v || !kv->slot_of_user || !kv->cached_len) return HSTU_ERR_NULL;
+    if (!kv->k || !kv->v || !kv->cached_len) return HSTU_ERR_NULL;
     if (!aligned16(kv->k) || !aligned16(kv->v)) return HSTU_ERR_ALIGN;
-    if (kv->slots <= 0 || kv->capacity <= 0) return HSTU_ERR_CAPACITY;
+    if (!paged) {
+      if (!kv->slot_of_user) return HSTU_ERR_NULL;
+      if (kv->slots <= 0 || kv->capacity <= 0) return HSTU_ERR_CAPACITY;
+    } else {
+      if (kv->page_rows != hstu::kPageRows || kv->pages <= 0 || kv->pages_per_user <= 0) return HSTU_ERR_CAPACITY;
+      if (!kv->page_table) return HSTU_ERR_NULL;
+      if (((uintptr_t)kv->page_table & 3) != 0) return HSTU_ERR_ALIGN;
+      // the kernels address a layer's pool with 32-bit byte offsets and the page table
+      // with 32-bit indices
+      if ((int64_t)kv->pages * hstu::kPageRows * d->d_model * es > INT32_MAX) return HSTU_ERR_CAPACITY;
+      if ((int64_t)c.B * kv->pages_per_user > INT32_MAX) return HSTU_ERR_CAPACITY;
+    }
   }
   for (int32_t b = 0; b < c.B; ++b) {
     const int64_t n = c.uo[b + 1] - c.uo[b];
@@ -321,17 +334,21 @@ hstu_status validate_encode(EncodeCall& c, int32_t* keys) {
     int64_t m = 0;
     if (kv) {
       m = kv->cached_len[b];
-      const int32_t slot = kv->slot_of_user[b];
-      if (m < 0 || slot < 0 || slot >= kv->slots) return HSTU_ERR_CAPACITY;
-      if (m + n > kv->capacity) return HSTU_ERR_CAPACITY;
+      if (m < 0) return HSTU_ERR_CAPACITY;
+      if (paged) {
+        if ((m + n + hstu::kPageRows - 1) / hstu::kPageRows > kv->pages_per_user) return HSTU_ERR_CAPACITY;
+      } else {
+        const int32_t slot = kv->slot_of_user[b];
+        if (slot < 0 || slot >= kv->slots) return HSTU_ERR_CAPACITY;
+        if (m + n > kv->capacity) return HSTU_ERR_CAPACITY;
+      }
     }
     if (m + n + 1 > d->max_len) return HSTU_ERR_CAPACITY;
     // the attention kernel addresses one user's key rows with 32-bit byte offsets
-    if ((m + n) * (int64_t)(kv ? d->d_model : 3 * d->d_model) * (d->dtype == HSTU_F32 ? 4 : 2) > INT32_MAX)
-      return HSTU_ERR_CAPACITY;
+    if (!paged && (m + n) * (int64_t)(kv ? d->d_model : 3 * d->d_model) * es > INT32_MAX) return HSTU_ERR_CAPACITY;
   }
   // distinct slots: no two users of the call may write the same cache rows
-  if (kv && c.B > 1) {
+  if (kv && !paged && c.B > 1) {
     std::copy(kv->slot_of_user, kv->slot_of_user + c.B, keys);
     std::sort(keys, keys + c.B);
     if (std::adjacent_find(keys, keys + c.B) != keys + c.B) return HSTU_ERR_CAPACITY;
@@ -350,6 +367,9 @@ hstu_status run_encode(const EncodeCall& c, const PlanSpace& ps, char* ws, hipSt
   const Layout& lay = c.lay;
   const hstu_kv_cache* kv = c.kv;
   const int32_t B = c.B, L = d->layers, D = d->d_model;
+  const bool paged = kv && kv->page_rows != 0;
+  const int32_t* pages = paged ? kv->page_table : nullptr;
+  const int32_t npages = paged ? kv->pages : 0;
 
   // ------------------------------------------------------------ plan (host)
   const int bm = hstu::attn_block_rows(d->dtype);
@@ -362,7 +382,7 @@ hstu_status run_encode(const EncodeCall& c, const PlanSpace& ps, char* ws, hipSt
     u.coff = c.co[b];
     u.c = c.co[b + 1] - c.co[b];
     u.m = kv ? kv->cached_len[b] : 0;
-    u.key_row = kv ? kv->slot_of_user[b] * kv->capacity : u.uoff;
+    u.key_row = !kv ? u.uoff : paged ? b * kv->pages_per_user : kv->slot_of_user[b] * kv->capacity;
     u.pad0 = u.pad1 = 0;
   }
   const void** wptr = reinterpret_cast<const void**>(ps.image + lay.wptr);
@@ -402,7 +422,8 @@ hstu_status run_encode(const EncodeCall& c, const PlanSpace& ps, char* ws, hipSt
   }
 
   const int dh = D / d->heads;
-  const size_t layer_cache = kv ? (size_t)kv->slots * kv->capacity * D * es : 0;
+  const size_t layer_cache = !kv ? 0 : paged ? (size_t)kv->pages * hstu::kPageRows * D * es
+                                            : (size_t)kv->slots * kv->capacity * D * es;
   for (int32_t l = 0; l < L; ++l) {
     const void* x_lo = l == 0 ? c.uih : xbuf;
     const void* x_hi = l == 0 ? c.cand : (const void*)(xbuf + nu_bytes);
@@ -417,7 +438,7 @@ hstu_status run_encode(const EncodeCall& c, const PlanSpace& ps, char* ws, hipSt
         return HSTU_ERR_HIP;
     }
     hstu::UvqkArgs ua{xn, x_lo, x_hi, cs + (size_t)l * 4 * D, rstat, lay.Nu, lay.T, D, c.w[l].w_uvqk,
-                      c.w[l].pos_bias, d_rows, d_users, vqk, aout, ck, cv};
+                      c.w[l].pos_bias, d_rows, d_users, vqk, aout, ck, cv, pages, npages};
     if (timed_launch(HSTU_KERNEL_UVQK, s, [&] { return hstu::launch_uvqk(d->dtype, ua, s); }) != hipSuccess)
       return HSTU_ERR_HIP;
 
@@ -436,6 +457,8 @@ hstu_status run_encode(const EncodeCall& c, const PlanSpace& ps, char* ws, hipSt
       aa.vbase = vqk;
       aa.ld = 3 * (int64_t)D;
     }
+    aa.pages = pages;
+    aa.npages = npages;
     aa.aout = aout;
     aa.rel = c.w[l].rel_bias;
     aa.max_len = d->max_len;

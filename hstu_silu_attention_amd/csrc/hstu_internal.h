@@ -11,8 +11,9 @@ namespace hstu {
 //  uoff/n:  new history rows uoff..uoff+n-1 of the packed row space
 //  coff/c:  candidate rows Nu+coff..Nu+coff+c-1 of the packed row space
 //  m:       cached history length (positions 0..m-1 live in the cache)
-//  key_row: row of key 0 in the key/value source (cache: slot*capacity;
-//           no cache: uoff, i.e. the user's first history row of the vqk buffer)
+//  key_row: row of key 0 in the key/value source (slot cache: slot*capacity;
+//           no cache: uoff, i.e. the user's first history row of the vqk buffer);
+//           paged cache: the first entry of the user's row of the page table
 struct UserRec {
   int32_t uoff, n, coff, c, m, key_row, pad0, pad1;
 };
@@ -112,17 +113,25 @@ struct UvqkArgs {
   const UserRec* users;
   void* vqk;             // [T_pad][3D] out: V, Q, K (rows < T written)
   void* aout;            // [T_pad][3D] out: U into columns [0, D)
-  void* cache_k;         // this layer's [slots][cap][D] or nullptr
+  void* cache_k;         // this layer's [slots][cap][D] or [pages][kPageRows][D], or nullptr
   void* cache_v;
+  const int32_t* pages;  // paged cache: the page table (device), else nullptr
+  int32_t npages;        // paged cache: pages of the pool; an id outside [0, npages) is skipped
 };
+
+// Rows of one page of a paged key/value cache: user row p lives in page
+// table[key_row + p / kPageRows], row p % kPageRows.
+constexpr int kPageRows = 64;
 
 struct AttnArgs {
   const AttnItem* items; // [grid], item w for workgroup w
   int32_t Nu, D;
   float inv;             // 1 / max_len
   const void* vqk;       // [T_pad][3D]: Q, and the candidates' own K, V
-  const void* kbase;     // key row r of user b is kbase + (key_row_b + r) * ld
-  const void* vbase;
+  const void* kbase;     // key row r of user b is kbase + (key_row_b + r) * ld (contiguous), or
+  const void* vbase;     // kbase + (pages[key_row_b + r / 64] * 64 + r % 64) * ld (paged)
+  const int32_t* pages;  // paged cache: the page table (device), else nullptr
+  int32_t npages;        // paged cache: pages of the pool (reads outside it give zeros)
   int64_t ld;
   void* aout;            // [T_pad][3D]: writes O (float32 also reads U, writes U*O)
   const void* rel;       // this layer's relative bias [H][max_len], or nullptr

@@ -76,7 +76,14 @@ __global__ __launch_bounds__(256) void uvqk_f32_kernel(UvqkArgs a) {
       ((float*)a.vqk)[(size_t)row * 3 * D + (slice - 1) * D + cc] = v;
     if (a.cache_k != nullptr && row < a.Nu && (slice == 1 || slice == 3)) {
       float* dst = (float*)(slice == 1 ? a.cache_v : a.cache_k);
-      dst[((size_t)a.users[ri.x].key_row + ri.y) * D + cc] = v;
+      const int kr = a.users[ri.x].key_row;
+      if (a.pages == nullptr) {
+        dst[((size_t)kr + ri.y) * D + cc] = v;
+      } else {
+        // paged: row pos % 64 of page table[key_row + pos / 64]; ids outside the pool skipped
+        const int pg = a.pages[kr + ri.y / kPageRows];
+        if ((unsigned)pg < (unsigned)a.npages) dst[((size_t)pg * kPageRows + ri.y % kPageRows) * D + cc] = v;
+      }
     }
   };
   gemm_f32(RowLoadF{(const float*)a.xn, D}, (const float*)a.w, D, a.T,
@@ -122,15 +129,21 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   const int key_end = it.key_end;
   const int qpos = cand ? key_end : it.m + it.q0 + tid;   // candidates sit at m + n
   const float* rel = a.rel == nullptr ? nullptr : (const float*)a.rel + (size_t)head * a.max_len;
-  const float* kp = (const float*)a.kbase + (size_t)it.key_row * a.ld + head * DH;
-  const float* vp = (const float*)a.vbase + (size_t)it.key_row * a.ld + head * DH;
+  const float* kp = (const float*)a.kbase + head * DH;
+  const float* vp = (const float*)a.vbase + head * DH;
+  // source row of key r: contiguous from key_row, or paged (-1: an id outside the pool)
+  auto key_src = [&](int r) -> long {
+    if (a.pages == nullptr) return (long)it.key_row + r;
+    const int pg = a.pages[it.key_row + r / kPageRows];
+    return (unsigned)pg < (unsigned)a.npages ? (long)pg * kPageRows + r % kPageRows : -1;
+  };
   for (int k0 = 0; k0 < key_end; k0 += FKB) {
     __syncthreads();
     for (int id = tid; id < FKB * DH; id += 64) {
       const int key = id / DH, e = id % DH;
-      const bool in = k0 + key < key_end;
-      sk[key][e] = in ? kp[(size_t)(k0 + key) * a.ld + e] : 0.0f;
-      sv[key][e] = in ? vp[(size_t)(k0 + key) * a.ld + e] : 0.0f;
+      const long src = k0 + key < key_end ? key_src(k0 + key) : -1;
+      sk[key][e] = src >= 0 ? kp[src * a.ld + e] : 0.0f;
+      sv[key][e] = src >= 0 ? vp[src * a.ld + e] : 0.0f;
     }
     __syncthreads();
     const int kn = min(FKB, key_end - k0);

@@ -1,11 +1,12 @@
-"""Time-ordered request replay over the streaming key/value cache.
+"""Time-ordered request replay over the paged streaming key/value cache.
 
 Each request brings a user's events since its previous request, and candidates to
 encode. Requests are served in time order, in batches of distinct users. Per batch the
-library's slot pool (``SlotPool``, hstu_pool_*) says, for each user, whether its cached
-rows are extended (only the new events are sent) or its history is sent again: a
-user seen for the first time, evicted from its slot, stale (older than the TTL), or
-out of room. A history sent again is the user's latest ``window`` events.
+library's page pool (``KvPool``, hstu_pool_*) says, for each user, whether its cached
+rows are extended (only the new events are sent) or its history is sent again (a user
+seen for the first time, evicted, stale (older than the TTL), or out of room), and
+which pages of the cache hold its rows; a user holds ceil(rows / 64) pages. A history
+sent again is the user's latest ``window`` events.
 
 This module is plumbing: it assembles each batch's history rows on the host (as a
 serving front end receives them) and copies them to the device in one transfer,
@@ -21,7 +22,7 @@ from typing import Dict, List, Optional, Sequence
 
 import numpy as np
 
-from . import HSTU_OK, KVCache, Model, ScoringHead, SlotPool, encode, hstu_flops, score
+from . import HSTU_OK, KvPool, Model, PagedKVCache, ScoringHead, encode, hstu_flops, score
 
 
 @dataclasses.dataclass
@@ -45,15 +46,15 @@ class Served:
 
 
 class Replayer:
-    """Serves requests against one model, one KVCache and one SlotPool of the same slots."""
+    """Serves requests against one model, one PagedKVCache and one KvPool of the cache's pages."""
 
-    def __init__(self, model: Model, cache: KVCache, pool: SlotPool, history: Dict[int, np.ndarray], *,
+    def __init__(self, model: Model, cache: PagedKVCache, pool: KvPool, history: Dict[int, np.ndarray], *,
                  window: int, head: Optional[ScoringHead] = None, device="cuda", keep_outputs: bool = True):
-        if window < 1 or window > pool.capacity:
-            raise ValueError("window must be in [1, pool capacity]")
-        if pool.capacity > min(cache.capacity, model.max_len - 1) or pool.slots != cache.slots:
-            raise ValueError("the pool must have the cache's slots and at most min(cache capacity, "
-                             "max_len - 1) rows per slot")
+        if window < 1 or window > pool.max_rows:
+            raise ValueError("window must be in [1, the pool's max_rows]")
+        if (pool.max_rows > min(cache.pages_per_user * 64, model.max_len - 1) or pool.pages != cache.pages):
+            raise ValueError("the pool must manage the cache's pages and allow at most min(pages_per_user * 64, "
+                             "max_len - 1) rows per user")
         self.model, self.cache, self.pool, self.history = model, cache, pool, history
         self.window, self.head, self.device, self.keep_outputs = window, head, device, keep_outputs
         self.seen: Dict[int, int] = {}          # events of each user already in its cached rows
@@ -95,15 +96,14 @@ class Replayer:
     def serve(self, batch: Sequence[Request]) -> List[Served]:
         now = max(r.time for r in batch)
         users = [r.user for r in batch]
+        if len(batch) > self.cache.max_users:
+            raise ValueError("a batch has more users than the cache's page table")
         new = [r.events - self.seen.get(r.user, 0) for r in batch]
-        # more new events than a slot holds: the cached rows cannot be extended
-        too_many = [u for u, n in zip(users, new) if n > self.pool.capacity]
-        if too_many:
-            self.pool.abort(too_many)
-        slot, cached, rebuild = self.pool.assign(users, [min(n, self.pool.capacity) for n in new], now)
+        window = [min(r.events, self.window) for r in batch]
+        table, cached, rebuild = self.pool.assign(users, new, window, now, self.cache.pages_per_user)
         parts, lengths, sent_from = [], [], []
         for r, c, rb in zip(batch, cached, rebuild):
-            lo = max(0, r.events - self.window) if rb else self.seen[r.user]
+            lo = r.events - min(r.events, self.window) if rb else self.seen[r.user]
             if rb:
                 self.start[r.user] = lo
             assert int(c) == (0 if rb else lo - self.start[r.user])
@@ -114,7 +114,9 @@ class Replayer:
         cand = self._to_device([r.cand for r in batch])
         uo = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
         co = np.concatenate([[0], np.cumsum([int(r.cand.shape[0]) for r in batch])]).astype(np.int32)
-        self.cache.slot_of_user = slot.astype(np.int32)
+        # the table is shared by the batches: the copy is ordered after the previous batch's
+        # kernels on the stream they share
+        self.cache.set_table(table)
         self.cache.cached_len = cached.astype(np.int32).copy()
         try:
             out_u, out_c = encode(self.model, uih, uo, cand, co, cache=self.cache)

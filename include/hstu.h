@@ -30,8 +30,8 @@
  * (see hstu_layer_weights). The new history rows' K, V (after bias) are appended to
  * the cache. Entry points around the encoder: hstu_pack_uih builds the history
  * tokens from per-event context and action embeddings, hstu_score turns candidate
- * rows into outcome probabilities, and hstu_pool_* manage cache slots for
- * time-ordered request replay.
+ * rows into outcome probabilities, and hstu_pool_* manage the pages of a paged
+ * cache for time-ordered request replay.
  *
  * bfloat16 mode: storage is bfloat16, accumulation float32; results are rounded
  * to bfloat16 (nearest, ties to even) at U,V,Q,K; at each attention weight SiLU(q.k)
@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 6
+#define HSTU_ABI_VERSION 7
 
 /* Element type of every device tensor of a call. */
 enum hstu_dtype { HSTU_F32 = 0, HSTU_BF16 = 1 };
@@ -82,7 +82,8 @@ enum hstu_status_code {
   HSTU_ERR_CAPACITY = 4,   /* m+n >= max_len, cache capacity < m+n, bad or repeated slot,   */
                            /* cached_len < 0, or one user's keys of one layer span 2 GiB or */
                            /* more ((m+n) * row pitch in bytes; the pitch is D elements with */
-                           /* a cache, 3D without)                                          */
+                           /* a cache, 3D without); paged: a bad page_rows, pages or        */
+                           /* pages_per_user, too few pages per user, or a pool of 2 GiB    */
   HSTU_ERR_WORKSPACE = 5,  /* workspace NULL or smaller than hstu_workspace_size()          */
   HSTU_ERR_HIP = 6,        /* a HIP runtime call failed; outputs and cache are undefined    */
   HSTU_ERR_ALIGN = 7,      /* a device pointer is not 16-byte aligned                       */
@@ -127,13 +128,26 @@ typedef struct hstu_layer_weights {
   const void* rel_bias;
 } hstu_layer_weights;
 
-/* Streaming key/value cache (caller-owned).
- *  k, v          device, each [layers][slots][capacity][D] in the call's dtype. Rows
- *                0..cached_len[b]-1 of slot slot_of_user[b] hold user b's earlier
- *                history keys / values (after position bias), in position order.
- *  slot_of_user  host [B]; distinct slots in [0, slots).
+/* Streaming key/value cache (caller-owned): user b's history keys / values (after
+ * position bias) at positions 0..cached_len[b]-1, in one of two layouts.
  *  cached_len    host [B], in/out: m_b on entry; m_b + n_b after a successful call.
- * The call reads rows 0..m_b-1 and writes rows m_b..m_b+n_b-1 of each layer.
+ *  page_rows == 0: slot layout.
+ *    k, v          device, each [layers][slots][capacity][D] in the call's dtype; user b's
+ *                  position p is row p of slot slot_of_user[b].
+ *    slot_of_user  host [B]; distinct slots in [0, slots). m_b + n_b <= capacity.
+ *  page_rows == 64: paged layout (the pages field set, slots/capacity/slot_of_user
+ *                  unused). The cache holds each user's rows in pages of 64, so the
+ *                  memory a user holds grows with its history, 64 rows at a time.
+ *    k, v          device, each [layers][pages][64][D] in the call's dtype.
+ *    page_table    DEVICE int32 [B][pages_per_user] (4-byte aligned): user b's position
+ *                  p is row p % 64 of page page_table[b][p / 64]. Entries
+ *                  0..ceil((m_b+n_b)/64)-1 of each row must hold page ids in [0, pages),
+ *                  no page used by two users (or twice) of one call. The library cannot
+ *                  check device contents: a page id outside [0, pages) reads as zeros
+ *                  and takes no writes (results are then wrong, but no memory outside
+ *                  the pool is touched). ceil((m_b+n_b)/64) <= pages_per_user, and one
+ *                  layer's pool spans under 2 GiB (pages * 64 * D * element size).
+ * The call reads positions 0..m_b-1 and writes positions m_b..m_b+n_b-1 of each layer.
  * Candidates are never appended. */
 typedef struct hstu_kv_cache {
   void* k;
@@ -142,6 +156,10 @@ typedef struct hstu_kv_cache {
   int32_t capacity;
   const int32_t* slot_of_user;
   int32_t* cached_len;
+  int32_t page_rows;
+  int32_t pages;
+  int32_t pages_per_user;
+  const int32_t* page_table;
 } hstu_kv_cache;
 
 /* HSTU_ABI_VERSION of the loaded library. */
@@ -258,62 +276,69 @@ typedef struct hstu_head_layer {
 hstu_status hstu_score(const hstu_dims* d, int32_t rows, const void* x, const hstu_head_layer* head,
                        int32_t head_layers, float* prob, void* stream);
 
-/* Streaming replay: a host-side manager of the cache's user slots. Requests are
- * replayed in time order (the DLRMv3 page, section "Dataset selection") and a user's
- * history keys/values are reused across its consecutive requests (section "Model
- * selection"); cached state goes stale (the multi-stage sequence model page, its
+/* Streaming replay: a host-side manager of a paged hstu_kv_cache (page_rows 64).
+ * Requests are replayed in time order (the DLRMv3 page, section "Dataset selection")
+ * and a user's history keys/values are reused across its consecutive requests (section
+ * "Model selection"); cached state goes stale (the multi-stage sequence model page, its
  * limitations section: invalidation and TTL design). Per request the pool decides
  * whether the user's cached rows are extended or its history is encoded again, and
- * which slot of an hstu_kv_cache the user gets. Host only: it launches nothing and
- * touches no device memory.
+ * which pages hold the user's rows: a user holds ceil(rows / 64) pages of the cache, so
+ * the memory it takes follows its history. Host only: it launches nothing and touches
+ * no device memory (the caller copies each batch's page table to the device).
  *
- * hstu_pool_create: `slots` (>= 1) user slots of `capacity` (>= 1) rows each, the
- *   capacity of the hstu_kv_cache the pool manages (use min(capacity, max_len - 1)
- *   so that a user's history also fits the position tables); `ttl` (>= 0): cached
- *   rows last used more than ttl time units before a request are stale. Errors:
+ * hstu_pool_create: a pool of `pages` (>= 1) pages, the `pages` of the hstu_kv_cache it
+ *   manages; `max_rows` (>= 1): most rows one user may hold (use at most max_len - 1,
+ *   so that a user's history also fits the position tables); `ttl` (>= 0): cached rows
+ *   last committed more than ttl time units before a request are stale. Errors:
  *   ERR_NULL, ERR_SHAPE, ERR_HIP (the host allocation failed).
- * hstu_pool_assign: one batch of B (<= slots) requests from distinct users (ids >= 0)
- *   at time `now`, user b bringing new_events[b] (0..capacity) new history rows. For
- *   each user it writes slot_of_user[b] and cached_len[b] (ready for hstu_kv_cache)
- *   and rebuild[b]:
- *     0  the user's slot holds cached_len[b] fresh rows and has room for the new
- *        events: send only the new events;
- *     1  cached_len[b] = 0: send the user's history again (as many of its latest
- *        events as the caller keeps, at most capacity), as new rows.
- *   A user without a slot gets a free one, else the least recently committed slot
- *   not held by this batch or an uncommitted one (its user is evicted). Every user
- *   of the batch is pending until hstu_pool_commit or hstu_pool_abort; a pending
- *   user may not be assigned again.
- *   Errors (the pool and the output arrays unchanged): ERR_NULL, ERR_SHAPE (B < 0, an
- *   id < 0, repeated or pending), ERR_CAPACITY (B > slots, new_events out of range,
- *   or too few slots not held by uncommitted batches).
- * hstu_pool_commit: after hstu_encode succeeded for the batch: user b's slot now
- *   holds total_len[b] rows (cached_len + rows sent, <= capacity), last used at `now`.
- *   Errors (nothing changed): ERR_SHAPE (a user not pending), ERR_CAPACITY (a length
- *   below the cached length or above capacity).
- * hstu_pool_abort: after a failed encode: the users' slots are freed.
- * hstu_pool_stats: counters since creation, indexed by enum hstu_pool_stat.
- * hstu_pool_lookup: a user's slot (-1 if none) and committed row count.
+ * hstu_pool_assign: one batch of B requests from distinct users (ids >= 0) at time
+ *   `now`; user b brings new_events[b] (>= 0) events since its last request, and
+ *   would resend window[b] (0..max_rows) events, its latest, if its history must be
+ *   encoded again. For each user it writes cached_len[b] and rebuild[b]:
+ *     0  the user's fresh rows can take the new events (cached + new <= max_rows):
+ *        send only the new events, after cached_len[b] cached rows;
+ *     1  cached_len[b] = 0: send the latest window[b] events, as new rows;
+ *   and row b of page_table (host int32 [B][pages_per_user]): the user's pages in
+ *   position order for its rows after the call (hits keep their pages and get more,
+ *   a rebuild reuses the user's pages), -1 past them. When too few pages are free,
+ *   the least recently committed users outside the batch and not pending are evicted
+ *   (all their pages freed), oldest first. Every user of the batch is pending until
+ *   hstu_pool_commit or hstu_pool_abort; a pending user may not be assigned again.
+ *   Errors (the pool and the output arrays unchanged): ERR_NULL, ERR_SHAPE (B < 0,
+ *   pages_per_user < 1, an id < 0, repeated or pending, new_events < 0, window out of
+ *   range), ERR_CAPACITY (a user would need more than pages_per_user pages, or the
+ *   batch does not fit even after evicting every user it may evict).
+ * hstu_pool_commit: after hstu_encode succeeded for the batch: user b now holds
+ *   total_len[b] rows (cached_len + rows sent), last used at `now`; pages beyond its
+ *   rows are freed. Errors (nothing changed): ERR_SHAPE (a user not pending),
+ *   ERR_CAPACITY (a length below the cached length, above max_rows or its pages).
+ * hstu_pool_abort: after a failed encode: the users' pages are freed, the users
+ *   forgotten.
+ * hstu_pool_stats: counters indexed by enum hstu_pool_stat.
+ * hstu_pool_lookup: a user's committed rows and the pages it holds (0, 0 if absent).
  * A pool is not synchronised: calls on one pool from several threads need the
  * caller's lock. */
-typedef struct hstu_slot_pool hstu_slot_pool;
+typedef struct hstu_kv_pool hstu_kv_pool;
 enum hstu_pool_stat {
   HSTU_POOL_HITS = 0,            /* cached rows extended                          */
-  HSTU_POOL_REBUILD_NEW = 1,     /* user had no slot                              */
+  HSTU_POOL_REBUILD_NEW = 1,     /* user had no cached rows                       */
   HSTU_POOL_REBUILD_STALE = 2,   /* cached rows older than ttl                    */
-  HSTU_POOL_REBUILD_FULL = 3,    /* no room for the new events                    */
-  HSTU_POOL_EVICTIONS = 4,       /* users whose slot was given to another user    */
-  HSTU_POOL_STATS = 5
+  HSTU_POOL_REBUILD_FULL = 3,    /* no room for the new events under max_rows     */
+  HSTU_POOL_EVICTIONS = 4,       /* users whose pages were taken for other users  */
+  HSTU_POOL_PAGES_IN_USE = 5,    /* pages held now                                */
+  HSTU_POOL_PAGES_PEAK = 6,      /* most pages held after any assign              */
+  HSTU_POOL_STATS = 7
 };
-hstu_status hstu_pool_create(int32_t slots, int32_t capacity, int64_t ttl, hstu_slot_pool** pool);
-void hstu_pool_destroy(hstu_slot_pool* pool);
-hstu_status hstu_pool_assign(hstu_slot_pool* pool, int32_t B, const int64_t* user, const int32_t* new_events,
-                             int64_t now, int32_t* slot_of_user, int32_t* cached_len, int32_t* rebuild);
-hstu_status hstu_pool_commit(hstu_slot_pool* pool, int32_t B, const int64_t* user, const int32_t* total_len,
+hstu_status hstu_pool_create(int32_t pages, int32_t max_rows, int64_t ttl, hstu_kv_pool** pool);
+void hstu_pool_destroy(hstu_kv_pool* pool);
+hstu_status hstu_pool_assign(hstu_kv_pool* pool, int32_t B, const int64_t* user, const int32_t* new_events,
+                             const int32_t* window, int64_t now, int32_t pages_per_user, int32_t* page_table,
+                             int32_t* cached_len, int32_t* rebuild);
+hstu_status hstu_pool_commit(hstu_kv_pool* pool, int32_t B, const int64_t* user, const int32_t* total_len,
                              int64_t now);
-hstu_status hstu_pool_abort(hstu_slot_pool* pool, int32_t B, const int64_t* user);
-hstu_status hstu_pool_stats(const hstu_slot_pool* pool, int64_t* stats, int32_t n);
-hstu_status hstu_pool_lookup(const hstu_slot_pool* pool, int64_t user, int32_t* slot, int32_t* len);
+hstu_status hstu_pool_abort(hstu_kv_pool* pool, int32_t B, const int64_t* user);
+hstu_status hstu_pool_stats(const hstu_kv_pool* pool, int64_t* stats, int32_t n);
+hstu_status hstu_pool_lookup(const hstu_kv_pool* pool, int64_t user, int32_t* len, int32_t* pages);
 
 /* Measurement aid: device time of each kernel that hstu_encode, hstu_pack_uih and
  * hstu_score launch, taken with HIP events recorded on the caller's stream

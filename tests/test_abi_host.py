@@ -210,6 +210,36 @@ def test_encode_capacity_and_slots_leave_cached_len_unchanged():
     assert b.call() == ERR_CAPACITY
 
 
+def fake_paged(cached, pages=8, pages_per_user=2, page_rows=64, table=0x500000):
+    cl = np.ascontiguousarray(cached, dtype=np.int32)
+    kv = hsa.HstuKvCache(0x200000, 0x300000, 0, 0, None, cl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                         page_rows, pages, pages_per_user, table)
+    return kv, cl
+
+
+def test_encode_paged_cache_validation_leaves_cached_len_unchanged():
+    """Paged layout (page_rows 64): each user's m + n rows must fit its pages_per_user pages,
+    the page table must be given and 4-byte aligned, page_rows must be 64, and a layer's
+    pool must span under 2 GiB. The device page table itself is not read on the host."""
+    a = FakeArgs(max_len=200, uih=(5, 3), cand=(2, 0))
+    kv, cl = fake_paged([124, 0])                       # 124 + 5 = 129 rows need three pages
+    assert a.call(kv=kv) == ERR_CAPACITY and cl.tolist() == [124, 0]
+    kv, cl = fake_paged([0, 0], page_rows=32)
+    assert a.call(kv=kv) == ERR_CAPACITY
+    kv, cl = fake_paged([0, 0], pages=0)
+    assert a.call(kv=kv) == ERR_CAPACITY
+    kv, cl = fake_paged([0, 0], pages_per_user=0)
+    assert a.call(kv=kv) == ERR_CAPACITY
+    kv, cl = fake_paged([0, 0], table=0)
+    assert a.call(kv=kv) == ERR_NULL
+    kv, cl = fake_paged([0, 0], table=0x500002)
+    assert a.call(kv=kv) == ERR_ALIGN
+    kv, cl = fake_paged([0, 0], pages=1 << 20)          # 2^20 pages x 64 rows x 256 x 2 B = 32 GiB
+    assert a.call(kv=kv) == ERR_CAPACITY
+    kv, cl = fake_paged([-1, 0])
+    assert a.call(kv=kv) == ERR_CAPACITY and cl.tolist() == [-1, 0]
+
+
 def test_encode_empty_batches_are_ok_without_device_work():
     d = dims()
     assert hsa.hstu_encode(d, 0, None, None, 0, 0, [hsa.HstuLayerWeights(1, 1, 1)] * 2, None,

@@ -186,6 +186,36 @@ def test_streaming_workload_sampled_user():
     assert eu <= BF16_TOL and ec <= BF16_TOL and ek <= BF16_TOL
 
 
+def test_streaming_workload_paged_matches_slot():
+    """The streaming workload (64 users, 3000 cached + 300 new rows, 2048 candidates, 8
+    layers) with its cache in 64-row pages under shuffled page ids, as `bench.py --paged`
+    runs it, against the slot layout: every output row and every cached row agree bit for
+    bit (the kernels add in the same order; only addresses differ)."""
+    torch = torch_cuda()
+    wl = workloads.make_workload("stream_3000p300_c2k")
+    B, D = wl.users, wl.d_model
+    model = make_model(torch, wl)
+    empty = np.zeros((0, D), np.float32)
+    cap = 3300
+    ppu = (cap + 63) // 64
+    slot = hsa.KVCache(model, slots=B, capacity=cap)
+    paged = hsa.PagedKVCache(model, pages=B * ppu, pages_per_user=ppu, max_users=B)
+    ids = np.random.default_rng(0).permutation(B * ppu).reshape(B, ppu).astype(np.int32)
+    paged.set_table(ids)
+    outs = []
+    for cache in (slot, paged):
+        cache.cached_len = np.zeros(B, dtype=np.int32)
+        gpu_encode(wl, model=model, uih=wl.prefix, cand=empty, uih_lengths=wl.cached_lengths,
+                   cand_lengths=np.zeros(B, np.int64), cache=cache)
+        outs.append(gpu_encode(wl, model=model, cache=cache))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+    idx = torch.from_numpy(ids.astype(np.int64)).to(paged.k.device)
+    for name in ("k", "v"):
+        ps = getattr(paged, name)[:, idx].reshape(wl.layers, B, ppu * 64, D)[:, :, :cap]
+        assert torch.equal(ps, getattr(slot, name))
+    say(f"  streaming workload, paged cache ({B * ppu} pages) = slot cache, bit for bit")
+
+
 def test_long_workload_layerwise_sampled_rows():
     """16 layers, 4 users with UIH 8K-16K, 2048 candidates, 8 heads (dh 64). The full call
     equals the chain of 16 one-layer calls bit for bit; layers 0, 7 and 15 are then checked

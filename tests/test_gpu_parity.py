@@ -162,6 +162,62 @@ def test_streaming_cache(dtype, position):
     assert eu1 <= tol and ec1 <= tol
 
 
+def _fill_and_encode(wl, model, cache):
+    """Prefix into the cache (no candidates), then the new events plus candidates."""
+    B = wl.users
+    empty = np.zeros((0, wl.d_model), np.float32)
+    gpu_encode(wl, model=model, uih=wl.prefix, cand=empty, uih_lengths=wl.cached_lengths,
+               cand_lengths=np.zeros(B, np.int64), cache=cache)
+    assert cache.cached_len[:B].tolist() == wl.cached_lengths.tolist()
+    out = gpu_encode(wl, model=model, cache=cache)
+    assert cache.cached_len[:B].tolist() == (wl.cached_lengths + wl.uih_lengths).tolist()
+    return out
+
+
+@pytest.mark.parametrize("dtype,D,H,position", [("bf16", 512, 4, "absolute"), ("bf16", 256, 4, "both"),
+                                                ("bf16", 512, 4, "relative"), ("f32", 128, 2, "both")])
+def test_paged_cache_matches_slot_cache(dtype, D, H, position):
+    """The paged layout (64-row pages, shuffled page ids, a device page table) against the
+    slot layout on the same calls: the kernels add in the same order, so outputs and
+    cached rows agree bit for bit; the outputs are also held to the oracle's bar. Cached
+    lengths cross page boundaries mid-block (200, 17, 129, 0 then +40, 0, 130, 7)."""
+    torch = torch_cuda()
+    L = 2
+    wl = workloads.make_custom(seed=1401, dtype=dtype, layers=L, d_model=D, heads=H, max_len=500,
+                               uih_lengths=[40, 0, 130, 7], cand_lengths=[9, 3, 65, 0],
+                               cached_lengths=[200, 17, 129, 0], position=position, rel_std=0.3)
+    B = wl.users
+    model = make_model(torch, wl)
+    slot = hsa.KVCache(model, slots=4, capacity=400)
+    slot.cached_len = np.zeros(B, dtype=np.int32)
+    su, sc = _fill_and_encode(wl, model, slot)
+    ppu, npool = 7, 40
+    rng = np.random.default_rng(3)
+    ids = rng.permutation(npool)[:B * ppu].reshape(B, ppu).astype(np.int32)
+    paged = hsa.PagedKVCache(model, pages=npool, pages_per_user=ppu, max_users=B)
+    paged.set_table(ids)
+    paged.cached_len = np.zeros(B, dtype=np.int32)
+    pu, pc = _fill_and_encode(wl, model, paged)
+    assert np.array_equal(pu, su) and np.array_equal(pc, sc)
+    total = wl.cached_lengths + wl.uih_lengths
+    for name in ("k", "v"):
+        sk, pk = to_np(getattr(slot, name)), to_np(getattr(paged, name))
+        for b in range(B):
+            rows = np.concatenate([pk[:, ids[b, i]] for i in range(ppu)], axis=1)   # [L][ppu*64][D]
+            assert np.array_equal(rows[:, :total[b]], sk[:, b, :total[b]])
+    import oracle
+    ocache = oracle.OracleCache(np.zeros((L, B, 400, D)), np.zeros((L, B, 400, D)), np.arange(B), np.zeros(B, np.int64))
+    mode = "bf16" if dtype == "bf16" else "f64"
+    tol = BF16_TOL if dtype == "bf16" else F32_TOL
+    empty = np.zeros((0, D), np.float32)
+    _, _, ocache = oracle_encode(wl, mode, cache=ocache, uih=wl.prefix, uih_lengths=wl.cached_lengths,
+                                 cand=empty, cand_lengths=np.zeros(B, np.int64))
+    ru, rc, _ = oracle_encode(wl, mode, cache=ocache)
+    eu, ec = normwise_per_user(pu, ru, wl.uih_lengths), normwise_per_user(pc, rc, wl.cand_lengths)
+    say(f"  paged {dtype} D={D} {position}: bit-identical to the slot layout; vs oracle uih {eu:.3e} cand {ec:.3e}")
+    assert eu <= tol and ec <= tol
+
+
 def test_uih_outputs_bit_identical_for_any_candidate_set():
     """The history's representation must not depend on the candidates: identical bits for the
     candidate sets {}, A, B and A permuted; permuting candidates permutes their outputs."""

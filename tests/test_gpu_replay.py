@@ -1,8 +1,8 @@
-"""GPU check of time-ordered request replay over the streaming cache and the slot pool:
-every request's candidate outputs and the outputs of the history rows it sent equal the
-oracle's one-shot encode of the user's cached window plus those rows (bfloat16 normwise
-<= 2e-2). The stream is built so that cache hits, evictions, stale rebuilds and rebuilds
-for want of room all occur."""
+"""GPU check of time-ordered request replay over the paged streaming cache and the page
+pool: every request's candidate outputs and the outputs of the history rows it sent equal
+the oracle's one-shot encode of the user's cached window plus those rows (bfloat16
+normwise <= 2e-2). The stream is built so that cache hits, evictions, stale rebuilds and
+rebuilds for want of room all occur; every user holds ceil(rows / 64) pages."""
 import numpy as np
 import pytest
 
@@ -34,8 +34,8 @@ def test_replay_matches_one_shot_encodes():
     wl = workloads.make_custom(seed=501, dtype="bf16", layers=L, d_model=D, heads=H, max_len=400,
                                uih_lengths=[0], cand_lengths=[0], position="both", rel_std=0.3)
     model = make_model(torch, wl)
-    cache = hsa.KVCache(model, slots=6, capacity=300)
-    pool = hsa.SlotPool(slots=6, capacity=240, ttl=30)
+    cache = hsa.PagedKVCache(model, pages=20, pages_per_user=4, max_users=4)
+    pool = hsa.KvPool(pages=20, max_rows=240, ttl=30)
     history, requests = _stream(np.random.default_rng(5), users=14, D=D, requests=80)
     rep = Replayer(model, cache, pool, history, window=200)
     served = []
@@ -44,6 +44,9 @@ def test_replay_matches_one_shot_encodes():
     stats = pool.stats()
     say(f"  replay: {len(served)} requests in {rep.batches} batches, {rep.rows_sent} rows sent; {stats}")
     assert all(stats[k] > 0 for k in ("hits", "rebuild_new", "rebuild_stale", "rebuild_full", "evictions"))
+    held = [pool.lookup(u) for u in history]
+    assert all(p == (n + 63) // 64 for n, p in held)
+    assert stats["pages_in_use"] == sum(p for _, p in held)
     worst = 0.0
     for s in served:
         r = s.request
