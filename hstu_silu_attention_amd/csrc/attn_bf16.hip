@@ -103,13 +103,16 @@ __device__ __forceinline__ float silu_bias(float x, float nlog2e, float bias) {
   return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(__builtin_fmaf(x, nlog2e, bias)));
 }
 
-// Relative bias (REL): each weight gains rel[h][pos_i - pos_j] after its SiLU. The head's
-// table is staged in LDS (kTabPad zero entries, then the table from the 16-byte-aligned
-// address at or before its start, mis entries early), so entry d sits at
-// tab[kTabPad + mis + d]; a lane reads its 16 weights' entries there. Wholly masked halves
-// read the zero pad instead, so every step stays branch-free.
-constexpr int kTabPad = 64, kTabEntries = 8192;
-static_assert(kTabPad + ((kRelMaxLen + 32 + 7 + 7) / 8 + 63) / 64 * 512 <= kTabEntries, "table must fit");
+// Relative bias (REL): each weight gains rel[h][pos_i - pos_j] after its SiLU. The table is
+// read from the 16-byte-aligned address at or before the head's row (mis entries early).
+// LDS holds a static part, kTabPad zero entries and then the row's first entries (entry d
+// at tab[kTabPad + mis + d], for the diagonal pass and a candidate's own key), and per wave
+// a ring of three slices of kSlice entries: for key block b a wave's weights only need
+// the 96 consecutive entries d in [q - 64b - 63, q + 31 - 64b] (q: the wave's first query
+// position), and the slice of block b + 2 is loaded beside K(b + 2), into the slot of
+// block b - 1. A lane reads its 16 weights' entries there; wholly masked halves read the
+// zero pad instead, so every step stays branch-free. Any max_len works.
+constexpr int kTabPad = 64, kSlice = 512, kRing = 3, kTabStatic = kTabPad + kSlice;
 
 // dh = 64 fits three waves per SIMD (under 168 registers; 32 KB of K/V slots, 48 KB with
 // a relative table, per workgroup), which hides more of each wave's latency; dh = 128
@@ -125,7 +128,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DH == 64 ? 
 void attn_kernel(AttnArgs a) {
   using C = AttnTile<DH>;
   __shared__ __attribute__((aligned(16))) u16 ks0[C::SLOT], ks1[C::SLOT], vs0[C::SLOT], vs1[C::SLOT];
-  __shared__ __attribute__((aligned(16))) u16 tab[REL ? kTabEntries : 8];
+  __shared__ __attribute__((aligned(16))) u16 tab[REL ? kTabStatic + C::WAVES * kRing * kSlice : 8];
 
   const AttnItem it = a.items[blockIdx.x];
   if (it.nq <= 0) return;
@@ -186,15 +189,14 @@ void attn_kernel(AttnArgs a) {
     return make_int2(tbl[min(max(c0, 0), last_pg)], tbl[min(max(c0 + 1, 0), last_pg)]);
   };
   // relative bias table of this head, read from the 16-byte-aligned address at or before it
-  int mis = 0, tab_chunks = 0;
+  // (offsets before it, or past the whole table, read as zero)
+  int mis = 0;
   i32x4 rel_src = {0, 0, 0, 0};
   if (REL) {
     const uintptr_t hb = (uintptr_t)((const u16*)a.rel + (size_t)head * a.max_len);
     const uintptr_t ab = hb & ~(uintptr_t)15;
     const uintptr_t end = (uintptr_t)((const u16*)a.rel + (size_t)(D / DH) * a.max_len);
     mis = (int)((hb - ab) / 2);
-    // entries mis .. mis + key_end + 32 cover every relative position a step looks up
-    tab_chunks = (mis + key_end + 32 + 7) / 8;
     rel_src = buffer_desc((const void*)ab, (int)(end - ab));
   }
 
@@ -274,11 +276,25 @@ void attn_kernel(AttnArgs a) {
   // Relative bias of the weights of query block qb in half h, elements e0 .. e0 + 7
   // (element e <-> key 8*(e/4) + 4*hi + e%4 of the half, query row l32): pos_q - pos_k is
   // wf + 32*qb - 32*h + l32 - key for history rows, key_end - 32*h - key for candidates.
+  // slice of key block b: the 16-byte chunk of the aligned row where it starts (floor
+  // division: negative chunks read as zero), and its slot in this wave's ring
+  const int qfirst = cand ? key_end : wf;
+  auto slice_chunk = [&](int b) { return (mis + qfirst - 64 * b - 63) >> 3; };
+  const int ring = kTabStatic + wv * kRing * kSlice;   // this wave's ring, in entries of tab
+  auto slice_slot = [&](int b) { return ring + (b % kRing) * kSlice; };
+  auto load_slice = [&](int b) {
+    if (REL)
+      lds_load16(rel_src, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)(tab + slice_slot(b))),
+                 (slice_chunk(b) + lane) * 16);
+  };
+  const int lane_off = (cand ? 0 : l32) - 4 * hi;
   auto rel_bias = [&](int h, int qb, int e0, float (&r)[8]) {
     if (!REL) return;
     const int d0 = cand ? key_end - 32 * h : wf + 32 * qb - 32 * h;
-    const int tb = bias(h, qb) == 0.0f ? kTabPad + mis + d0 : 31;   // masked: the zero pad
-    const u16* tl = tab + tb + (cand ? 0 : l32) - 4 * hi;
+    const int b = h >> 1;
+    // an integer select (a pointer select became a branch): masked halves read the zero pad
+    const int at = bias(h, qb) == 0.0f ? slice_slot(b) + d0 + mis - 8 * slice_chunk(b) : 31;
+    const u16* tl = tab + at + lane_off;
 #pragma unroll
     for (int e = e0; e < e0 + 8; ++e)
       r[e - e0] = __uint_as_float((uint32_t)tl[-(8 * (e >> 2) + (e & 3))] << 16);
@@ -342,9 +358,11 @@ void attn_kernel(AttnArgs a) {
   }
   if (REL) {
     if (tid < kTabPad / 8) *reinterpret_cast<uint4*>(tab + 8 * tid) = make_uint4(0, 0, 0, 0);
-    const uint32_t tab_lds = (uint32_t)(uintptr_t)(lds_void*)(tab + kTabPad);
-    for (int j = wv; j * 64 < tab_chunks; j += C::WAVES)   // 64 chunks of 8 entries per load
-      lds_load16(rel_src, __builtin_amdgcn_readfirstlane(tab_lds + j * 1024), (j * 64 + lane) * 16);
+    // the static part: 64 chunks = the row's first 512 - mis entries
+    if (wv == 0)
+      lds_load16(rel_src, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)(tab + kTabPad)), lane * 16);
+    load_slice(0);
+    load_slice(1);
   }
   wait_loads();
   __syncthreads();
@@ -369,6 +387,7 @@ void attn_kernel(AttnArgs a) {
     body(2 * b + 1, kn, vb, sB, wB, sA, wA, [&] {                  // K rows of half 2b+2, V of half 2b
       load_k(kb, b + 2, pk);           // past the last block these rows read as zero
       load_v(vp, b + 1, pv);
+      load_slice(b + 2);               // into the slot of block b - 1, last read in step 2b
     });
   };
   int b = 0;

@@ -301,7 +301,6 @@ hstu_status validate_encode(EncodeCall& c, int32_t* keys) {
     if (!w.w_uvqk || !w.w_out) return HSTU_ERR_NULL;
     if (!aligned16(w.w_uvqk) || !aligned16(w.w_out) || !aligned16(w.pos_bias) || !aligned16(w.rel_bias))
       return HSTU_ERR_ALIGN;
-    if (w.rel_bias && d->dtype == HSTU_BF16 && d->max_len > hstu::kRelMaxLen) return HSTU_ERR_SHAPE;
   }
   const Layout& lay = c.lay;
   if ((lay.Nu > 0 && (!c.uih || !c.uih_out)) || (lay.Nc > 0 && (!c.cand || !c.cand_out))) return HSTU_ERR_NULL;

@@ -138,10 +138,6 @@ struct AttnArgs {
   int32_t max_len;
 };
 
-// Largest max_len of a bfloat16 model with a relative bias: the attention stages a
-// head's table (plus a zero pad) in 16 KB of LDS.
-constexpr int kRelMaxLen = 7600;
-
 struct OutArgs {
   const void* aout;      // [T_pad][3D] A operand [U | O | U*O] (bfloat16: U | O read)
   const void* w;         // [D][3D]

@@ -182,11 +182,13 @@ def test_encode_rejects_before_launch():
     assert a.call() == ERR_ALIGN
 
 
-def test_encode_rejects_relative_bias_past_the_staged_table():
-    """A bfloat16 model with a relative bias stages each head's table in LDS: max_len <= 7600."""
-    a = FakeArgs(max_len=7601)
+def test_encode_takes_relative_bias_at_any_max_len():
+    """The attention streams the relative table through LDS a slice per key block, so a
+    bfloat16 model with a relative bias takes any max_len: validation passes the table
+    (and here stops at the workspace, before any launch)."""
+    a = FakeArgs(max_len=65536)
     a.w = [hsa.HstuLayerWeights(0x10000, 0x20000, 0, 0x38000) for _ in range(2)]
-    assert a.call() == ERR_SHAPE
+    assert a.call(ws_bytes=a.ws_bytes - 1) == ERR_WORKSPACE
 
 
 def test_encode_capacity_and_slots_leave_cached_len_unchanged():

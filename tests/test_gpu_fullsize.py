@@ -216,13 +216,15 @@ def test_streaming_workload_paged_matches_slot():
     say(f"  streaming workload, paged cache ({B * ppu} pages) = slot cache, bit for bit")
 
 
-def test_long_workload_layerwise_sampled_rows():
-    """16 layers, 4 users with UIH 8K-16K, 2048 candidates, 8 heads (dh 64). The full call
-    equals the chain of 16 one-layer calls bit for bit; layers 0, 7 and 15 are then checked
-    row by row against the oracle on sampled history and candidate rows of every user, fed
-    with the GPU's own input to that layer."""
+@pytest.mark.parametrize("name", ["long_uih16k_c2k", "long_uih16k_c2k_rel"])
+def test_long_workload_layerwise_sampled_rows(name):
+    """16 layers, 4 users with UIH 8K-16K, 2048 candidates, 8 heads (dh 64), with the
+    absolute position table, and in the original HSTU form with a relative table over
+    positions up to 16384. The full call equals the chain of 16 one-layer calls bit for
+    bit; layers 0, 7 and 15 are then checked row by row against the oracle on sampled
+    history and candidate rows of every user, fed with the GPU's own input to that layer."""
     torch = torch_cuda()
-    wl = workloads.make_workload("long_uih16k_c2k")
+    wl = workloads.make_workload(name)
     D = wl.d_model
     full_u, full_c = gpu_encode(wl, keep_device=True)
     full_u, full_c = to_np(full_u), to_np(full_c)
@@ -238,7 +240,8 @@ def test_long_workload_layerwise_sampled_rows():
     worst = 0.0
     for l in (0, 7, 15):
         p = wl.params[l]
-        w1, w2, pos = (a.astype(np.float64) for a in (p.w1, p.w2, p.pos))
+        f64 = lambda a: None if a is None else a.astype(np.float64)
+        w1, w2, pos, rel = f64(p.w1), f64(p.w2), f64(p.pos), f64(getattr(p, "rel", None))
         xin_u, xin_c = to_np(xs[l][0]), to_np(xs[l][1])
         xo_u, xo_c = to_np(xs[l + 1][0]), to_np(xs[l + 1][1])
         for b in range(wl.users):
@@ -248,11 +251,11 @@ def test_long_workload_layerwise_sampled_rows():
             yu, yc, _, _ = oracle.layer_user(xin_u[uo[b]:uo[b + 1]], xin_c[co[b]:co[b + 1]], w1, w2, pos,
                                              k_cached=np.zeros((0, D)), v_cached=np.zeros((0, D)),
                                              heads=wl.heads, max_len=wl.max_len, bf16=True,
-                                             uih_rows=rows, cand_rows=crows)
+                                             uih_rows=rows, cand_rows=crows, rel=rel)
             gu_rows = xo_u[uo[b] + rows]
             gc_rows = xo_c[co[b] + crows]
             eu = float(np.max(np.abs(gu_rows - yu)) / np.max(np.abs(yu)))
             ec = float(np.max(np.abs(gc_rows - yc)) / np.max(np.abs(yc)))
             worst = max(worst, eu, ec)
-        say(f"  long: layer {l} worst sampled normwise error so far {worst:.3e}")
+        say(f"  {name}: layer {l} worst sampled normwise error so far {worst:.3e}")
     assert worst <= BF16_TOL

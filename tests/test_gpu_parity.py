@@ -83,12 +83,34 @@ def test_f32_relative_bias(D, H):
     check(wl, gu, gc, "f64", F32_TOL, label=f"f32 relative bias D={D} H={H}")
 
 
-def test_bf16_relative_bias_long_table():
-    """One long history: the staged relative table spans several thousand positions."""
-    wl = workloads.make_custom(seed=977, dtype="bf16", layers=1, d_model=256, heads=4, max_len=7600,
-                               uih_lengths=[4500], cand_lengths=[2], position="relative", rel_std=0.3)
-    gu, gc = gpu_encode(wl)
-    check(wl, gu, gc, "bf16", BF16_TOL, label="bf16 relative bias, 4500 history rows")
+@pytest.mark.parametrize("D,H,max_len,n,m", [(256, 4, 7600, 4500, 0), (512, 4, 12000, 9000, 0),
+                                              (256, 4, 12000, 1500, 8001)])
+def test_bf16_relative_bias_long_table(D, H, max_len, n, m):
+    """Long histories with a relative table of thousands of positions (dh 64 and 128; a
+    table longer than one workgroup could hold in LDS; a cached prefix that puts the
+    history's positions past 8000): the attention streams the table a slice per key
+    block."""
+    torch = torch_cuda()
+    wl = workloads.make_custom(seed=977 + n, dtype="bf16", layers=1, d_model=D, heads=H, max_len=max_len,
+                               uih_lengths=[n, 77], cand_lengths=[2, 130], cached_lengths=[m, 0],
+                               position="relative", rel_std=0.3)
+    if m == 0:
+        gu, gc = gpu_encode(wl)
+        check(wl, gu, gc, "bf16", BF16_TOL, label=f"bf16 relative bias, {n} history rows, max_len {max_len}")
+        return
+    import oracle
+    model = make_model(torch, wl)
+    cache = hsa.KVCache(model, slots=2, capacity=m + n)
+    gu, gc = _fill_and_encode(wl, model, cache)
+    ocache = oracle.OracleCache(np.zeros((1, 2, m + n, D)), np.zeros((1, 2, m + n, D)), np.arange(2),
+                                np.zeros(2, np.int64))
+    empty = np.zeros((0, D), np.float32)
+    _, _, ocache = oracle_encode(wl, "bf16", cache=ocache, uih=wl.prefix, uih_lengths=wl.cached_lengths,
+                                 cand=empty, cand_lengths=np.zeros(2, np.int64))
+    ru, rc, _ = oracle_encode(wl, "bf16", cache=ocache)
+    eu, ec = normwise_per_user(gu, ru, wl.uih_lengths), normwise_per_user(gc, rc, wl.cand_lengths)
+    say(f"  bf16 relative bias after a {m}-row cached prefix: uih {eu:.3e} cand {ec:.3e}")
+    assert eu <= BF16_TOL and ec <= BF16_TOL
 
 
 def test_bf16_single_layer_many_tiles():

@@ -74,6 +74,10 @@ WORKLOADS: Dict[str, WorkloadSpec] = {
         # form: relative position bias only
         WorkloadSpec("d512_uih2k_c2k_rel", 3, 8, "bf16", 16, ("lognormal", 2000, 0.5, 512, 4096), 0, 2048,
                      512, 4, 4097, "relative"),
+        # the long-history workload (same seed: same lengths and tokens) in the original HSTU
+        # form: relative position bias only, over histories of 8K-16K rows
+        WorkloadSpec("long_uih16k_c2k_rel", 5, 16, "bf16", 4, ("uniform", 8192, 16384), 0, 2048, 512, 8, 16385,
+                     "relative"),
         # the headline workload's users and event counts in the original HSTU input form:
         # each event's context and action embeddings interleaved, two tokens per event
         WorkloadSpec("d512_uih2k_c2k_interleaved", 3, 8, "bf16", 16, ("lognormal", 2000, 0.5, 512, 4096), 0,
