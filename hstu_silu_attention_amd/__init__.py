@@ -19,7 +19,7 @@ from typing import List, Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = ["HSTU_F32", "HSTU_BF16", "HstuError", "load_library", "library_path",
-           "hstu_abi_version", "hstu_status_string", "hstu_workspace_size", "hstu_flops",
+           "hstu_abi_version", "hstu_status_string", "hstu_workspace_size", "hstu_flops", "hstu_attention_plan",
            "hstu_encode", "hstu_encode_static", "encode_static", "HSTU_ERR_TOO_LARGE", "hstu_pack_uih", "hstu_timing_enable", "hstu_timing_select", "hstu_timing_read", "KERNEL_KINDS",
            "PACK_MODES", "Model", "KVCache", "ScoringHead", "encode", "pack_uih", "score", "hstu_score",
            "HstuDims", "HstuLayerWeights", "HstuKvCache", "HstuHeadLayer", "KvPool", "PagedKVCache", "POOL_STATS",
@@ -62,7 +62,9 @@ class HstuError(RuntimeError):
 
 
 def library_path() -> str:
-    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhstu.so")
+    """The in-tree libhstu.so, or the library named by $HSTU_LIBRARY (e.g. the sanitizer
+    build, libhstu_asan.so)."""
+    return os.environ.get("HSTU_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhstu.so")
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -88,6 +90,9 @@ def load_library() -> ctypes.CDLL:
     lib.hstu_flops.restype = ctypes.c_int32
     lib.hstu_flops.argtypes = [P(HstuDims), ctypes.c_int32, i32p, i32p, i32p, P(ctypes.c_uint64),
                                P(ctypes.c_uint64)]
+    lib.hstu_attention_plan.restype = ctypes.c_int32
+    lib.hstu_attention_plan.argtypes = [P(HstuDims), ctypes.c_int32, i32p, i32p, i32p, i32p, P(ctypes.c_int64),
+                                        ctypes.c_int64]
     lib.hstu_timing_enable.restype = ctypes.c_int32
     lib.hstu_timing_enable.argtypes = [ctypes.c_int32]
     lib.hstu_timing_select.restype = ctypes.c_int32
@@ -164,6 +169,23 @@ def hstu_flops(dims: HstuDims, B: int, uih_offsets, cand_offsets, cached_len=Non
     alg, form = ctypes.c_uint64(0), ctypes.c_uint64(0)
     st = load_library().hstu_flops(ctypes.byref(dims), B, uo, co, cl, ctypes.byref(alg), ctypes.byref(form))
     return int(st), int(alg.value), int(form.value)
+
+
+def hstu_attention_plan(dims: HstuDims, B: int, uih_offsets, cand_offsets, cached_len=None):
+    """Returns (status, codes): the attention's work item of every workgroup, as int64
+    (user << 32) | (query block << 8) | (head << 1) | is_candidate, -1 for none."""
+    _, uo = _i32(uih_offsets)
+    _, co = _i32(cand_offsets)
+    _, cl = _i32(cached_len)
+    lib = load_library()
+    grid = ctypes.c_int32(0)
+    st = int(lib.hstu_attention_plan(ctypes.byref(dims), B, uo, co, cl, ctypes.byref(grid), None, 0))
+    if st != HSTU_OK:
+        return st, None
+    codes = np.empty(max(grid.value, 1), dtype=np.int64)
+    st = int(lib.hstu_attention_plan(ctypes.byref(dims), B, uo, co, cl, ctypes.byref(grid),
+                                     codes.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), codes.shape[0]))
+    return st, codes[:grid.value]
 
 
 def hstu_encode(dims: HstuDims, B: int, uih_offsets, cand_offsets, uih_ptr: int, cand_ptr: int,

@@ -593,6 +593,35 @@ hstu_status hstu_workspace_size(const hstu_dims* d, int32_t B, const int32_t* ui
   return HSTU_OK;
 }
 
+hstu_status hstu_attention_plan(const hstu_dims* d, int32_t B, const int32_t* uih_offsets,
+                                const int32_t* cand_offsets, const int32_t* cached_len, int32_t* grid,
+                                int64_t* codes, int64_t capacity) {
+  hstu_status st = check_dims(d);
+  if (st != HSTU_OK) return st;
+  if (!grid) return HSTU_ERR_NULL;
+  st = check_offsets(B, uih_offsets, cand_offsets);
+  if (st != HSTU_OK) return st;
+  const Layout lay = make_layout(d, B, uih_offsets, cand_offsets);
+  std::vector<UserRec> users((size_t)B);
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t m = cached_len ? cached_len[b] : 0;
+    if (m < 0) return HSTU_ERR_CAPACITY;
+    users[b] = UserRec{uih_offsets[b], uih_offsets[b + 1] - uih_offsets[b], cand_offsets[b],
+                       cand_offsets[b + 1] - cand_offsets[b], m, 0, 0, 0};
+  }
+  std::vector<PlanGroup> groups((size_t)lay.groups);
+  std::vector<PlanItem> items((size_t)lay.ntiles);
+  std::vector<hstu::ItemCode> out((size_t)hstu::kXcds * lay.ntiles);
+  const int g = plan_attention(users.data(), B, d->heads, hstu::attn_block_rows(d->dtype), groups.data(),
+                               items.data(), out.data());
+  *grid = g;
+  if (!codes) return HSTU_OK;
+  if (capacity < g) return HSTU_ERR_WORKSPACE;
+  for (int w = 0; w < g; ++w)
+    codes[w] = out[w].user < 0 ? -1 : ((int64_t)out[w].user << 32) | (uint32_t)out[w].code;
+  return HSTU_OK;
+}
+
 hstu_status hstu_flops(const hstu_dims* d, int32_t B, const int32_t* uih_offsets,
                        const int32_t* cand_offsets, const int32_t* cached_len,
                        uint64_t* algorithmic_flops, uint64_t* formula_flops) {

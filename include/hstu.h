@@ -187,6 +187,21 @@ hstu_status hstu_flops(const hstu_dims* d, int32_t B, const int32_t* uih_offsets
                        const int32_t* cand_offsets, const int32_t* cached_len,
                        uint64_t* algorithmic_flops, uint64_t* formula_flops);
 
+/* The attention's work plan of one hstu_encode call (host-only; launches nothing), for
+ * inspection and tests. A work item is (user, head, up to Q query rows of one kind) with
+ * Q = 128 in bfloat16 and 64 in float32. Items of one (user, head) go whole to one of
+ * 8 bins (one per XCD; workgroup w runs on XCD w % 8), groups largest first on the least
+ * loaded bin, and inside a bin the items run longest first. Writes *grid (the
+ * attention's workgroup count, 8 x the longest bin) and, when codes is not NULL and
+ * capacity >= *grid, codes[w] for workgroup w: -1 for no work, else
+ * (user << 32) | (query block << 8) | (head << 1) | is_candidate, the query block
+ * counting Q-row blocks of the user's history (or candidate) rows. cached_len may be
+ * NULL (all m = 0). Errors: as hstu_workspace_size; HSTU_ERR_WORKSPACE if codes is not
+ * NULL and capacity < *grid (then *grid is still written). */
+hstu_status hstu_attention_plan(const hstu_dims* d, int32_t B, const int32_t* uih_offsets,
+                                const int32_t* cand_offsets, const int32_t* cached_len, int32_t* grid,
+                                int64_t* codes, int64_t capacity);
+
 /* Encode one jagged batch through all layers.
  *  uih        device [uih_offsets[B]][D]   new history tokens of every user
  *  cand       device [cand_offsets[B]][D]  candidate tokens
