@@ -303,8 +303,8 @@ class KVCache:
 class PagedKVCache:
     """Caller-owned paged cache: k, v [layers][pages][64][D] on the device, the device page
     table [max_users][pages_per_user] int32 (row b: user b of the next call) and host int32
-    ``cached_len`` per user of the next call. ``set_table`` copies host rows into the device
-    table on the current stream."""
+    ``cached_len`` per user of the next call. ``set_table`` queues a copy of host rows into
+    the device table on the current stream (ordered after the kernels queued before it)."""
 
     def __init__(self, model: Model, pages: int, pages_per_user: int, max_users: int, device="cuda"):
         torch = _torch()
@@ -321,7 +321,9 @@ class PagedKVCache:
         rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
         if rows.ndim != 2 or rows.shape[1] != self.pages_per_user or rows.shape[0] > self.max_users:
             raise ValueError("page table rows must be [B <= max_users][pages_per_user]")
-        self.table[:rows.shape[0]].copy_(torch.from_numpy(rows), non_blocking=False)
+        # staged in pinned memory: the copy is queued on the stream without waiting for the
+        # host, after the kernels queued before it (torch keeps the staging block until then)
+        self.table[:rows.shape[0]].copy_(torch.from_numpy(rows).pin_memory(), non_blocking=True)
 
     def struct(self) -> HstuKvCache:
         self.cached_len = np.ascontiguousarray(self.cached_len, dtype=np.int32)

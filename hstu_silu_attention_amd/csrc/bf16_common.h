@@ -76,14 +76,15 @@ __device__ __forceinline__ float2 group_stats(uint4 q) {
 // one at a time by the pairwise update of Chan, Golub and LeVeque (1979): merging n
 // values (mean ma, M2 Ma) with 128 more (mb, Mb) gives mean ma + d * 128 / (n + 128) and
 // M2 Ma + Mb + d^2 * n * 128 / (n + 128), with d = mb - ma. Returns {mean, M2 / D}.
+// One step of that merge: {mean, M2} of groups 0..i-1 and group i's {mean, M2}.
+__device__ __forceinline__ void merge_group_step(float& mean, float& m2, float2 b, int i) {
+  const float d = b.x - mean, f = 1.0f / (float)(i + 1);   // 128 / (n + 128) with n = 128 i
+  mean = __builtin_fmaf(d, f, mean);
+  m2 += b.y + d * d * (128.0f * (float)i * f);
+}
 __device__ __forceinline__ float2 merge_group_stats(const float2* g, int groups) {
   float mean = g[0].x, m2 = g[0].y;
-  for (int i = 1; i < groups; ++i) {
-    const float2 b = g[i];
-    const float d = b.x - mean, f = 1.0f / (float)(i + 1);   // 128 / (n + 128) with n = 128 i
-    mean = __builtin_fmaf(d, f, mean);
-    m2 += b.y + d * d * (128.0f * (float)i * f);
-  }
+  for (int i = 1; i < groups; ++i) merge_group_step(mean, m2, g[i], i);
   return make_float2(mean, m2 / (float)(128 * groups));
 }
 

@@ -22,11 +22,12 @@ namespace {
 // needs one barrier; staging through registers lets it form the gate columns of
 // [U | O | U*O] from U and O on the way. The projection (gemm_tile_dma) loads its
 // operands, the layer input rows as stored and W1, straight into LDS.
-template <int BM_, int BN_, int WM_, int WN_>
+template <int BM_, int BN_, int WM_, int WN_, int BK_ = 64, int STAGES_ = 2>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
   static constexpr int NT = 64 * WM * WN;          // threads
-  static constexpr int BK = 64, LDK = BK + 8;
+  static constexpr int BK = BK_, LDK = BK + 8;
+  static constexpr int STAGES = STAGES_;           // LDS stages of the projection's ring
   static constexpr int TM = BM / WM, TN = BN / WN, MI = TM / 32, NI = TN / 32;
   static constexpr int RSTEP = NT / 8;             // rows between a thread's chunks
   static constexpr int AC = BM * BK / 8 / NT;      // 16-byte A chunks per thread per step
@@ -198,19 +199,24 @@ __device__ __forceinline__ void lds_load16(uint32_t lds_addr, const void* src) {
 }
 
 // The projection's main loop with its operands loaded straight into LDS. A stage holds
-// BM A rows then BN W rows of BK = 64 elements, unpadded (128 bytes a row); the 16-byte
-// chunk c of row r sits at slot c ^ ((r >> 1) & 7), which keeps the fragment reads of
-// 16 consecutive rows on distinct banks. Load j of a stage (64 lanes, 8 rows) fills its
-// rows 8j..8j+7; wave w issues loads w, w + WAVES, ... Each step waits for its own
-// stage (issued one whole step earlier), synchronises, requests the next stage into the
-// other buffer, then runs its MFMAs.
+// BM A rows then BN W rows of BK elements (BK = 64 or 32), unpadded (RB = 2 * BK bytes a
+// row). The 16-byte chunk c of row r sits at slot c ^ swz(r), swz(r) = (r / (256 / RB)) %
+// (RB / 16): rows 256 / RB apart start on the same bank, and swz gives the RB / 16 such
+// rows among any 16 consecutive ones distinct slots, so the fragment reads of 16
+// consecutive rows hit distinct banks. Load j of a stage (64 lanes, 1 KB) fills its rows
+// (1024 / RB) j .. (1024 / RB) (j + 1) - 1; wave w issues loads w, w + WAVES, ... The
+// stages form a ring of STAGES: step t waits for its own stage (issued STAGES - 1 steps
+// earlier; the loads of later steps stay in flight), synchronises, requests step
+// t + STAGES - 1 into the stage step t - 1 used, then runs its MFMAs.
 template <typename C>
 __device__ __forceinline__ void gemm_tile_dma(const UvqkArgs& a, int row0, int col0, f32x16 (&acc)[C::MI][C::NI],
                                               u16* smem) {
-  static_assert(C::BK == 64 && (C::BM + C::BN) % (8 * C::NT / 64) == 0, "whole loads per wave");
+  constexpr int BK = C::BK, S = C::STAGES, RB = 2 * BK, CPRW = RB / 16, RPL = 1024 / RB;
   constexpr int WAVES = C::NT / 64;
-  constexpr int LOADS = (C::BM + C::BN) / 8 / WAVES;     // per wave per stage
+  static_assert((BK == 64 || BK == 32) && S >= 2 && (C::BM + C::BN) % (RPL * WAVES) == 0, "whole loads per wave");
+  constexpr int LOADS = (C::BM + C::BN) / RPL / WAVES;   // per wave per stage
   constexpr int SROWS = C::BM + C::BN;                   // rows of a stage
+  auto swz = [](int r) { return (r / (256 / RB)) & (CPRW - 1); };
   const int D = a.D, K = D;
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wv / C::WN, wn = wv % C::WN, l32 = lane & 31, hi = lane >> 5;
@@ -218,8 +224,8 @@ __device__ __forceinline__ void gemm_tile_dma(const UvqkArgs& a, int row0, int c
   const u16* src[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
-    const int r = 8 * (wv + WAVES * i) + lane / 8;          // row of the stage
-    const int c = (lane & 7) ^ ((r >> 1) & 7);              // chunk that belongs in this slot
+    const int r = RPL * (wv + WAVES * i) + lane / CPRW;    // row of the stage
+    const int c = (lane % CPRW) ^ swz(r);                  // chunk that belongs in this slot
     if (r < C::BM) {
       const int row = min(row0 + r, a.T - 1);
       src[i] = (row < a.Nu ? (const u16*)a.x_lo + (size_t)row * D : (const u16*)a.x_hi + (size_t)(row - a.Nu) * D) + c * 8;
@@ -231,9 +237,8 @@ __device__ __forceinline__ void gemm_tile_dma(const UvqkArgs& a, int row0, int c
   auto issue = [&](int stage, int k0) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i)
-      lds_load16(lds0 + stage * SROWS * 128 + (wv + WAVES * i) * 1024, src[i] + k0);
+      lds_load16(lds0 + stage * SROWS * RB + (wv + WAVES * i) * 1024, src[i] + k0);
   };
-  auto wait_loads = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 #pragma unroll
   for (int i = 0; i < C::MI; ++i)
 #pragma unroll
@@ -241,29 +246,35 @@ __device__ __forceinline__ void gemm_tile_dma(const UvqkArgs& a, int row0, int c
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  const int sw = (l32 >> 1) & 7;                             // this lane's rows' chunk swizzle
-  const int nstep = K / C::BK;
-  issue(0, 0);
+  const int sw = swz(l32);                                   // this lane's rows' chunk swizzle
+  const int nstep = K / BK;
+#pragma unroll
+  for (int t = 0; t + 1 < S; ++t)
+    if (t < nstep) issue(t, t * BK);
   for (int t = 0; t < nstep; ++t) {
-    wait_loads();
-    __syncthreads();                                          // stage t & 1 is complete; stage (t + 1) & 1 is free
-    if (t + 1 < nstep) issue((t + 1) & 1, (t + 1) * C::BK);
-    const u16* sa = smem + (t & 1) * SROWS * 64 + (wm * C::TM + l32) * 64;
-    const u16* sb = smem + (t & 1) * SROWS * 64 + (C::BM + wn * C::TN + l32) * 64;
+    // stage t has landed once at most the loads of the steps after it are outstanding
+    if (S > 2 && t + 1 < nstep)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS * (S - 2)) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();                                          // stage t % S is complete; stage (t - 1) % S is free
+    if (t + S - 1 < nstep) issue((t + S - 1) % S, (t + S - 1) * BK);
+    const u16* sa = smem + (t % S) * SROWS * BK + (wm * C::TM + l32) * BK;
+    const u16* sb = smem + (t % S) * SROWS * BK + (C::BM + wn * C::TN + l32) * BK;
     bf16x8 af[2][C::MI], bw[2][C::NI];
     auto rd = [&](const u16* p, int kk) { return as_bf16x8(*reinterpret_cast<const uint4*>(p + (((2 * kk + hi) ^ sw) * 8))); };
 #pragma unroll
-    for (int i = 0; i < C::MI; ++i) af[0][i] = rd(sa + i * 32 * 64, 0);
+    for (int i = 0; i < C::MI; ++i) af[0][i] = rd(sa + i * 32 * BK, 0);
 #pragma unroll
-    for (int j = 0; j < C::NI; ++j) bw[0][j] = rd(sb + j * 32 * 64, 0);
+    for (int j = 0; j < C::NI; ++j) bw[0][j] = rd(sb + j * 32 * BK, 0);
 #pragma unroll
-    for (int kk = 0; kk < C::BK / 16; ++kk) {
+    for (int kk = 0; kk < BK / 16; ++kk) {
       const int cur = kk & 1, nxt = cur ^ 1;
-      if (kk + 1 < C::BK / 16) {
+      if (kk + 1 < BK / 16) {
 #pragma unroll
-        for (int i = 0; i < C::MI; ++i) af[nxt][i] = rd(sa + i * 32 * 64, kk + 1);
+        for (int i = 0; i < C::MI; ++i) af[nxt][i] = rd(sa + i * 32 * BK, kk + 1);
 #pragma unroll
-        for (int j = 0; j < C::NI; ++j) bw[nxt][j] = rd(sb + j * 32 * 64, kk + 1);
+        for (int j = 0; j < C::NI; ++j) bw[nxt][j] = rd(sb + j * 32 * BK, kk + 1);
       }
 #pragma unroll
       for (int i = 0; i < C::MI; ++i)
@@ -275,7 +286,7 @@ __device__ __forceinline__ void gemm_tile_dma(const UvqkArgs& a, int row0, int c
       constexpr unsigned MFMA = 0x008, DS_READ = 0x100;
       __builtin_amdgcn_sched_group_barrier(DS_READ, kRead, 0);
 #pragma unroll
-      for (int kk = 0; kk + 1 < C::BK / 16; ++kk)
+      for (int kk = 0; kk + 1 < BK / 16; ++kk)
 #pragma unroll
         for (int i = 0; i < (kMfma > kRead ? kMfma : kRead); ++i) {
           if (i < kRead) __builtin_amdgcn_sched_group_barrier(DS_READ, 1, 0);
@@ -290,26 +301,48 @@ __device__ __forceinline__ void gemm_tile_dma(const UvqkArgs& a, int row0, int c
 template <typename C>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::WAVES_PER_EU, C::WAVES_PER_EU)))
 void uvqk_kernel(UvqkArgs a) {
-  constexpr int SMEM = 2 * (C::BM + C::BN) * 64 > C::BM * (C::BN + 8) ? 2 * (C::BM + C::BN) * 64 : C::BM * (C::BN + 8);
+  constexpr int RING = C::STAGES * (C::BM + C::BN) * C::BK, STAGED = C::BM * (C::BN + 8);
+  constexpr int SMEM = RING > STAGED ? RING : STAGED;
   __shared__ __attribute__((aligned(1024))) u16 smem[SMEM];
   const int D = a.D, N = 4 * D, ncol = N / C::BN;
   const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
   const int row0 = (tile / ncol) * C::BM, col0 = (tile % ncol) * C::BN;
   __shared__ float row_mean[C::BM];
   __shared__ float2 row_scale[C::BM];                // {-log2(e) / sigma, sigma}, sigma = sqrt(var + eps)
+  __shared__ int row_pos[C::BM];                     // position of each tile row (its bias row)
+  __shared__ __attribute__((aligned(16))) float col_sum[256];   // W1 column sums of the tile's columns
+  static_assert(C::BN <= 256 && C::NT >= C::BM, "one tile row per thread; one load of column sums");
+  // The epilogue's inputs that depend only on the tile are requested before the main
+  // loop, so their latency hides under it: the row's group statistics (the first four
+  // groups in registers; a wider row reads the rest in the epilogue) and its position,
+  // and the W1 column sums (one 64-lane LDS load by wave 0, issued ahead of its first
+  // stage, whose wait then covers it).
+  const int groups = D / 128;
+  const bool has_row = threadIdx.x < C::BM;
+  const int rr = min(row0 + (int)threadIdx.x, a.T - 1);
+  float2 stp[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) stp[g] = has_row && g < groups ? a.st[(size_t)rr * groups + g] : make_float2(0.0f, 0.0f);
+  const int posp = has_row ? a.row_info[rr].y : 0;
+  if (threadIdx.x < 64)
+    lds_load16((uint32_t)(uintptr_t)(lds_void*)col_sum, a.cs + col0 + min(4 * (int)threadIdx.x, C::BN - 4));
   f32x16 acc[C::MI][C::NI];
   gemm_tile_dma<C>(a, row0, col0, acc, smem);
 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int wm = wv / C::WN, wn = wv % C::WN, l32 = lane & 31, hi = lane >> 5;
   // Row mean and variance from the per-128-column group statistics, merged in column
-  // order.
-  for (int r = threadIdx.x; r < C::BM; r += C::NT) {
-    const float2 mv = merge_group_stats(a.st + (size_t)min(row0 + r, a.T - 1) * (D / 128), D / 128);
-    const float mean = mv.x;
-    const float sigma = sqrtf(mv.y + kNormEps);
-    row_mean[r] = mean;
-    row_scale[r] = make_float2(-1.4426950408889634f / sigma, sigma);
+  // order (as merge_group_stats does).
+  if (has_row) {
+    float mean = stp[0].x, m2 = stp[0].y;
+#pragma unroll
+    for (int i = 1; i < 4; ++i)
+      if (i < groups) merge_group_step(mean, m2, stp[i], i);
+    for (int i = 4; i < groups; ++i) merge_group_step(mean, m2, a.st[(size_t)rr * groups + i], i);
+    const float sigma = sqrtf(m2 / (float)(128 * groups) + kNormEps);
+    row_mean[threadIdx.x] = mean;
+    row_scale[threadIdx.x] = make_float2(-1.4426950408889634f / sigma, sigma);
+    row_pos[threadIdx.x] = posp;
   }
   // Column sums of W1 for this lane's columns: the normalisation is applied to the
   // product, Xn W1 = (X W1 - mean * colsum(W1)) / sigma row by row, exactly; the mean
@@ -319,7 +352,7 @@ void uvqk_kernel(UvqkArgs a) {
   for (int j = 0; j < C::NI; ++j)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const float4 c4 = *reinterpret_cast<const float4*>(a.cs + col0 + wn * C::TN + j * 32 + g * 8 + hi * 4);
+      const float4 c4 = *reinterpret_cast<const float4*>(col_sum + wn * C::TN + j * 32 + g * 8 + hi * 4);
       csum[j][g][0] = c4.x;
       csum[j][g][1] = c4.y;
       csum[j][g][2] = c4.z;
@@ -359,9 +392,8 @@ void uvqk_kernel(UvqkArgs a) {
 #pragma unroll
     for (int i = 0; i < C::BM * CPR / C::NT; ++i) {
       const int r = r_first + RSTEP_O * i;
-      const int2 q = a.row_info[min(row0 + r, a.T - 1)];
       *reinterpret_cast<uint4*>(smem + r * OLD + cc) =
-          *reinterpret_cast<const uint4*>(pos + __umul24((unsigned)q.y, 3u * (unsigned)D));
+          *reinterpret_cast<const uint4*>(pos + __umul24((unsigned)row_pos[r], 3u * (unsigned)D));
     }
     __syncthreads();
   }
@@ -370,6 +402,8 @@ void uvqk_kernel(UvqkArgs a) {
   // the global writes are whole cache lines.
   // With a = X W1 - mean * colsum(W1) and y = a / sigma: SiLU(y) = y / (1 + 2^(-y log2 e))
   // = a / (sigma + sigma * 2^(a * (-log2(e) / sigma))).
+  // without a bias the staged area holds stale bits: masked to +0 (integer, so NaN-safe)
+  const uint32_t bias_mask = has_bias ? ~0u : 0u;
   auto silu_n = [](float a, float2 sc) {
     return a * __builtin_amdgcn_rcpf(__builtin_fmaf(__builtin_amdgcn_exp2f(a * sc.x), sc.y, sc.y));
   };
@@ -382,7 +416,9 @@ void uvqk_kernel(UvqkArgs a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         uint2* at = reinterpret_cast<uint2*>(smem + r * OLD + wn * C::TN + j * 32 + g * 8 + hi * 4);
-        const uint2 bias = has_bias ? *at : make_uint2(0, 0);
+        uint2 bias = *at;          // read unconditionally (a select here became a branch per read)
+        bias.x &= bias_mask;
+        bias.y &= bias_mask;
         const float v0 = silu_n(acc[i][j][4 * g + 0], sc) + bf2f_lo(bias.x);
         const float v1 = silu_n(acc[i][j][4 * g + 1], sc) + bf2f_hi(bias.x);
         const float v2 = silu_n(acc[i][j][4 * g + 2], sc) + bf2f_lo(bias.y);
@@ -508,6 +544,10 @@ void out_kernel(OutArgs a) {
 // would not give every CU at least one workgroup (small batches, D = 128 outputs).
 using BigTile = Tile<256, 256, 2, 4>;
 using SmallTile = Tile<128, 128, 2, 2>;
+// The projection's 256 x 128 tile on 4 waves with a 3-stage ring of 32-wide K steps:
+// 74 KB of LDS, so two workgroups share a CU and one's epilogue runs beside the
+// other's main loop.
+using HalfTile = Tile<256, 128, 2, 2, 32, 3>;
 
 template <typename C>
 long tiles_of(int T, int N) {
@@ -519,11 +559,15 @@ long tiles_of(int T, int N) {
 hipError_t launch_uvqk_bf16(const UvqkArgs& a, hipStream_t s) {
   // A tile must lie inside one of the U, V, Q, K column blocks: D % BN == 0.
   const int N = 4 * a.D;
-  // Big tiles need whole D-wide column blocks and enough tiles that the last of the
-  // rounds of 256 (one per CU) is mostly full: 352 big tiles would run as a full round
-  // and a 38% one, where the same work in small tiles fills its rounds evenly.
+  // Half tiles (two workgroups per CU) when they fill at least two rounds of 512. Big
+  // tiles need whole D-wide column blocks and enough tiles that the last of the rounds
+  // of 256 (one per CU) is mostly full: 352 big tiles would run as a full round and a
+  // 38% one, where the same work in small tiles fills its rounds evenly.
+  const int th = tiles_of<HalfTile>(a.T, N);
   const int tb = tiles_of<BigTile>(a.T, N), rounds = (tb + 255) / 256;
-  if (a.D % BigTile::BN == 0 && tb >= 256 && (rounds >= 4 || 4 * tb >= 3 * 256 * rounds))
+  if (a.D % HalfTile::BN == 0 && th >= 1024)
+    uvqk_kernel<HalfTile><<<th, HalfTile::NT, 0, s>>>(a);
+  else if (a.D % BigTile::BN == 0 && tb >= 256 && (rounds >= 4 || 4 * tb >= 3 * 256 * rounds))
     uvqk_kernel<BigTile><<<tiles_of<BigTile>(a.T, N), BigTile::NT, 0, s>>>(a);
   else
     uvqk_kernel<SmallTile><<<tiles_of<SmallTile>(a.T, N), SmallTile::NT, 0, s>>>(a);
