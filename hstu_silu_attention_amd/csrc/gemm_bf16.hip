@@ -22,7 +22,7 @@ namespace {
 // needs one barrier; staging through registers lets it form the gate columns of
 // [U | O | U*O] from U and O on the way. The projection (gemm_tile_dma) loads its
 // operands, the layer input rows as stored and W1, straight into LDS.
-template <int BM_, int BN_, int WM_, int WN_, int BK_ = 64, int STAGES_ = 2>
+template <int BM_, int BN_, int WM_, int WN_, int BK_ = 64, int STAGES_ = 2, int WPE_ = 0>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
   static constexpr int NT = 64 * WM * WN;          // threads
@@ -33,8 +33,9 @@ struct Tile {
   static constexpr int AC = BM * BK / 8 / NT;      // 16-byte A chunks per thread per step
   static constexpr int BC = BN * BK / 8 / NT;      // 16-byte W chunks per thread per step
   static constexpr int STAGE = (BM + BN) * LDK;    // elements per LDS stage
-  // 256 accumulators per lane leave room for one wave per SIMD only.
-  static constexpr int WAVES_PER_EU = MI * NI * 16 >= 256 ? 1 : 2;
+  // 256 accumulators per lane leave room for one wave per SIMD only; WPE_ asks for more
+  // waves per SIMD where the registers allow.
+  static constexpr int WAVES_PER_EU = WPE_ ? WPE_ : MI * NI * 16 >= 256 ? 1 : 2;
 };
 
 // Thread t moves the chunks of rows t/8 + RSTEP*i (i < AC or BC), k offset (t%8)*8.
@@ -545,9 +546,11 @@ void out_kernel(OutArgs a) {
 using BigTile = Tile<256, 256, 2, 4>;
 using SmallTile = Tile<128, 128, 2, 2>;
 // The projection's 256 x 128 tile on 4 waves with a 3-stage ring of 32-wide K steps:
-// 74 KB of LDS, so two workgroups share a CU and one's epilogue runs beside the
-// other's main loop.
+// 77 KB of LDS, so two workgroups share a CU and one's epilogue runs beside the
+// other's main loop. Its 128 x 128 tile with the same ring takes 51 KB and under 170
+// registers a lane, so three workgroups share a CU.
 using HalfTile = Tile<256, 128, 2, 2, 32, 3>;
+using QuarterTile = Tile<128, 128, 2, 2, 32, 3, 3>;
 
 template <typename C>
 long tiles_of(int T, int N) {
@@ -559,14 +562,17 @@ long tiles_of(int T, int N) {
 hipError_t launch_uvqk_bf16(const UvqkArgs& a, hipStream_t s) {
   // A tile must lie inside one of the U, V, Q, K column blocks: D % BN == 0.
   const int N = 4 * a.D;
-  // Half tiles (two workgroups per CU) when they fill at least two rounds of 512. Big
-  // tiles need whole D-wide column blocks and enough tiles that the last of the rounds
-  // of 256 (one per CU) is mostly full: 352 big tiles would run as a full round and a
-  // 38% one, where the same work in small tiles fills its rounds evenly.
-  const int th = tiles_of<HalfTile>(a.T, N);
+  // Half tiles (two workgroups per CU) when they fill at least two rounds of 512;
+  // quarter tiles (three per CU) when they fill a round of 768. Otherwise big tiles
+  // need whole D-wide column blocks and enough tiles that the last of the rounds of 256
+  // (one per CU) is mostly full: 352 big tiles would run as a full round and a 38% one,
+  // where the same work in small tiles fills its rounds evenly.
+  const int th = tiles_of<HalfTile>(a.T, N), tq = tiles_of<QuarterTile>(a.T, N);
   const int tb = tiles_of<BigTile>(a.T, N), rounds = (tb + 255) / 256;
   if (a.D % HalfTile::BN == 0 && th >= 1024)
     uvqk_kernel<HalfTile><<<th, HalfTile::NT, 0, s>>>(a);
+  else if (a.D % QuarterTile::BN == 0 && tq >= 768)
+    uvqk_kernel<QuarterTile><<<tq, QuarterTile::NT, 0, s>>>(a);
   else if (a.D % BigTile::BN == 0 && tb >= 256 && (rounds >= 4 || 4 * tb >= 3 * 256 * rounds))
     uvqk_kernel<BigTile><<<tiles_of<BigTile>(a.T, N), BigTile::NT, 0, s>>>(a);
   else

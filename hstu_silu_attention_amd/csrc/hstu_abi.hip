@@ -117,7 +117,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 // sort key is a total order (ties broken by a sequence number), so std::sort gives the
 // same order on every call.
 struct PlanItem {
-  int64_t cost;           // key blocks swept, plus a fixed per-item overhead
+  int64_t cost;           // key blocks swept, plus a fixed per-item overhead (below)
   int32_t user, code;     // code as in hstu::ItemCode
   int32_t seq, bin;       // push order inside the group, then append order inside the bin
 };
@@ -130,6 +130,12 @@ struct PlanGroup {
 // Fills codes[0, grid) and returns grid, the attention's workgroup count: workgroup w
 // runs on XCD w % kXcds and takes position w / kXcds of that XCD's bin (user -1 past
 // the bin's end).
+// An item's cost is in key blocks: the blocks it sweeps, plus its fixed work (Q and first
+// K/V loads, the diagonal pass of a history item, a candidate's own key, the stores)
+// as measured on MI355X at dh = 128: about 13 blocks' time for a history item and 22
+// for a candidate item.
+constexpr int64_t kHistoryItemFixed = 13, kCandidateItemFixed = 22;
+
 int plan_attention(const UserRec* users, int32_t B, int32_t heads, int bm, PlanGroup* groups, PlanItem* items,
                    hstu::ItemCode* codes) {
   int32_t G = 0, N = 0;
@@ -139,11 +145,11 @@ int plan_attention(const UserRec* users, int32_t B, int32_t heads, int bm, PlanG
       const int32_t first = N;
       for (int32_t q0 = 0; q0 < u.n; q0 += bm) {
         const int32_t nq = std::min(bm, u.n - q0);
-        items[N] = {cdiv((int64_t)u.m + q0 + nq, 64) + 2, b, ((q0 / bm) << 8) | (h << 1), N - first, -1};
+        items[N] = {cdiv((int64_t)u.m + q0 + nq, 64) + kHistoryItemFixed, b, ((q0 / bm) << 8) | (h << 1), N - first, -1};
         ++N;
       }
       for (int32_t q0 = 0; q0 < u.c; q0 += bm) {
-        items[N] = {cdiv((int64_t)u.m + u.n, 64) + 2, b, ((q0 / bm) << 8) | (h << 1) | 1, N - first, -1};
+        items[N] = {cdiv((int64_t)u.m + u.n, 64) + kCandidateItemFixed, b, ((q0 / bm) << 8) | (h << 1) | 1, N - first, -1};
         ++N;
       }
       if (N == first) continue;

@@ -25,18 +25,18 @@ def decode(codes):
 
 def expected_bins(ul, cl, ml, heads, q):
     """The documented rule, written independently: per (user, head) its items with their
-    costs (key blocks swept + 2), groups largest first (ties in user-then-head order) onto
-    the least loaded bin (the first such), items of a bin longest first (ties in the
-    order they were added)."""
+    costs (key blocks swept, plus a fixed 13 for a history item and 22 for a candidate
+    item), groups largest first (ties in user-then-head order) onto the least loaded bin
+    (the first such), items of a bin longest first (ties in the order they were added)."""
     groups = []
     for b in range(len(ul)):
         for h in range(heads):
             items = []
             for i, q0 in enumerate(range(0, ul[b], q)):
                 nq = min(q, ul[b] - q0)
-                items.append(((ml[b] + q0 + nq + 63) // 64 + 2, (b, h, 0, i)))
+                items.append(((ml[b] + q0 + nq + 63) // 64 + 13, (b, h, 0, i)))
             for i, q0 in enumerate(range(0, cl[b], q)):
-                items.append(((ml[b] + ul[b] + 63) // 64 + 2, (b, h, 1, i)))
+                items.append(((ml[b] + ul[b] + 63) // 64 + 22, (b, h, 1, i)))
             if items:
                 items = [it for _, it in sorted(enumerate(items), key=lambda t: (-t[1][0], t[0]))]
                 groups.append((sum(c for c, _ in items), items))
