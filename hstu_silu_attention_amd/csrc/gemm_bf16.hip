@@ -548,8 +548,9 @@ void out_kernel(OutArgs a) {
   }
 }
 
-// Tile shapes: a large one for big batches and a 128 x 128 one when the large tiles
-// would not give every CU at least one workgroup (small batches, D = 128 outputs).
+// Tile shapes: the output GEMM takes the large one for big batches and the 128 x 128 one
+// when the large tiles would not give every CU at least one workgroup; the projection
+// takes the ring tiles below, or the 128 x 128 one for small batches.
 using BigTile = Tile<256, 256, 2, 4>;
 using SmallTile = Tile<128, 128, 2, 2>;
 // The projection's 256 x 128 tile on 4 waves with a 3-stage ring of 32-wide K steps:
@@ -567,21 +568,16 @@ long tiles_of(int T, int N) {
 }  // namespace
 
 hipError_t launch_uvqk_bf16(const UvqkArgs& a, hipStream_t s) {
-  // A tile must lie inside one of the U, V, Q, K column blocks: D % BN == 0.
+  // A tile must lie inside one of the U, V, Q, K column blocks: D % BN == 0 (D is a
+  // multiple of 128 for bfloat16 models). Half tiles (two workgroups per CU) when they
+  // fill at least two rounds of 512; quarter tiles (three per CU) when they fill a round
+  // of 768; otherwise 128 x 128 tiles one per CU (small batches).
   const int N = 4 * a.D;
-  // Half tiles (two workgroups per CU) when they fill at least two rounds of 512;
-  // quarter tiles (three per CU) when they fill a round of 768. Otherwise big tiles
-  // need whole D-wide column blocks and enough tiles that the last of the rounds of 256
-  // (one per CU) is mostly full: 352 big tiles would run as a full round and a 38% one,
-  // where the same work in small tiles fills its rounds evenly.
   const int th = tiles_of<HalfTile>(a.T, N), tq = tiles_of<QuarterTile>(a.T, N);
-  const int tb = tiles_of<BigTile>(a.T, N), rounds = (tb + 255) / 256;
   if (a.D % HalfTile::BN == 0 && th >= 1024)
     uvqk_kernel<HalfTile><<<th, HalfTile::NT, 0, s>>>(a);
   else if (a.D % QuarterTile::BN == 0 && tq >= 768)
     uvqk_kernel<QuarterTile><<<tq, QuarterTile::NT, 0, s>>>(a);
-  else if (a.D % BigTile::BN == 0 && tb >= 256 && (rounds >= 4 || 4 * tb >= 3 * 256 * rounds))
-    uvqk_kernel<BigTile><<<tiles_of<BigTile>(a.T, N), BigTile::NT, 0, s>>>(a);
   else
     uvqk_kernel<SmallTile><<<tiles_of<SmallTile>(a.T, N), SmallTile::NT, 0, s>>>(a);
   return hipGetLastError();

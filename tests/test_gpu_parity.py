@@ -113,6 +113,21 @@ def test_bf16_relative_bias_long_table(D, H, max_len, n, m):
     assert eu <= BF16_TOL and ec <= BF16_TOL
 
 
+@pytest.mark.parametrize("uih,cand", [
+    ([1200, 900, 0], [301, 500, 99]),                         # 3000 rows: 128 x 128 tiles, one per CU
+    ([3001, 2500, 1700, 0], [1024, 1499, 300, 1]),            # 10025 rows: 128 x 128 ring tiles, three per CU
+    ([4000, 3901, 3000, 1999], [2048, 1100, 700, 301]),       # 17049 rows: 256 x 128 ring tiles, two per CU
+])
+def test_bf16_projection_tiles(uih, cand):
+    """D = 512, one layer: batch sizes that select each of the projection's tile shapes (the
+    launcher picks by the tile counts), ragged tails and an empty user; every user against
+    the oracle."""
+    wl = workloads.make_custom(seed=1200 + sum(uih), dtype="bf16", layers=1, d_model=512, heads=4, max_len=4200,
+                               uih_lengths=uih, cand_lengths=cand)
+    gu, gc = gpu_encode(wl)
+    check(wl, gu, gc, "bf16", BF16_TOL, label=f"bf16 projection tiles, {sum(uih) + sum(cand)} rows")
+
+
 def test_bf16_single_layer_many_tiles():
     """One layer, long rows: attention work items of up to 16 key blocks per query tile."""
     wl = workloads.make_custom(seed=301, dtype="bf16", layers=1, d_model=256, heads=2, max_len=1100,
