@@ -93,11 +93,13 @@ __device__ __forceinline__ void lds_load16(const i32x4& desc, uint32_t lds_addr,
 // Chunk permutations of the slots. gfx950's LDS has 64 four-byte banks; a 16-byte read
 // is served 16 lanes at a time (16 consecutive K rows of one fragment) and a transpose
 // read 32 lanes at a time (4 V rows x 4 chunks), so each group must cover distinct
-// 16-byte bank groups.
+// 16-byte bank groups. At dh = 32 a row is 64 bytes: K rows 4 apart start on the same
+// bank and get distinct slots from bits 2-3 of the row; the 4 V rows of a transpose
+// read are 256 consecutive bytes, all 64 banks once, so V needs no permutation.
 template <int DH>
-__device__ __forceinline__ int k_swz(int r) { return DH == 128 ? (r & 15) : ((r >> 1) & 7); }
+__device__ __forceinline__ int k_swz(int r) { return DH == 128 ? (r & 15) : DH == 64 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
 template <int DH>
-__device__ __forceinline__ int v_swz(int r) { return DH == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+__device__ __forceinline__ int v_swz(int r) { return DH == 128 ? 4 * (r & 3) : DH == 64 ? 4 * ((r >> 1) & 1) : 0; }
 
 __device__ __forceinline__ float silu_bias(float x, float nlog2e, float bias) {
   return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(__builtin_fmaf(x, nlog2e, bias)));
@@ -116,15 +118,18 @@ constexpr int kTabPad = 64, kSlice = 512, kRing = 3, kTabStatic = kTabPad + kSli
 
 // dh = 64 fits three waves per SIMD (under 168 registers; 32 KB of K/V slots, 48 KB with
 // a relative table, per workgroup), which hides more of each wave's latency; dh = 128
-// needs two (233 registers, 64 KB).
+// needs two (233 registers, 64 KB); dh = 32 fits four (under 128 registers, 16 KB).
 //
 // Paged cache (PAGED): key r of the user lives in row r % 64 of page pages[key_row + r / 64]
 // of the layer's pool. The buffer range is then the whole pool, and each DMA lane takes its
 // row's page from the pair of page ids that a block of 64 consecutive keys can touch; the
 // pair is read (wave-uniform) one block ahead. A key outside [0, key_end), or an id
 // outside the pool, gets an offset past the range and reads as zero.
+template <int DH>
+constexpr int attn_waves_per_eu() { return DH == 32 ? 4 : DH == 64 ? 3 : 2; }
+
 template <int DH, bool REL, bool PAGED>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DH == 64 ? 3 : 2, DH == 64 ? 3 : 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<DH>(), attn_waves_per_eu<DH>())))
 void attn_kernel(AttnArgs a) {
   using C = AttnTile<DH>;
   __shared__ __attribute__((aligned(16))) u16 ks0[C::SLOT], ks1[C::SLOT], vs0[C::SLOT], vs1[C::SLOT];
@@ -499,6 +504,10 @@ hipError_t launch_attn_bf16(int dh, const AttnArgs& a, int grid, hipStream_t s) 
   static_assert(AttnTile<128>::NT == NT, "one block size");
 #define HSTU_ATTN_CASE(DH, REL, PAGED) \
   if (dh == DH && rel == REL && paged == PAGED) { attn_kernel<DH, REL, PAGED><<<grid, NT, 0, s>>>(a); return hipGetLastError(); }
+  HSTU_ATTN_CASE(32, false, false)
+  HSTU_ATTN_CASE(32, true, false)
+  HSTU_ATTN_CASE(32, false, true)
+  HSTU_ATTN_CASE(32, true, true)
   HSTU_ATTN_CASE(64, false, false)
   HSTU_ATTN_CASE(64, true, false)
   HSTU_ATTN_CASE(128, false, false)

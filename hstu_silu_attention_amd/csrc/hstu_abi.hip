@@ -36,7 +36,7 @@ hstu_status check_dims(const hstu_dims* d) {
   if (d->dtype == HSTU_F32) {
     if (d->d_model % 64 || (dh != 32 && dh != 64 && dh != 128)) return HSTU_ERR_SHAPE;
   } else if (d->dtype == HSTU_BF16) {
-    if (d->d_model % 128 || (dh != 64 && dh != 128)) return HSTU_ERR_SHAPE;
+    if (d->d_model % 128 || (dh != 32 && dh != 64 && dh != 128)) return HSTU_ERR_SHAPE;
   } else {
     return HSTU_ERR_SHAPE;
   }

@@ -95,7 +95,7 @@ typedef int32_t hstu_status;
  *  layers  >= 1
  *  d_model  D; heads H (at most 127) with dh = D / H.
  *           float32:  D % 64 == 0 and dh in {32, 64, 128}
- *           bfloat16: D % 128 == 0 and dh in {64, 128}
+ *           bfloat16: D % 128 == 0 and dh in {32, 64, 128}
  *  max_len  rows of each position-bias table; every user needs m + n + 1 <= max_len
  *           (history positions 0..m+n-1 plus the candidate slot m+n). The attention
  *           scale is 1/max_len. A table has fewer than 2^31 elements:

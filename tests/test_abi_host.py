@@ -52,7 +52,8 @@ def dims(L=2, D=256, H=4, max_len=64, dtype=hsa.HSTU_BF16):
 
 @pytest.mark.parametrize("d,want", [
     (dims(), OK),
-    (dims(D=256, H=8), ERR_SHAPE),               # dh = 32 not supported in bf16
+    (dims(D=256, H=8), OK),                      # bf16, dh = 32
+    (dims(D=256, H=16), ERR_SHAPE),              # dh = 16
     (dims(D=192, H=3), ERR_SHAPE),               # D % 128
     (dims(D=256, H=3), ERR_SHAPE),               # D % H
     (dims(dtype=2), ERR_SHAPE),

@@ -37,9 +37,10 @@ def test_f32_ragged(D, H):
     check(wl, gu, gc, "f64", F32_TOL, label=f"f32 D={D} H={H}")
 
 
-@pytest.mark.parametrize("D,H", [(256, 4), (256, 2), (512, 8), (512, 4), (640, 10), (768, 6), (1024, 8)])
+@pytest.mark.parametrize("D,H", [(256, 4), (256, 2), (512, 8), (512, 4), (640, 10), (768, 6), (1024, 8),
+                                 (256, 8), (512, 16)])
 def test_bf16_ragged(D, H):
-    """dh = 64 and 128; histories of 0, 1, 127, 129, 300 rows and candidate sets of 1, 0, 130,
+    """dh = 32, 64 and 128; histories of 0, 1, 127, 129, 300 rows and candidate sets of 1, 0, 130,
     5, 64 rows cover empty users, single rows and ragged tails of 128-row query tiles and
     64-key blocks. Widths up to D = 1024, including ones whose projection column blocks are
     not whole 256-wide tiles (640, 768)."""
@@ -63,7 +64,7 @@ def test_history_fills_the_position_table(dtype, tol):
 
 
 @pytest.mark.parametrize("position", ["relative", "both"])
-@pytest.mark.parametrize("D,H", [(256, 4), (512, 4)])
+@pytest.mark.parametrize("D,H", [(256, 4), (512, 4), (256, 8)])
 def test_bf16_relative_bias(D, H, position):
     """The original HSTU form: a relative position bias on every attention weight (alone,
     and with the absolute table), dh = 64 and 128, the ragged lengths of the other tests."""
@@ -212,7 +213,8 @@ def _fill_and_encode(wl, model, cache):
 
 
 @pytest.mark.parametrize("dtype,D,H,position", [("bf16", 512, 4, "absolute"), ("bf16", 256, 4, "both"),
-                                                ("bf16", 512, 4, "relative"), ("f32", 128, 2, "both")])
+                                                ("bf16", 512, 4, "relative"), ("bf16", 256, 8, "both"),
+                                                ("f32", 128, 2, "both")])
 def test_paged_cache_matches_slot_cache(dtype, D, H, position):
     """The paged layout (64-row pages, shuffled page ids, a device page table) against the
     slot layout on the same calls: the kernels add in the same order, so outputs and
