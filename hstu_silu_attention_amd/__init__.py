@@ -20,10 +20,11 @@ import numpy as np
 
 __all__ = ["HSTU_F32", "HSTU_BF16", "HstuError", "load_library", "library_path",
            "hstu_abi_version", "hstu_status_string", "hstu_workspace_size", "hstu_flops", "hstu_attention_plan",
-           "hstu_encode", "hstu_encode_static", "encode_static", "HSTU_ERR_TOO_LARGE", "hstu_pack_uih", "hstu_timing_enable", "hstu_timing_select", "hstu_timing_read", "KERNEL_KINDS",
-           "PACK_MODES", "Model", "KVCache", "ScoringHead", "encode", "pack_uih", "score", "hstu_score",
-           "HstuDims", "HstuLayerWeights", "HstuKvCache", "HstuHeadLayer", "KvPool", "PagedKVCache", "POOL_STATS",
-           "PAGE_ROWS"]
+           "hstu_encode", "hstu_encode_static", "encode_static", "HSTU_ERR_TOO_LARGE", "hstu_pack_uih",
+           "hstu_transpose_weights", "transpose_weights", "hstu_timing_enable", "hstu_timing_select",
+           "hstu_timing_read", "KERNEL_KINDS", "PACK_MODES", "Model", "KVCache", "ScoringHead", "encode", "pack_uih",
+           "score", "hstu_score", "HstuDims", "HstuLayerWeights", "HstuKvCache", "HstuHeadLayer", "KvPool",
+           "PagedKVCache", "POOL_STATS", "PAGE_ROWS"]
 
 HSTU_F32, HSTU_BF16 = 0, 1
 HSTU_OK = 0
@@ -129,6 +130,9 @@ def load_library() -> ctypes.CDLL:
     lib.hstu_pack_uih.restype = ctypes.c_int32
     lib.hstu_pack_uih.argtypes = [P(HstuDims), ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.hstu_transpose_weights.restype = ctypes.c_int32
+    lib.hstu_transpose_weights.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_void_p]
     _lib = lib
     return lib
 
@@ -218,6 +222,11 @@ def hstu_pack_uih(dims: HstuDims, events: int, mode: int, context_ptr: int, acti
     """Raw call with integer device pointers. Returns the status."""
     return int(load_library().hstu_pack_uih(ctypes.byref(dims), events, mode, context_ptr, action_ptr,
                                             uih_ptr, stream))
+
+
+def hstu_transpose_weights(dtype: int, rows: int, cols: int, src_ptr: int, dst_ptr: int, stream: int) -> int:
+    """Raw call with integer device pointers. Returns the status."""
+    return int(load_library().hstu_transpose_weights(dtype, rows, cols, src_ptr, dst_ptr, stream))
 
 
 def hstu_score(dims: HstuDims, rows: int, x_ptr: int, head: Sequence[HstuHeadLayer], prob_ptr: int,
@@ -386,6 +395,27 @@ def encode_static(model: Model, uih, uih_offsets, cand, cand_offsets, *, cache: 
                             model.weights, kv, out[0].data_ptr(), out[1].data_ptr(), stream)
     if st != HSTU_OK:
         raise HstuError(st, "hstu_encode_static")
+    return out
+
+
+def transpose_weights(w, *, out=None, stream=None):
+    """Run hstu_transpose_weights on the current (or given) stream: a device matrix [rows][cols]
+    (bfloat16 or float32) in the layout the method writes it (W1 [D][4D], W2 [3D][D]) to the
+    layout hstu_encode reads (w_uvqk [4D][D], w_out [D][3D]). Returns out [cols][rows]."""
+    torch = _torch()
+    dtypes = {torch.bfloat16: HSTU_BF16, torch.float32: HSTU_F32}
+    if w.dim() != 2 or w.dtype not in dtypes:
+        raise ValueError("a 2-D bfloat16 or float32 device matrix")
+    w = w.contiguous()
+    rows, cols = int(w.shape[0]), int(w.shape[1])
+    if out is None:
+        out = torch.empty((cols, rows), dtype=w.dtype, device=w.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(w.device).cuda_stream
+    ptr = lambda t: t.data_ptr() if t.numel() else None
+    st = hstu_transpose_weights(dtypes[w.dtype], rows, cols, ptr(w), ptr(out), stream)
+    if st != HSTU_OK:
+        raise HstuError(st, "hstu_transpose_weights")
     return out
 
 

@@ -715,6 +715,21 @@ hstu_status hstu_pack_uih(const hstu_dims* d, int32_t events, int32_t mode, cons
   return HSTU_OK;
 }
 
+hstu_status hstu_transpose_weights(int32_t dtype, int32_t rows, int32_t cols, const void* src, void* dst,
+                                   void* stream) {
+  if (dtype != HSTU_F32 && dtype != HSTU_BF16) return HSTU_ERR_SHAPE;
+  if (rows < 0 || cols < 0 || (int64_t)rows * cols >= ((int64_t)1 << 31)) return HSTU_ERR_SHAPE;
+  if ((int64_t)rows * cols == 0) return HSTU_OK;
+  if (!src || !dst) return HSTU_ERR_NULL;
+  const size_t esize = dtype == HSTU_BF16 ? 2 : 4;
+  if ((uintptr_t)src % esize || (uintptr_t)dst % esize) return HSTU_ERR_ALIGN;
+  const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst, n = (uintptr_t)rows * cols * esize;
+  if (s0 < d0 + n && d0 < s0 + n) return HSTU_ERR_SHAPE;   // the two matrices overlap
+  if (hstu::launch_transpose((int)esize, src, dst, rows, cols, (hipStream_t)stream) != hipSuccess)
+    return HSTU_ERR_HIP;
+  return HSTU_OK;
+}
+
 hstu_status hstu_score(const hstu_dims* d, int32_t rows, const void* x, const hstu_head_layer* head,
                        int32_t head_layers, float* prob, void* stream) {
   hstu_status st = check_dims(d);

@@ -184,6 +184,7 @@ hipError_t launch_rowstats(const void* x_lo, const void* x_hi, int Nu, int T, in
 hipError_t launch_uvqk(int dtype, const UvqkArgs& a, hipStream_t s);
 // grid = kXcds * (longest bin)
 hipError_t launch_attn(int dtype, int dh, const AttnArgs& a, int grid, hipStream_t s);
+hipError_t launch_transpose(int esize, const void* src, void* dst, int rows, int cols, hipStream_t s);
 hipError_t launch_out(int dtype, const OutArgs& a, hipStream_t s);
 
 }  // namespace hstu

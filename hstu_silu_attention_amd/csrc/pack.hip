@@ -56,7 +56,40 @@ __global__ __launch_bounds__(kPackThreads) void pack_sum_f32_kernel(
   out[q] = make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w);
 }
 
+// dst[c][r] = src[r][c] on 64 x 64 tiles through LDS (rows padded by one element), so
+// both the reads of src rows and the writes of dst rows are consecutive per wave.
+// Elements are moved as bits. Block (bx, by) owns source rows 64 by.. and columns 64 bx..
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ src, T* __restrict__ dst, int rows,
+                                                        int cols) {
+  __shared__ T tile[64][65];
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = r0 + ty + 4 * i, c = c0 + tx;
+    if (r < rows && c < cols) tile[ty + 4 * i][tx] = src[(size_t)r * cols + c];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int c = c0 + ty + 4 * i, r = r0 + tx;   // dst row c, column r
+    if (c < cols && r < rows) dst[(size_t)c * rows + r] = tile[tx][ty + 4 * i];
+  }
+}
+
 }  // namespace
+
+// rows * cols < 2^31 and both > 0 (checked by the caller); esize 2 or 4.
+hipError_t launch_transpose(int esize, const void* src, void* dst, int rows, int cols, hipStream_t s) {
+  const dim3 grid((cols + 63) / 64, (rows + 63) / 64);
+  if (grid.y > 65535) return hipErrorInvalidValue;
+  if (esize == 2)
+    transpose_kernel<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)src, (uint16_t*)dst, rows, cols);
+  else
+    transpose_kernel<uint32_t><<<grid, 256, 0, s>>>((const uint32_t*)src, (uint32_t*)dst, rows, cols);
+  return hipGetLastError();
+}
 
 // `chunks` counts 16-byte chunks of the output (< 2^31, checked by the caller).
 hipError_t launch_pack(const PackArgs& a, hipStream_t s) {

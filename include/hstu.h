@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 7
+#define HSTU_ABI_VERSION 8
 
 /* Element type of every device tensor of a call. */
 enum hstu_dtype { HSTU_F32 = 0, HSTU_BF16 = 1 };
@@ -113,7 +113,8 @@ typedef struct hstu_dims {
  *  w_uvqk   [4D][D]: output feature j of the projection in row j (the transpose of
  *           the math-layout W1 [D][4D]); row blocks U, V, Q, K.
  *  w_out    [D][3D]: output feature j of the output GEMM in row j (the transpose of
- *           W2 [3D][D]); column blocks U, O, U*O.
+ *           W2 [3D][D]); column blocks U, O, U*O. hstu_transpose_weights makes both
+ *           from the math layout.
  *  pos_bias [max_len][3D]: row p is the absolute bias of position p, added to V, Q, K
  *           after the SiLU (column blocks V, Q, K); NULL: no absolute bias.
  *  rel_bias [H][max_len]: rel_bias[h][d] is added to every attention weight
@@ -263,6 +264,22 @@ hstu_status hstu_encode_static(const hstu_dims* d, int32_t B, const int32_t* uih
 enum hstu_pack_mode { HSTU_PACK_SUM = 0, HSTU_PACK_INTERLEAVE = 1 };
 hstu_status hstu_pack_uih(const hstu_dims* d, int32_t events, int32_t mode, const void* context,
                           const void* action, void* uih, void* stream);
+
+/* Weights from the layout the method writes them in to the layout hstu_encode reads,
+ * once per model (e.g. at load time): dst[c][r] = src[r][c] for a device matrix src
+ * [rows][cols], row-major, in dtype (HSTU_F32 or HSTU_BF16); elements are copied bit for
+ * bit. The projection X W1 with W1 [D][4D] (column blocks U, V, Q, K) gives w_uvqk
+ * [4D][D] from rows = D, cols = 4D; the output GEMM [U | O | U*O] W2 with W2 [3D][D]
+ * (row blocks U, O, U*O) gives w_out [D][3D] from rows = 3D, cols = D. The DLRMv3 page's
+ * FLOP formula (section "Model selection") names the two GEMMs; this only changes where
+ * each weight sits.
+ *  src, dst  device, element-aligned, not overlapping
+ * Errors: HSTU_ERR_SHAPE (unknown dtype, rows or cols < 0, rows * cols >= 2^31, or the
+ * two matrices overlap), HSTU_ERR_NULL (a pointer is NULL while rows * cols > 0),
+ * HSTU_ERR_ALIGN, HSTU_ERR_HIP (the launch failed). An empty matrix launches nothing.
+ * Enqueued on `stream` like hstu_encode. */
+hstu_status hstu_transpose_weights(int32_t dtype, int32_t rows, int32_t cols, const void* src, void* dst,
+                                   void* stream);
 
 /* Candidate scoring head: the probability of each predicted outcome for every
  * candidate row. The DLRMv3 page keeps a top-layer MLP for the final prediction

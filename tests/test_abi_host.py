@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     assert {"hstu_abi_version", "hstu_status_string", "hstu_workspace_size", "hstu_flops", "hstu_encode",
             "hstu_pack_uih", "hstu_score", "hstu_pool_create", "hstu_pool_destroy", "hstu_pool_assign",
             "hstu_pool_commit", "hstu_pool_abort", "hstu_pool_stats", "hstu_pool_lookup", "hstu_timing_enable",
-            "hstu_timing_select", "hstu_timing_read", "hstu_encode_static"} <= set(names)
+            "hstu_timing_select", "hstu_timing_read", "hstu_encode_static", "hstu_transpose_weights"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
     version = int(re.search(r"#define HSTU_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
@@ -283,6 +283,29 @@ def test_pack_validation(args, want):
     lib = hsa.load_library()
     st = lib.hstu_pack_uih(ctypes.byref(d) if d is not None else None, events, mode, c, a, o, None)
     assert st == want
+
+
+# --------------------------------------------------------------------------- hstu_transpose_weights
+
+BIG = 1 << 40   # device-looking addresses far apart (never dereferenced: every case is rejected)
+
+
+@pytest.mark.parametrize("dtype,rows,cols,src,dst,want", [
+    (2, 4, 4, BIG, 2 * BIG, ERR_SHAPE),                           # unknown dtype
+    (hsa.HSTU_BF16, -1, 4, BIG, 2 * BIG, ERR_SHAPE),
+    (hsa.HSTU_BF16, 4, -1, BIG, 2 * BIG, ERR_SHAPE),
+    (hsa.HSTU_BF16, 1 << 16, 1 << 15, BIG, 2 * BIG, ERR_SHAPE),  # 2^31 elements
+    (hsa.HSTU_BF16, 4, 4, None, 2 * BIG, ERR_NULL),
+    (hsa.HSTU_F32, 4, 4, BIG, None, ERR_NULL),
+    (hsa.HSTU_BF16, 4, 4, BIG + 1, 2 * BIG, ERR_ALIGN),         # bfloat16 elements are 2-byte aligned
+    (hsa.HSTU_F32, 4, 4, BIG, 2 * BIG + 2, ERR_ALIGN),           # float32 elements 4-byte aligned
+    (hsa.HSTU_F32, 4, 4, BIG, BIG + 60, ERR_SHAPE),              # the matrices overlap (64 bytes each)
+    (hsa.HSTU_BF16, 0, 5, None, None, OK),                       # empty: nothing to do, pointers unused
+    (hsa.HSTU_F32, 7, 0, None, None, OK),
+])
+def test_transpose_weights_validation(dtype, rows, cols, src, dst, want):
+    """Every rejected case returns before anything is enqueued (no GPU here)."""
+    assert hsa.hstu_transpose_weights(dtype, rows, cols, src, dst, None) == want
 
 
 # --------------------------------------------------------------------------- hstu_score
