@@ -202,7 +202,13 @@ void attn_kernel(AttnArgs a) {
     const uintptr_t ab = hb & ~(uintptr_t)15;
     const uintptr_t end = (uintptr_t)((const u16*)a.rel + (size_t)(D / DH) * a.max_len);
     mis = (int)((hb - ab) / 2);
-    rel_src = buffer_desc((const void*)ab, (int)(end - ab));
+    // The range ends at the end of the table's last 16-byte chunk: a load returns zero for
+    // each 4-byte word that crosses the range's end, so a range ending at the table's
+    // last byte lost its last entry whenever H * max_len is odd. The chunk lies in the
+    // same page as the table's last byte (page boundaries are 16-byte aligned), and the
+    // bytes past the table in it stand for distances of max_len or more, which no key
+    // is at.
+    rel_src = buffer_desc((const void*)ab, (int)(((end + 15) & ~(uintptr_t)15) - ab));
   }
 
   // 64-lane LDS loads: load j of a region covers rows RPI*j.. of it; lane i brings the

@@ -75,6 +75,25 @@ def test_bf16_relative_bias(D, H, position):
     check(wl, gu, gc, "bf16", BF16_TOL, label=f"bf16 {position} bias D={D} H={H}")
 
 
+@pytest.mark.parametrize("D,H,max_len,uih,cand", [
+    (128, 1, 1, [0], [54]),            # a one-entry table: every candidate at position 0
+    (128, 1, 3, [2, 0], [5, 3]),       # three entries
+    (384, 3, 5, [4, 1], [3, 2]),       # 15 entries: head 2's distance 4 is the last
+    (640, 5, 7, [6], [9]),             # 35 entries: head 4's distance 6 is the last
+])
+def test_bf16_relative_table_end(D, H, max_len, uih, cand):
+    """Relative tables with an odd number of entries H * max_len: the last entry shares its
+    4-byte word with bytes past the table. The kernel reads the table in 16-byte chunks
+    through a buffer range, which returns zero for every word that crosses the range's end;
+    the range must reach past the last entry (it ended at the last byte and lost that
+    entry). Short histories, so the last distances weigh in every output."""
+    wl = workloads.make_custom(seed=61 + max_len + H, dtype="bf16", layers=2, d_model=D, heads=H,
+                               max_len=max_len, uih_lengths=uih, cand_lengths=cand, position="relative",
+                               rel_std=1.0)
+    gu, gc = gpu_encode(wl)
+    check(wl, gu, gc, "bf16", BF16_TOL, label=f"bf16 relative table of {H} x {max_len}")
+
+
 @pytest.mark.parametrize("D,H", [(64, 2), (128, 2)])
 def test_f32_relative_bias(D, H):
     wl = workloads.make_custom(seed=950 + D, dtype="f32", layers=2, d_model=D, heads=H, max_len=300,
