@@ -50,7 +50,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 // block get bias 0; the diagonal half and every later one get +inf inside the loop,
 // and a short pass after it adds the diagonal halves with a per-element mask.
 // Candidate rows take bias 0 everywhere (keys past the last history key are zero, and
-// SiLU(0) = 0) and add their own key in the epilogue.
+// SiLU(0) = 0) and add their own key in the same short pass, masked to j == i.
 template <int DH>
 struct AttnTile {
   static constexpr int WAVES = 4, NT = 64 * WAVES, QB = 1;
@@ -415,17 +415,33 @@ void attn_kernel(AttnArgs a) {
     for (int qb = 0; qb < C::QB; ++qb) pv_mfma(vf, qb, wA[qb]);
   }
 
-  if (!cand) {
-    // The diagonal half of each history block, in a private LDS area per wave (32 K
-    // rows, then 32 V rows, laid out like the slots): key offset j of the half is
-    // visible to row offset i when j <= i.
-    static_assert(C::WAVES == 4 && 64 * DH == C::SLOT, "one slot per wave for the diagonal pass");
-    u16* dk = wv == 0 ? ks0 : wv == 1 ? ks1 : wv == 2 ? vs0 : vs1;
-    u16* dv = dk + 32 * DH;
+  // The diagonal pass, in a private LDS area per wave (32 K rows, then 32 V rows, laid
+  // out like the slots). History rows: the diagonal half of each query block, key offset
+  // j visible to row offset i when j <= i. Candidates: each row's own key (j == i), whose
+  // K and V rows sit in the candidate rows of the V | Q | K buffer (rows past the item
+  // read as zero).
+  static_assert(C::WAVES == 4 && 64 * DH == C::SLOT, "one slot per wave for the diagonal pass");
+  u16* dk = wv == 0 ? ks0 : wv == 1 ? ks1 : wv == 2 ? vs0 : vs1;
+  u16* dv = dk + 32 * DH;
+  const u16* own = (const u16*)a.vqk + (size_t)it.rbase * ld3 + head * DH;   // V of the item's first row
+  const int own_bytes = ((nq - 1) * (int)ld3 + DH) * 2;
+  const i32x4 own_v = buffer_desc(own, own_bytes), own_k = buffer_desc(own + 2 * D, own_bytes);
 #pragma unroll
-    for (int qb = 0; qb < C::QB; ++qb) {
-      wait_loads();
-      __syncthreads();   // the slots (or the previous block's area) are free
+  for (int qb = 0; qb < C::QB; ++qb) {
+    wait_loads();
+    __syncthreads();   // the slots (or the previous block's area) are free
+    if (cand) {
+      const int r0 = wv * 32 * C::QB + qb * 32;   // the block's first row in the item
+#pragma unroll
+      for (int j = 0; j < 32 / C::RPI; ++j) {
+        const int r = C::RPI * j + lane / C::CPR, slot = lane % C::CPR;
+        const int roff = (r0 + r) * (int)ld3;
+        lds_load16(own_k, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)(dk + j * 512)),
+                   (roff + 8 * (slot ^ k_swz<DH>(r))) * 2);
+        lds_load16(own_v, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)(dv + j * 512)),
+                   (roff + 8 * (slot ^ v_swz<DH>(r))) * 2);
+      }
+    } else {
       const int k0 = wf + 32 * qb - shift;   // key of the half's first row
       const int2 pp = page_pair(k0);
 #pragma unroll
@@ -433,59 +449,28 @@ void attn_kernel(AttnArgs a) {
         lds_rows(rk_src, dk, k0, j, false, pp);
         lds_rows(rv_src, dv, k0, j, true, pp);
       }
-      wait_loads();
-      __syncthreads();
-      bf16x8 kf[C::KK], vf[2][C::MB], w[2];
-      f32x16 sd;
-      read_k_at(dk, kf);
-      score_mfma(kf, qb, sd);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int j = 8 * (e >> 2) + 4 * hi + (e & 3);
-        // relative position l32 - j on the diagonal
-        const float r = REL && j <= l32 ? __uint_as_float((uint32_t)tab[kTabPad + mis + l32 - j] << 16) : 0.0f;
-        const float x = silu_bias(sd[e], nlog2e, j <= l32 ? 0.0f : kInf);
-        w[e >> 3][e & 7] = (__bf16)(REL ? x + r : x);
-      }
-      read_v_at(dv, vf);
-      pv_mfma(vf, qb, w);
     }
+    wait_loads();
+    __syncthreads();
+    bf16x8 kf[C::KK], vf[2][C::MB], w[2];
+    f32x16 sd;
+    read_k_at(dk, kf);
+    score_mfma(kf, qb, sd);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int j = 8 * (e >> 2) + 4 * hi + (e & 3);
+      const bool vis = cand ? j == l32 : j <= l32;
+      // relative position l32 - j on the diagonal (0 for a candidate's own key)
+      const float r = REL && vis ? __uint_as_float((uint32_t)tab[kTabPad + mis + l32 - j] << 16) : 0.0f;
+      const float x = silu_bias(sd[e], nlog2e, vis ? 0.0f : kInf);
+      w[e >> 3][e & 7] = (__bf16)(REL ? x + r : x);
+    }
+    read_v_at(dv, vf);
+    pv_mfma(vf, qb, w);
   }
 
 #pragma unroll
   for (int qb = 0; qb < C::QB; ++qb) {
-    const u16* vqk = (const u16*)a.vqk + row[qb] * ld3 + head * DH;   // V | Q | K of this row
-    if (cand) {
-      // the candidate's own key and value: a_self = bf16(SiLU(q . k_self))
-      float part = 0.0f;
-      if (qok[qb]) {
-#pragma unroll
-        for (int kk = 0; kk < C::KK; ++kk) {
-          const uint4 kv = *reinterpret_cast<const uint4*>(vqk + 2 * D + kk * 16 + hi * 8);
-          const uint32_t wds[4] = {kv.x, kv.y, kv.z, kv.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            part += (float)qf[qb][kk][2 * e] * bf2f_lo(wds[e]);
-            part += (float)qf[qb][kk][2 * e + 1] * bf2f_hi(wds[e]);
-          }
-        }
-      }
-      const float dot = part + __shfl_xor(part, 32);
-      const float r0 = REL ? __uint_as_float((uint32_t)tab[kTabPad + mis] << 16) : 0.0f;   // position 0
-      const float as = qok[qb] ? round_bf(REL ? silu(dot) + r0 : silu(dot)) : 0.0f;
-      if (qok[qb]) {
-#pragma unroll
-        for (int mb = 0; mb < C::MB; ++mb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint2 vv = *reinterpret_cast<const uint2*>(vqk + mb * 32 + i * 8 + hi * 4);
-            oacc[qb][mb][4 * i + 0] += as * bf2f_lo(vv.x);
-            oacc[qb][mb][4 * i + 1] += as * bf2f_hi(vv.x);
-            oacc[qb][mb][4 * i + 2] += as * bf2f_lo(vv.y);
-            oacc[qb][mb][4 * i + 3] += as * bf2f_hi(vv.y);
-          }
-      }
-    }
     if (qok[qb]) {
       // O = bf16(inv * acc) into columns [D, 2D) of the output GEMM's operand row
       u16* orow = (u16*)a.aout + row[qb] * ld3 + D + head * DH;
