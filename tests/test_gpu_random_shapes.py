@@ -1,9 +1,11 @@
 """GPU parity over seeded random configurations, beside the hand-picked cases: dtype, head
 width (32, 64, 128) and count, 1-6 users with ragged lengths and empty users, no cache, a
 slot cache or a paged cache (shuffled page ids) with cached prefixes, absolute, relative
-or both position biases, one or two layers. Each case fills the cache with the prefixes
-(no candidates), then encodes the new events and candidates; every user's outputs are
-held to the oracle's bar (bf16 mirror or float64), the oracle doing the same two calls."""
+or both position biases, one or two layers; the wide draw goes to 8 users, histories of
+up to 900 new and 600 cached rows, 400 candidates, 3 or 6 heads and D up to 768. Each
+case fills the cache with the prefixes (no candidates), then encodes the new events and
+candidates; every user's outputs are held to the oracle's bar (bf16 mirror or float64),
+the oracle doing the same two calls."""
 import numpy as np
 import pytest
 
@@ -14,6 +16,7 @@ from gpu_util import BF16_TOL, F32_TOL, gpu_encode, make_model, normwise_per_use
 pytestmark = pytest.mark.gpu
 
 SEEDS = list(range(9100, 9116))
+WIDE_SEEDS = list(range(9200, 9216))
 
 
 def draw(seed):
@@ -35,10 +38,37 @@ def draw(seed):
                 position=position, layers=layers, max_len=max_len)
 
 
+def draw_wide(seed):
+    rng = np.random.default_rng(seed)
+    dtype = "bf16" if rng.random() < 0.8 else "f32"
+    dh = int(rng.choice([32, 64, 128]))
+    unit = 128 if dtype == "bf16" else 64
+    heads = [h for h in (1, 2, 3, 4, 6, 8) if (dh * h) % unit == 0 and dh * h <= 768]
+    H = int(rng.choice(heads))
+    B = int(rng.integers(1, 9))
+    uih = np.where(rng.random(B) < 0.15, 0, rng.integers(1, 900, B))
+    cand = np.where(rng.random(B) < 0.2, 0, rng.integers(1, 400, B))
+    cache = str(rng.choice(["none", "slot", "paged"]))
+    cached = np.zeros(B, np.int64) if cache == "none" else np.where(rng.random(B) < 0.3, 0, rng.integers(1, 600, B))
+    position = str(rng.choice(["absolute", "relative", "both"]))
+    layers = int(rng.integers(1, 3))
+    max_len = int((cached + uih).max()) + 1 + int(rng.integers(0, 300))
+    return dict(dtype=dtype, D=dh * H, H=H, B=B, uih=uih, cand=cand, cache=cache, cached=cached,
+                position=position, layers=layers, max_len=max_len)
+
+
 @pytest.mark.parametrize("seed", SEEDS)
 def test_random_configuration(seed):
+    run_configuration(seed, draw(seed))
+
+
+@pytest.mark.parametrize("seed", WIDE_SEEDS)
+def test_random_wide_configuration(seed):
+    run_configuration(seed, draw_wide(seed))
+
+
+def run_configuration(seed, c):
     torch = torch_cuda()
-    c = draw(seed)
     say(f"  seed {seed}: {c['dtype']} D={c['D']} H={c['H']} B={c['B']} layers={c['layers']} cache={c['cache']} "
         f"{c['position']} uih={c['uih'].tolist()} cand={c['cand'].tolist()} cached={c['cached'].tolist()}")
     wl = workloads.make_custom(seed=seed, dtype=c["dtype"], layers=c["layers"], d_model=c["D"], heads=c["H"],
