@@ -5,7 +5,10 @@ or both position biases, one or two layers; the wide draw goes to 8 users, histo
 up to 900 new and 600 cached rows, 400 candidates, 3 or 6 heads and D up to 768. Each
 case fills the cache with the prefixes (no candidates), then encodes the new events and
 candidates; every user's outputs are held to the oracle's bar (bf16 mirror or float64),
-the oracle doing the same two calls."""
+the oracle doing the same two calls. The large draw (one layer, 4-16 users, up to 2500
+new and 1500 cached rows, 1200 candidates, D 256-1024) reaches the batch sizes at which
+the projection takes its 256 x 128 and 128 x 128 ring tiles and the output GEMM its
+256 x 256 tile."""
 import numpy as np
 import pytest
 
@@ -17,6 +20,10 @@ pytestmark = pytest.mark.gpu
 
 SEEDS = list(range(9100, 9116))
 WIDE_SEEDS = list(range(9200, 9216))
+# large draws covering each projection tile and the output GEMM's large tile, with every
+# cache layout: 40000 (128 x 128 ring, paged), 40003 and 40007 (256 x 128, 256 x 256, paged),
+# 40008 and 40011 (slot cache; the latter 16 heads of 64), 40014 (no cache)
+LARGE_SEEDS = [40000, 40003, 40007, 40008, 40011, 40014]
 
 
 def draw(seed):
@@ -57,6 +64,21 @@ def draw_wide(seed):
                 position=position, layers=layers, max_len=max_len)
 
 
+def draw_large(seed):
+    rng = np.random.default_rng(seed)
+    D = int(rng.choice([256, 512, 768, 1024]))
+    dh = int(rng.choice([64, 128])) if D != 768 else 128
+    B = int(rng.integers(4, 17))
+    uih = np.where(rng.random(B) < 0.1, 0, rng.integers(1, 2500, B))
+    cand = np.where(rng.random(B) < 0.1, 0, rng.integers(1, 1200, B))
+    cache = str(rng.choice(["none", "slot", "paged"]))
+    cached = np.zeros(B, np.int64) if cache == "none" else np.where(rng.random(B) < 0.3, 0, rng.integers(1, 1500, B))
+    position = str(rng.choice(["absolute", "relative", "both"]))
+    max_len = int((cached + uih).max()) + 1 + int(rng.integers(0, 300))
+    return dict(dtype="bf16", D=D, H=D // dh, B=B, uih=uih, cand=cand, cache=cache, cached=cached,
+                position=position, layers=1, max_len=max_len)
+
+
 @pytest.mark.parametrize("seed", SEEDS)
 def test_random_configuration(seed):
     run_configuration(seed, draw(seed))
@@ -65,6 +87,11 @@ def test_random_configuration(seed):
 @pytest.mark.parametrize("seed", WIDE_SEEDS)
 def test_random_wide_configuration(seed):
     run_configuration(seed, draw_wide(seed))
+
+
+@pytest.mark.parametrize("seed", LARGE_SEEDS)
+def test_random_large_configuration(seed):
+    run_configuration(seed, draw_large(seed))
 
 
 def run_configuration(seed, c):
