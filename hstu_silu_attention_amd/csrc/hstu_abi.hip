@@ -635,22 +635,27 @@ hstu_status hstu_flops(const hstu_dims* d, int32_t B, const int32_t* uih_offsets
   if (st != HSTU_OK) return st;
   st = check_offsets(B, uih_offsets, cand_offsets);
   if (st != HSTU_OK) return st;
-  const uint64_t D = (uint64_t)d->d_model, L = (uint64_t)d->layers;
-  uint64_t alg = 0, form = 0;
+  // 128-bit sums: with n, c, m < 2^31, D < 2^14 (at most 127 heads of 128) and layers
+  // < 2^31, each user adds under 2^112, so a running total checked after every user
+  // cannot wrap
+  typedef unsigned __int128 u128;
+  const u128 D = (u128)d->d_model, L = (u128)d->layers, lim = (u128)UINT64_MAX;
+  u128 alg = 0, form = 0;
   for (int32_t b = 0; b < B; ++b) {
-    const uint64_t n = (uint64_t)(uih_offsets[b + 1] - uih_offsets[b]);
-    const uint64_t c = (uint64_t)(cand_offsets[b + 1] - cand_offsets[b]);
-    int32_t mm = cached_len ? cached_len[b] : 0;
+    const u128 n = (u128)(uih_offsets[b + 1] - uih_offsets[b]);
+    const u128 c = (u128)(cand_offsets[b + 1] - cand_offsets[b]);
+    const int32_t mm = cached_len ? cached_len[b] : 0;
     if (mm < 0) return HSTU_ERR_CAPACITY;
-    const uint64_t m = (uint64_t)mm;
+    const u128 m = (u128)mm;
     // masked (query, key) pairs: history row i sees m+i+1 keys, a candidate m+n keys + itself
-    const uint64_t pairs = n * m + n * (n + 1) / 2 + c * (m + n + 1);
+    const u128 pairs = n * m + n * (n + 1) / 2 + c * (m + n + 1);
     alg += L * (14 * (n + c) * D * D + 4 * D * pairs);
-    const uint64_t N = m + n;
+    const u128 N = m + n;
     form += 2 * L * (N * N * D / 2 + N * D * D * 4 + N * D * D * 3);
+    if (alg > lim || form > lim) return HSTU_ERR_SHAPE;
   }
-  if (algorithmic_flops) *algorithmic_flops = alg;
-  if (formula_flops) *formula_flops = form;
+  if (algorithmic_flops) *algorithmic_flops = (uint64_t)alg;
+  if (formula_flops) *formula_flops = (uint64_t)form;
   return HSTU_OK;
 }
 

@@ -185,7 +185,10 @@ hstu_status hstu_workspace_size(const hstu_dims* d, int32_t B, const int32_t* ui
  *    itself). Per layer and user: 14*(n+c)*D^2 + 4*D*(n*m + n(n+1)/2 + c*(m+n+1)).
  *  formula_flops: the benchmark page's expression
  *    2*layers*(N*N*D/2 + N*D*D*4 + N*D*D*3) with N = m+n, summed over users.
- * cached_len may be NULL (all m = 0). Either output pointer may be NULL. */
+ * cached_len may be NULL (all m = 0). Either output pointer may be NULL.
+ * Errors: those of hstu_workspace_size's arguments, HSTU_ERR_CAPACITY for a negative
+ * cached_len, HSTU_ERR_SHAPE when either count exceeds 2^64 - 1 (possible only for
+ * batches hstu_encode would refuse: it bounds every user by max_len). */
 hstu_status hstu_flops(const hstu_dims* d, int32_t B, const int32_t* uih_offsets,
                        const int32_t* cand_offsets, const int32_t* cached_len,
                        uint64_t* algorithmic_flops, uint64_t* formula_flops);

@@ -118,6 +118,46 @@ def test_flops_equal_oracle_counter(uih, cand, cached):
     assert form == sum(2 * L * ((m + n) ** 2 * D // 2 + (m + n) * D * D * 7) for n, m in zip(uih, ms))
 
 
+def test_flops_near_and_past_the_64_bit_limit():
+    """Counts for batches far beyond any max_len: exact while they fit 64 bits (against
+    Python's integers, the documented per-user formula), HSTU_ERR_SHAPE once either passes
+    2^64 - 1, never a wrapped value."""
+    def exact(L, D, users):
+        alg = form = 0
+        for n, c, m in users:
+            pairs = n * m + n * (n + 1) // 2 + c * (m + n + 1)
+            alg += L * (14 * (n + c) * D * D + 4 * D * pairs)
+            form += 2 * L * ((m + n) ** 2 * D // 2 + (m + n) * D * D * 7)
+        return alg, form
+
+    D = 127 * 128                                                  # the widest model the checks allow
+    cases = [
+        (1, [(2 ** 20, 0, 0)]),                                    # about 2^55
+        (16, [(2 ** 20, 3, 2 ** 20)]),                             # about 2^61
+        (1024, [(2 ** 20, 3, 2 ** 20)]),                           # about 2^67
+        (1, [(2 ** 30, 0, 0)]),                                    # 4 D n^2 / 2 is about 2^75
+        (2 ** 31 - 1, [(1, 0, 0)] * 2),                            # about 2^63.8
+        (2 ** 31 - 1, [(1, 0, 0)] * 3),                            # the third user passes 2^64
+        (2 ** 31 - 1, [(2 ** 31 - 1, 2 ** 31 - 1, 2 ** 31 - 1)]),  # the largest user possible: about 2^111
+    ]
+    seen = set()
+    for L, users in cases:
+        uo, co = [0], [0]
+        for n, c, _ in users:
+            uo.append(uo[-1] + n)
+            co.append(co[-1] + c)
+        st, alg, form = hsa.hstu_flops(hsa.HstuDims(L, D, 127, 1, hsa.HSTU_BF16), len(users), uo, co,
+                                       [m for _, _, m in users])
+        want_alg, want_form = exact(L, D, users)
+        fits = want_alg < 2 ** 64 and want_form < 2 ** 64
+        seen.add(fits)
+        if fits:
+            assert st == OK and (alg, form) == (want_alg, want_form)
+        else:
+            assert st == ERR_SHAPE
+    assert seen == {True, False}
+
+
 @pytest.mark.parametrize("name", ["d256_uih1k_c64", "d512_uih2k_c2k", "stream_3000p300_c2k", "long_uih16k_c2k"])
 def test_flops_of_workloads_equal_enumeration(name):
     spec = workloads.WORKLOADS[name]
