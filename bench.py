@@ -250,6 +250,9 @@ def main():
                     help="workloads with a cached prefix: keep it in a paged cache of 64-row pages instead "
                          "of one slot per user, the page ids a random permutation of the pool (shuffled) "
                          "or each user's pages consecutive (ordered)")
+    ap.add_argument("--weight-layout", choices=("prepared", "math"), default="prepared",
+                    help="weights as the GEMMs read them (prepared once per model) or in the method's "
+                         "layout W1 [D][4D], W2 [3D][D], transposed by every call into its workspace")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (to scale the HBM "
                          "byte counters of a profiler run) and exit")
@@ -284,7 +287,7 @@ def main():
         print("bench.py times the bf16 workloads (a cached prefix only with plain tokens)", file=sys.stderr)
         sys.exit(1)
     model = hsa.Model(wl.params, d_model=wl.d_model, heads=wl.heads, max_len=wl.max_len,
-                      dtype=wl.dtype, device=dev)
+                      dtype=wl.dtype, device=dev, weight_layout=args.weight_layout)
     bf = lambda a: torch.from_numpy(a).to(device=dev, dtype=torch.bfloat16)
     cand = bf(wl.cand)
     eo = workloads.lengths_to_offsets(wl.uih_lengths)
@@ -422,6 +425,7 @@ def main():
                 "N(0,0.02) position bias)" + ("" if wl.packing == "none" else
                                               "; N(0,1) context and action embeddings per event"),
         "config": {"workload": args.workload, "users": wl.users, "layers": wl.layers,
+                   **({"weight_layout": "math"} if args.weight_layout == "math" else {}),
                    **({"cached_per_user": int(wl.cached_lengths[0]),
                        "cache_layout": f"paged (64-row pages, {args.paged} ids)" if args.paged else "slot"}
                     if cache is not None else {}),

@@ -18,7 +18,7 @@ from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
 
-__all__ = ["HSTU_F32", "HSTU_BF16", "HstuError", "load_library", "library_path",
+__all__ = ["HSTU_F32", "HSTU_BF16", "HSTU_WEIGHTS_PREPARED", "HSTU_WEIGHTS_MATH", "ABI_VERSION", "HstuError", "load_library", "library_path",
            "hstu_abi_version", "hstu_status_string", "hstu_workspace_size", "hstu_flops", "hstu_attention_plan",
            "hstu_encode", "hstu_encode_static", "encode_static", "HSTU_ERR_TOO_LARGE", "hstu_pack_uih",
            "hstu_transpose_weights", "transpose_weights", "hstu_timing_enable", "hstu_timing_select",
@@ -27,6 +27,8 @@ __all__ = ["HSTU_F32", "HSTU_BF16", "HstuError", "load_library", "library_path",
            "PagedKVCache", "POOL_STATS", "PAGE_ROWS"]
 
 HSTU_F32, HSTU_BF16 = 0, 1
+HSTU_WEIGHTS_PREPARED, HSTU_WEIGHTS_MATH = 0, 1
+ABI_VERSION = 9          # the HSTU_ABI_VERSION these structures follow
 HSTU_OK = 0
 HSTU_ERR_TOO_LARGE = 8
 KERNEL_KINDS = ("plan", "uvqk", "attention", "out", "norm", "pack", "score")
@@ -37,7 +39,7 @@ PAGE_ROWS = 64
 
 class HstuDims(ctypes.Structure):
     _fields_ = [("layers", ctypes.c_int32), ("d_model", ctypes.c_int32), ("heads", ctypes.c_int32),
-                ("max_len", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("max_len", ctypes.c_int32), ("dtype", ctypes.c_int32), ("weight_layout", ctypes.c_int32)]
 
 
 class HstuLayerWeights(ctypes.Structure):
@@ -84,6 +86,9 @@ def load_library() -> ctypes.CDLL:
     i32p = P(ctypes.c_int32)
     lib.hstu_abi_version.restype = ctypes.c_int32
     lib.hstu_abi_version.argtypes = []
+    if lib.hstu_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{path} has ABI version {lib.hstu_abi_version()}, this binding follows {ABI_VERSION}: "
+                           "rebuild the library (__graft_entry__.build())")
     lib.hstu_status_string.restype = ctypes.c_char_p
     lib.hstu_status_string.argtypes = [ctypes.c_int32]
     lib.hstu_workspace_size.restype = ctypes.c_int32
@@ -144,8 +149,8 @@ def _i32(a) -> Tuple[np.ndarray, ctypes.POINTER(ctypes.c_int32)]:
     return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
 
 
-def _dims(layers, d_model, heads, max_len, dtype) -> HstuDims:
-    return HstuDims(layers, d_model, heads, max_len, dtype)
+def _dims(layers, d_model, heads, max_len, dtype, weight_layout=HSTU_WEIGHTS_PREPARED) -> HstuDims:
+    return HstuDims(layers, d_model, heads, max_len, dtype, weight_layout)
 
 
 def hstu_abi_version() -> int:
@@ -267,25 +272,33 @@ class Model:
 
     ``params``: per layer objects with ``w1`` [D,4D], ``w2`` [3D,D], ``pos`` [max_len,3D] or
     None and optionally ``rel`` [heads,max_len] or None (math layout, float32 numpy
-    arrays); the weights are stored transposed as [out][in].
+    arrays). ``weight_layout`` "prepared" stores the weights transposed as [out][in], the
+    layout the GEMMs read; "math" stores W1 and W2 as given, and every encode call then
+    transposes them into its workspace (HSTU_WEIGHTS_MATH).
     """
 
-    def __init__(self, params, *, d_model: int, heads: int, max_len: int, dtype: str, device="cuda"):
+    def __init__(self, params, *, d_model: int, heads: int, max_len: int, dtype: str, device="cuda",
+                 weight_layout: str = "prepared"):
         torch = _torch()
         self.d_model, self.heads, self.max_len = d_model, heads, max_len
         self.dtype_code = HSTU_BF16 if dtype == "bf16" else HSTU_F32
+        if weight_layout not in ("prepared", "math"):
+            raise ValueError(f"weight_layout must be 'prepared' or 'math', not {weight_layout!r}")
+        self.weight_layout = HSTU_WEIGHTS_MATH if weight_layout == "math" else HSTU_WEIGHTS_PREPARED
+        math = self.weight_layout == HSTU_WEIGHTS_MATH
         self.torch_dtype = torch.bfloat16 if dtype == "bf16" else torch.float32
         self.layers: List[Tuple] = []
         dev = lambda a: (None if a is None else
                          torch.from_numpy(np.ascontiguousarray(a)).to(device=device, dtype=self.torch_dtype).contiguous())
         ptr = lambda t: None if t is None else t.data_ptr()
         for p in params:
-            self.layers.append((dev(p.w1.T), dev(p.w2.T), dev(p.pos), dev(getattr(p, "rel", None))))
+            self.layers.append((dev(p.w1 if math else p.w1.T), dev(p.w2 if math else p.w2.T), dev(p.pos),
+                                dev(getattr(p, "rel", None))))
         self.weights = [HstuLayerWeights(ptr(a), ptr(b), ptr(c), ptr(r)) for a, b, c, r in self.layers]
 
     def dims(self, layers: Optional[int] = None) -> HstuDims:
         return _dims(len(self.layers) if layers is None else layers, self.d_model, self.heads,
-                     self.max_len, self.dtype_code)
+                     self.max_len, self.dtype_code, self.weight_layout)
 
 
 class KVCache:

@@ -29,6 +29,7 @@ hstu_status check_dims(const hstu_dims* d) {
   if (!d) return HSTU_ERR_NULL;
   if (d->layers < 1 || d->d_model <= 0 || d->heads <= 0 || d->max_len < 1) return HSTU_ERR_SHAPE;
   if (d->heads > 127) return HSTU_ERR_SHAPE;   // the planner's item codes hold a head in 7 bits
+  if (d->weight_layout != HSTU_WEIGHTS_PREPARED && d->weight_layout != HSTU_WEIGHTS_MATH) return HSTU_ERR_SHAPE;
   if (d->d_model % d->heads) return HSTU_ERR_SHAPE;
   // a position table holds fewer than 2^31 elements (the kernels index it in 32 bits)
   if ((int64_t)d->max_len * 3 * d->d_model >= ((int64_t)1 << 31)) return HSTU_ERR_SHAPE;
@@ -61,7 +62,7 @@ struct Layout {
   int32_t B = 0, Nu = 0, Nc = 0, T = 0;
   int64_t ntiles = 0, groups = 0;
   size_t users = 0, wptr = 0, codes = 0, items = 0, rows = 0, xn = 0, cs = 0, st = 0, vqk = 0, aout = 0, x = 0,
-         total = 0;
+         wt = 0, total = 0;
   size_t staged = 0;  // host-planned part: users table, W1 pointers, item codes (sent up to the grid)
 };
 
@@ -99,6 +100,9 @@ Layout make_layout(const hstu_dims* d, int32_t B, const int32_t* uo, const int32
   L.vqk = off; off += align_up(Tp * 3 * D * es);
   L.aout = off; off += align_up(Tp * 3 * D * es);
   L.x = off; off += d->layers > 1 ? align_up(T * D * es) : 0;
+  // weights given in the math layout: each layer's W1 [D][4D] and W2 [3D][D], transposed
+  // into [4D][D] and [D][3D] at the start of the call
+  L.wt = off; off += d->weight_layout == HSTU_WEIGHTS_MATH ? align_up((size_t)d->layers * 7 * D * D * es) : 0;
   L.total = L.T == 0 ? 0 : off;
   return L;
 }
@@ -390,8 +394,18 @@ hstu_status run_encode(const EncodeCall& c, const PlanSpace& ps, char* ws, hipSt
     u.key_row = !kv ? u.uoff : paged ? b * kv->pages_per_user : kv->slot_of_user[b] * kv->capacity;
     u.pad0 = u.pad1 = 0;
   }
+  // the layers' W1 [4D][D] and W2 [D][3D] as the GEMMs read them: the caller's, or their
+  // transposes in the workspace (math layout)
+  const size_t esz = d->dtype == HSTU_F32 ? 4 : 2;
+  const bool math = d->weight_layout == HSTU_WEIGHTS_MATH;
+  auto w1 = [&](int32_t l) -> const void* {
+    return math ? ws + lay.wt + (size_t)l * 7 * D * D * esz : c.w[l].w_uvqk;
+  };
+  auto w2 = [&](int32_t l) -> const void* {
+    return math ? ws + lay.wt + ((size_t)l * 7 + 4) * D * D * esz : c.w[l].w_out;
+  };
   const void** wptr = reinterpret_cast<const void**>(ps.image + lay.wptr);
-  for (int32_t l = 0; l < L; ++l) wptr[l] = c.w[l].w_uvqk;
+  for (int32_t l = 0; l < L; ++l) wptr[l] = w1(l);
   hstu::ItemCode* codes = reinterpret_cast<hstu::ItemCode*>(ps.image + lay.codes);
   const int attn_grid = plan_attention(users, B, d->heads, bm, ps.groups, ps.items, codes);
 
@@ -417,6 +431,25 @@ hstu_status run_encode(const EncodeCall& c, const PlanSpace& ps, char* ws, hipSt
   if (timed_launch(HSTU_KERNEL_PLAN, s, [&] { return hstu::launch_plan(pa, s); }) != hipSuccess)
     return HSTU_ERR_HIP;
 
+  // math layout: every layer's W1 [D][4D] and W2 [3D][D] transposed into the workspace,
+  // up to kTransposeList layers a launch
+  for (int32_t l0 = 0; math && l0 < L; l0 += hstu::kTransposeList) {
+    hstu::TransposeList t1{}, t2{};
+    t1.count = t2.count = std::min(L - l0, hstu::kTransposeList);
+    t1.rows = D, t1.cols = 4 * D;
+    t2.rows = 3 * D, t2.cols = D;
+    for (int32_t i = 0; i < t1.count; ++i) {
+      t1.src[i] = c.w[l0 + i].w_uvqk;
+      t1.dst[i] = const_cast<void*>(w1(l0 + i));
+      t2.src[i] = c.w[l0 + i].w_out;
+      t2.dst[i] = const_cast<void*>(w2(l0 + i));
+    }
+    if (timed_launch(HSTU_KERNEL_NORM, s, [&] {
+          const hipError_t e = hstu::launch_transpose_list((int)esz, t1, s);
+          return e != hipSuccess ? e : hstu::launch_transpose_list((int)esz, t2, s);
+        }) != hipSuccess)
+      return HSTU_ERR_HIP;
+  }
   if (d->dtype != HSTU_F32) {
     hstu::ColsumArgs ca{reinterpret_cast<const void* const*>(ws + lay.wptr), L, D, cs};
     if (timed_launch(HSTU_KERNEL_NORM, s, [&] { return hstu::launch_colsum(ca, s); }) != hipSuccess)
@@ -442,7 +475,7 @@ hstu_status run_encode(const EncodeCall& c, const PlanSpace& ps, char* ws, hipSt
       if (timed_launch(HSTU_KERNEL_NORM, s, [&] { return hstu::launch_norm(d->dtype, na, s); }) != hipSuccess)
         return HSTU_ERR_HIP;
     }
-    hstu::UvqkArgs ua{xn, x_lo, x_hi, cs + (size_t)l * 4 * D, rstat, lay.Nu, lay.T, D, c.w[l].w_uvqk,
+    hstu::UvqkArgs ua{xn, x_lo, x_hi, cs + (size_t)l * 4 * D, rstat, lay.Nu, lay.T, D, w1(l),
                       c.w[l].pos_bias, d_rows, d_users, vqk, aout, ck, cv, pages, npages};
     if (timed_launch(HSTU_KERNEL_UVQK, s, [&] { return hstu::launch_uvqk(d->dtype, ua, s); }) != hipSuccess)
       return HSTU_ERR_HIP;
@@ -472,7 +505,7 @@ hstu_status run_encode(const EncodeCall& c, const PlanSpace& ps, char* ws, hipSt
       return HSTU_ERR_HIP;
 
     // the output GEMM also leaves the next layer's row statistics (bfloat16 path)
-    hstu::OutArgs oa{aout, c.w[l].w_out, x_lo, x_hi, y_lo, y_hi,
+    hstu::OutArgs oa{aout, w2(l), x_lo, x_hi, y_lo, y_hi,
                      d->dtype == HSTU_F32 || l == L - 1 ? nullptr : rstat, lay.Nu, lay.T, D};
     if (timed_launch(HSTU_KERNEL_OUT, s, [&] { return hstu::launch_out(d->dtype, oa, s); }) != hipSuccess)
       return HSTU_ERR_HIP;

@@ -185,6 +185,15 @@ hipError_t launch_uvqk(int dtype, const UvqkArgs& a, hipStream_t s);
 // grid = kXcds * (longest bin)
 hipError_t launch_attn(int dtype, int dh, const AttnArgs& a, int grid, hipStream_t s);
 hipError_t launch_transpose(int esize, const void* src, void* dst, int rows, int cols, hipStream_t s);
+// Up to kTransposeList matrices of one shape [rows][cols], each to its own destination
+// [cols][rows], in one launch.
+constexpr int kTransposeList = 16;
+struct TransposeList {
+  const void* src[kTransposeList];
+  void* dst[kTransposeList];
+  int32_t rows, cols, count;
+};
+hipError_t launch_transpose_list(int esize, const TransposeList& t, hipStream_t s);
 hipError_t launch_out(int dtype, const OutArgs& a, hipStream_t s);
 
 }  // namespace hstu

@@ -58,10 +58,14 @@ __global__ __launch_bounds__(kPackThreads) void pack_sum_f32_kernel(
 
 // dst[c][r] = src[r][c] on 64 x 64 tiles through LDS (rows padded by one element), so
 // both the reads of src rows and the writes of dst rows are consecutive per wave.
-// Elements are moved as bits. Block (bx, by) owns source rows 64 by.. and columns 64 bx..
+// Elements are moved as bits. Block (bx, by, z) owns rows 64 by.. and columns 64 bx..
+// of matrix z of the list: one launch moves every matrix of a list (a model's layers),
+// which keeps enough workgroups in flight to hide the memory latency.
 template <typename T>
-__global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ src, T* __restrict__ dst, int rows,
-                                                        int cols) {
+__global__ __launch_bounds__(256) void transpose_kernel(TransposeList t) {
+  const T* __restrict__ src = static_cast<const T*>(t.src[blockIdx.z]);
+  T* __restrict__ dst = static_cast<T*>(t.dst[blockIdx.z]);
+  const int rows = t.rows, cols = t.cols;
   __shared__ T tile[64][65];
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
@@ -80,15 +84,26 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ sr
 
 }  // namespace
 
-// rows * cols < 2^31 and both > 0 (checked by the caller); esize 2 or 4.
-hipError_t launch_transpose(int esize, const void* src, void* dst, int rows, int cols, hipStream_t s) {
-  const dim3 grid((cols + 63) / 64, (rows + 63) / 64);
-  if (grid.y > 65535) return hipErrorInvalidValue;
+// rows * cols < 2^31 and both > 0 (checked by the caller); esize 2 or 4; 1 <= count <=
+// kTransposeList.
+hipError_t launch_transpose_list(int esize, const TransposeList& t, hipStream_t s) {
+  const dim3 grid((t.cols + 63) / 64, (t.rows + 63) / 64, t.count);
+  if (grid.y > 65535 || t.count < 1 || t.count > kTransposeList) return hipErrorInvalidValue;
   if (esize == 2)
-    transpose_kernel<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)src, (uint16_t*)dst, rows, cols);
+    transpose_kernel<uint16_t><<<grid, 256, 0, s>>>(t);
   else
-    transpose_kernel<uint32_t><<<grid, 256, 0, s>>>((const uint32_t*)src, (uint32_t*)dst, rows, cols);
+    transpose_kernel<uint32_t><<<grid, 256, 0, s>>>(t);
   return hipGetLastError();
+}
+
+hipError_t launch_transpose(int esize, const void* src, void* dst, int rows, int cols, hipStream_t s) {
+  TransposeList t{};
+  t.src[0] = src;
+  t.dst[0] = dst;
+  t.rows = rows;
+  t.cols = cols;
+  t.count = 1;
+  return launch_transpose_list(esize, t, s);
 }
 
 // `chunks` counts 16-byte chunks of the output (< 2^31, checked by the caller).

@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 8
+#define HSTU_ABI_VERSION 9
 
 /* Element type of every device tensor of a call. */
 enum hstu_dtype { HSTU_F32 = 0, HSTU_BF16 = 1 };
@@ -100,21 +100,39 @@ typedef int32_t hstu_status;
  *           (history positions 0..m+n-1 plus the candidate slot m+n). The attention
  *           scale is 1/max_len. A table has fewer than 2^31 elements:
  *           max_len * 3 * D < 2^31.
- *  dtype    enum hstu_dtype. */
+ *  dtype    enum hstu_dtype.
+ *  weight_layout  enum hstu_weight_layout: how hstu_encode and hstu_encode_static
+ *           read w_uvqk and w_out (hstu_layer_weights); every entry point that takes
+ *           dims rejects other values with HSTU_ERR_SHAPE. */
 typedef struct hstu_dims {
   int32_t layers;
   int32_t d_model;
   int32_t heads;
   int32_t max_len;
   int32_t dtype;
+  int32_t weight_layout;
 } hstu_dims;
 
+/* Layout of the two weight matrices of a layer.
+ *  HSTU_WEIGHTS_PREPARED  w_uvqk [4D][D], w_out [D][3D]: each output feature's weights
+ *                         in one row, as the GEMMs read them (hstu_transpose_weights
+ *                         makes them from the other layout once per model).
+ *  HSTU_WEIGHTS_MATH      w_uvqk [D][4D] (W1, column blocks U, V, Q, K) and w_out
+ *                         [3D][D] (W2, row blocks U, O, U*O), as the projection X W1 and
+ *                         the output GEMM [U | O | U*O] W2 are written. Each call then
+ *                         transposes both into its workspace first (7 D^2 elements a
+ *                         layer, counted in hstu_workspace_size; two launches for up to
+ *                         16 layers): 29 MB and about 40 us a call at D = 512 and 8
+ *                         layers, 1% of that call. */
+typedef enum hstu_weight_layout { HSTU_WEIGHTS_PREPARED = 0, HSTU_WEIGHTS_MATH = 1 } hstu_weight_layout;
+
 /* One layer's parameters: device pointers, row-major, in the call's dtype.
- *  w_uvqk   [4D][D]: output feature j of the projection in row j (the transpose of
- *           the math-layout W1 [D][4D]); row blocks U, V, Q, K.
- *  w_out    [D][3D]: output feature j of the output GEMM in row j (the transpose of
- *           W2 [3D][D]); column blocks U, O, U*O. hstu_transpose_weights makes both
- *           from the math layout.
+ *  w_uvqk   HSTU_WEIGHTS_PREPARED: [4D][D], output feature j of the projection in row j
+ *           (the transpose of W1 [D][4D]); row blocks U, V, Q, K.
+ *           HSTU_WEIGHTS_MATH: W1 itself, [D][4D].
+ *  w_out    HSTU_WEIGHTS_PREPARED: [D][3D], output feature j of the output GEMM in row
+ *           j (the transpose of W2 [3D][D]); column blocks U, O, U*O.
+ *           HSTU_WEIGHTS_MATH: W2 itself, [3D][D].
  *  pos_bias [max_len][3D]: row p is the absolute bias of position p, added to V, Q, K
  *           after the SiLU (column blocks V, Q, K); NULL: no absolute bias.
  *  rel_bias [H][max_len]: rel_bias[h][d] is added to every attention weight

@@ -46,8 +46,8 @@ def test_status_strings():
     assert hsa.hstu_status_string(99) == "unknown status"
 
 
-def dims(L=2, D=256, H=4, max_len=64, dtype=hsa.HSTU_BF16):
-    return hsa.HstuDims(L, D, H, max_len, dtype)
+def dims(L=2, D=256, H=4, max_len=64, dtype=hsa.HSTU_BF16, weight_layout=hsa.HSTU_WEIGHTS_PREPARED):
+    return hsa.HstuDims(L, D, H, max_len, dtype, weight_layout)
 
 
 @pytest.mark.parametrize("d,want", [
@@ -64,6 +64,9 @@ def dims(L=2, D=256, H=4, max_len=64, dtype=hsa.HSTU_BF16):
     (dims(D=64, H=2, dtype=hsa.HSTU_F32), OK),   # fp32, dh = 32
     (dims(D=96, H=3, dtype=hsa.HSTU_F32), ERR_SHAPE),
     (dims(D=512, H=2, dtype=hsa.HSTU_F32), ERR_SHAPE),   # dh = 256
+    (dims(weight_layout=hsa.HSTU_WEIGHTS_MATH), OK),
+    (dims(weight_layout=2), ERR_SHAPE),
+    (dims(weight_layout=-1), ERR_SHAPE),
 ])
 def test_workspace_size_dims(d, want):
     st, _ = hsa.hstu_workspace_size(d, 1, [0, 5], [0, 3])
@@ -84,6 +87,23 @@ def test_workspace_size_offsets_and_growth():
     # at least the [T][4D] projection, [T][D] attention output and [T][D] layer buffer
     T = 603
     assert big >= T * 6 * 256 * 2
+
+
+@pytest.mark.parametrize("dtype,D,L", [(hsa.HSTU_BF16, 256, 2), (hsa.HSTU_BF16, 512, 8), (hsa.HSTU_F32, 192, 3)])
+def test_workspace_size_math_layout_adds_the_transposed_weights(dtype, D, L):
+    """With weights in the math layout the workspace also holds every layer's W1 and W2
+    transposed: 7 D^2 elements a layer (a multiple of the 256-byte alignment here)."""
+    es = 2 if dtype == hsa.HSTU_BF16 else 4
+    H = D // 64
+    _, prep = hsa.hstu_workspace_size(dims(L, D, H, 64, dtype), 2, [0, 5, 9], [0, 3, 3])
+    _, math = hsa.hstu_workspace_size(dims(L, D, H, 64, dtype, hsa.HSTU_WEIGHTS_MATH), 2, [0, 5, 9], [0, 3, 3])
+    assert math - prep == L * 7 * D * D * es
+    # nothing to encode: no workspace in either layout
+    assert hsa.hstu_workspace_size(dims(L, D, H, 64, dtype, hsa.HSTU_WEIGHTS_MATH), 1, [0, 0], [0, 0]) == (OK, 0)
+
+
+def test_binding_and_library_abi_versions_agree():
+    assert hsa.hstu_abi_version() == hsa.ABI_VERSION
 
 
 def test_workspace_size_page_offsets_example():
