@@ -1,7 +1,7 @@
 """GPU parity over seeded random configurations, beside the hand-picked cases: dtype, head
 width (32, 64, 128) and count, 1-6 users with ragged lengths and empty users, no cache, a
 slot cache or a paged cache (shuffled page ids) with cached prefixes, absolute, relative
-or both position biases, one or two layers; the wide draw goes to 8 users, histories of
+or both position biases, one or two layers, weights prepared or in the method's layout; the wide draw goes to 8 users, histories of
 up to 900 new and 600 cached rows, 400 candidates, 3 or 6 heads and D up to 768. Each
 case fills the cache with the prefixes (no candidates), then encodes the new events and
 candidates; every user's outputs are held to the oracle's bar (bf16 mirror or float64),
@@ -14,7 +14,7 @@ import pytest
 
 import hstu_silu_attention_amd as hsa
 import workloads
-from gpu_util import BF16_TOL, F32_TOL, gpu_encode, make_model, normwise_per_user, oracle_encode, say, torch_cuda
+from gpu_util import BF16_TOL, F32_TOL, gpu_encode, normwise_per_user, oracle_encode, say, torch_cuda
 
 pytestmark = pytest.mark.gpu
 
@@ -41,8 +41,9 @@ def draw(seed):
     position = str(rng.choice(["absolute", "relative", "both"]))
     layers = int(rng.integers(1, 3))
     max_len = int((cached + uih).max()) + 1 + int(rng.integers(0, 100))   # every candidate position fits
+    weights = "math" if rng.random() < 0.3 else "prepared"
     return dict(dtype=dtype, D=dh * H, H=H, B=B, uih=uih, cand=cand, cache=cache, cached=cached,
-                position=position, layers=layers, max_len=max_len)
+                position=position, layers=layers, max_len=max_len, weights=weights)
 
 
 def draw_wide(seed):
@@ -60,8 +61,9 @@ def draw_wide(seed):
     position = str(rng.choice(["absolute", "relative", "both"]))
     layers = int(rng.integers(1, 3))
     max_len = int((cached + uih).max()) + 1 + int(rng.integers(0, 300))
+    weights = "math" if rng.random() < 0.3 else "prepared"
     return dict(dtype=dtype, D=dh * H, H=H, B=B, uih=uih, cand=cand, cache=cache, cached=cached,
-                position=position, layers=layers, max_len=max_len)
+                position=position, layers=layers, max_len=max_len, weights=weights)
 
 
 def draw_large(seed):
@@ -75,8 +77,9 @@ def draw_large(seed):
     cached = np.zeros(B, np.int64) if cache == "none" else np.where(rng.random(B) < 0.3, 0, rng.integers(1, 1500, B))
     position = str(rng.choice(["absolute", "relative", "both"]))
     max_len = int((cached + uih).max()) + 1 + int(rng.integers(0, 300))
+    weights = "math" if rng.random() < 0.3 else "prepared"
     return dict(dtype="bf16", D=D, H=D // dh, B=B, uih=uih, cand=cand, cache=cache, cached=cached,
-                position=position, layers=1, max_len=max_len)
+                position=position, layers=1, max_len=max_len, weights=weights)
 
 
 @pytest.mark.parametrize("seed", SEEDS)
@@ -97,12 +100,14 @@ def test_random_large_configuration(seed):
 def run_configuration(seed, c):
     torch = torch_cuda()
     say(f"  seed {seed}: {c['dtype']} D={c['D']} H={c['H']} B={c['B']} layers={c['layers']} cache={c['cache']} "
+        f"weights={c.get('weights', 'prepared')} "
         f"{c['position']} uih={c['uih'].tolist()} cand={c['cand'].tolist()} cached={c['cached'].tolist()}")
     wl = workloads.make_custom(seed=seed, dtype=c["dtype"], layers=c["layers"], d_model=c["D"], heads=c["H"],
                                max_len=c["max_len"], uih_lengths=c["uih"], cand_lengths=c["cand"],
                                cached_lengths=c["cached"], position=c["position"], rel_std=0.3)
     B, D, L = wl.users, wl.d_model, wl.layers
-    model = make_model(torch, wl)
+    model = hsa.Model(wl.params, d_model=wl.d_model, heads=wl.heads, max_len=wl.max_len, dtype=wl.dtype,
+                      weight_layout=c.get("weights", "prepared"))
     total = wl.cached_lengths + wl.uih_lengths
     cap = max(int(total.max()), 1)
     empty = np.zeros((0, D), np.float32)
