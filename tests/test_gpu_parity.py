@@ -53,6 +53,19 @@ def test_bf16_ragged(D, H):
         f"cand={normwise_per_user(gc, fc, wl.cand_lengths):.3e}")
 
 
+@pytest.mark.parametrize("dtype,D,H", [("bf16", 4096, 32), ("bf16", 8192, 64), ("f32", 8128, 127)])
+def test_widest_models(dtype, D, H):
+    """Wide models, one layer: D = 4096 and 8192 in bfloat16 (32 and 64 heads of 128; the
+    projection's N = 4D = 32768 columns, the row statistics of 64 column groups) and the
+    most heads the planner takes, 127 heads of 64 in float32 (D = 8128), with both biases,
+    ragged users and an empty one."""
+    wl = workloads.make_custom(seed=5000 + H, dtype=dtype, layers=1, d_model=D, heads=H, max_len=200,
+                               uih_lengths=[70, 0, 129], cand_lengths=[3, 9, 0], position="both")
+    gu, gc = gpu_encode(wl)
+    check(wl, gu, gc, "bf16" if dtype == "bf16" else "f64", BF16_TOL if dtype == "bf16" else F32_TOL,
+          label=f"{dtype} D={D} H={H}")
+
+
 @pytest.mark.parametrize("dtype,tol", [("bf16", BF16_TOL), ("f32", F32_TOL)])
 def test_history_fills_the_position_table(dtype, tol):
     """m + n + 1 == max_len: the candidates of the long user take the table's last row, its

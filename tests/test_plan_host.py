@@ -49,7 +49,8 @@ def expected_bins(ul, cl, ml, heads, q):
     return [[it for _, it in sorted(enumerate(bn), key=lambda t: (-t[1][0], t[0]))] for bn in bins]
 
 
-@pytest.mark.parametrize("seed,dtype,heads", [(0, "bf16", 4), (1, "bf16", 8), (2, "f32", 2), (3, "bf16", 1)])
+@pytest.mark.parametrize("seed,dtype,heads", [(0, "bf16", 4), (1, "bf16", 8), (2, "f32", 2), (3, "bf16", 1),
+                                              (4, "bf16", 127)])   # the most heads an item code holds
 def test_plan_matches_the_documented_rule(seed, dtype, heads):
     rng = np.random.default_rng(seed)
     B = int(rng.integers(1, 24))
