@@ -105,16 +105,18 @@ __device__ __forceinline__ float silu_bias(float x, float nlog2e, float bias) {
   return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(__builtin_fmaf(x, nlog2e, bias)));
 }
 
-// Relative bias (REL): each weight gains rel[h][pos_i - pos_j] after its SiLU. The table is
-// read from the 16-byte-aligned address at or before the head's row (mis entries early).
-// LDS holds a static part, kTabPad zero entries and then the row's first entries (entry d
-// at tab[kTabPad + mis + d], for the diagonal pass and a candidate's own key), and per wave
-// a ring of three slices of kSlice entries: for key block b a wave's weights only need
-// the 96 consecutive entries d in [q - 64b - 63, q + 31 - 64b] (q: the wave's first query
-// position), and the slice of block b + 2 is loaded beside K(b + 2), into the slot of
-// block b - 1. A lane reads its 16 weights' entries there; wholly masked halves read the
-// zero pad instead, so every step stays branch-free. Any max_len works.
-constexpr int kTabPad = 64, kSlice = 512, kRing = 3, kTabStatic = kTabPad + kSlice;
+// Relative bias (REL): each weight gains rel[h][pos_i - pos_j] after its SiLU. The kernel
+// reads a float32 copy of the layer's table (widened before the launch, so the entries
+// add to the float32 weights with no conversion), from the 16-byte-aligned address at or
+// before the head's row (mis entries early). LDS holds a static part, kTabPad zero
+// entries and then the row's first entries (entry d at tab[kTabPad + mis + d], for the
+// diagonal pass and a candidate's own key), and per wave a ring of three slices of
+// kSlice entries: for key block b a wave's weights only need the 96 consecutive entries
+// d in [q - 64b - 63, q + 31 - 64b] (q: the wave's first query position), and the slice
+// of block b + 2 (one 64-lane load of 16 bytes a lane) is loaded beside K(b + 2), into
+// the slot of block b - 1. A lane reads its 16 weights' entries there; wholly masked
+// halves read the zero pad instead, so every step stays branch-free. Any max_len works.
+constexpr int kTabPad = 64, kSlice = 256, kRing = 3, kTabStatic = kTabPad + kSlice;
 
 // dh = 64 fits three waves per SIMD (under 168 registers; 32 KB of K/V slots, 48 KB with
 // a relative table, per workgroup), which hides more of each wave's latency; dh = 128
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(attn_waves_
 void attn_kernel(AttnArgs a) {
   using C = AttnTile<DH>;
   __shared__ __attribute__((aligned(16))) u16 ks0[C::SLOT], ks1[C::SLOT], vs0[C::SLOT], vs1[C::SLOT];
-  __shared__ __attribute__((aligned(16))) u16 tab[REL ? kTabStatic + C::WAVES * kRing * kSlice : 8];
+  __shared__ __attribute__((aligned(16))) float tab[REL ? kTabStatic + C::WAVES * kRing * kSlice : 4];
 
   const AttnItem it = a.items[blockIdx.x];
   if (it.nq <= 0) return;
@@ -198,17 +200,13 @@ void attn_kernel(AttnArgs a) {
   int mis = 0;
   i32x4 rel_src = {0, 0, 0, 0};
   if (REL) {
-    const uintptr_t hb = (uintptr_t)((const u16*)a.rel + (size_t)head * a.max_len);
+    const uintptr_t hb = (uintptr_t)((const float*)a.rel + (size_t)head * a.max_len);
     const uintptr_t ab = hb & ~(uintptr_t)15;
-    const uintptr_t end = (uintptr_t)((const u16*)a.rel + (size_t)(D / DH) * a.max_len);
-    mis = (int)((hb - ab) / 2);
-    // The range ends at the end of the table's last 16-byte chunk: a load returns zero for
-    // each 4-byte word that crosses the range's end, so a range ending at the table's
-    // last byte lost its last entry whenever H * max_len is odd. The chunk lies in the
-    // same page as the table's last byte (page boundaries are 16-byte aligned), and the
-    // bytes past the table in it stand for distances of max_len or more, which no key
-    // is at.
-    rel_src = buffer_desc((const void*)ab, (int)(((end + 15) & ~(uintptr_t)15) - ab));
+    const uintptr_t end = (uintptr_t)((const float*)a.rel + (size_t)(D / DH) * a.max_len);
+    mis = (int)((hb - ab) / 4);
+    // The range ends at the table's end: a load returns zero for each 4-byte word past
+    // it, and every entry is one whole word.
+    rel_src = buffer_desc((const void*)ab, (int)(end - ab));
   }
 
   // 64-lane LDS loads: load j of a region covers rows RPI*j.. of it; lane i brings the
@@ -290,7 +288,7 @@ void attn_kernel(AttnArgs a) {
   // slice of key block b: the 16-byte chunk of the aligned row where it starts (floor
   // division: negative chunks read as zero), and its slot in this wave's ring
   const int qfirst = cand ? key_end : wf;
-  auto slice_chunk = [&](int b) { return (mis + qfirst - 64 * b - 63) >> 3; };
+  auto slice_chunk = [&](int b) { return (mis + qfirst - 64 * b - 63) >> 2; };
   const int ring = kTabStatic + wv * kRing * kSlice;   // this wave's ring, in entries of tab
   auto slice_slot = [&](int b) { return ring + (b % kRing) * kSlice; };
   auto load_slice = [&](int b) {
@@ -304,11 +302,10 @@ void attn_kernel(AttnArgs a) {
     const int d0 = cand ? key_end - 32 * h : wf + 32 * qb - 32 * h;
     const int b = h >> 1;
     // an integer select (a pointer select became a branch): masked halves read the zero pad
-    const int at = bias(h, qb) == 0.0f ? slice_slot(b) + d0 + mis - 8 * slice_chunk(b) : 31;
-    const u16* tl = tab + at + lane_off;
+    const int at = bias(h, qb) == 0.0f ? slice_slot(b) + d0 + mis - 4 * slice_chunk(b) : 31;
+    const float* tl = tab + at + lane_off;
 #pragma unroll
-    for (int e = e0; e < e0 + 8; ++e)
-      r[e - e0] = __uint_as_float((uint32_t)tl[-(8 * (e >> 2) + (e & 3))] << 16);
+    for (int e = e0; e < e0 + 8; ++e) r[e - e0] = tl[-(8 * (e >> 2) + (e & 3))];
   };
 
   // Step h: (si, wi) = scores of half h, weights of half h - 1 -> (so, wo) = scores of
@@ -368,8 +365,8 @@ void attn_kernel(AttnArgs a) {
     load_v(vs0, 0, p0);
   }
   if (REL) {
-    if (tid < kTabPad / 8) *reinterpret_cast<uint4*>(tab + 8 * tid) = make_uint4(0, 0, 0, 0);
-    // the static part: 64 chunks = the row's first 512 - mis entries
+    if (tid < kTabPad / 4) *reinterpret_cast<uint4*>(tab + 4 * tid) = make_uint4(0, 0, 0, 0);
+    // the static part: 64 chunks = the row's first 256 - mis entries
     if (wv == 0)
       lds_load16(rel_src, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)(tab + kTabPad)), lane * 16);
     load_slice(0);
@@ -461,7 +458,7 @@ void attn_kernel(AttnArgs a) {
       const int j = 8 * (e >> 2) + 4 * hi + (e & 3);
       const bool vis = cand ? j == l32 : j <= l32;
       // relative position l32 - j on the diagonal (0 for a candidate's own key)
-      const float r = REL && vis ? __uint_as_float((uint32_t)tab[kTabPad + mis + l32 - j] << 16) : 0.0f;
+      const float r = REL && vis ? tab[kTabPad + mis + l32 - j] : 0.0f;
       const float x = silu_bias(sd[e], nlog2e, vis ? 0.0f : kInf);
       w[e >> 3][e & 7] = (__bf16)(REL ? x + r : x);
     }

@@ -62,7 +62,7 @@ struct Layout {
   int32_t B = 0, Nu = 0, Nc = 0, T = 0;
   int64_t ntiles = 0, groups = 0;
   size_t users = 0, wptr = 0, codes = 0, items = 0, rows = 0, xn = 0, cs = 0, st = 0, vqk = 0, aout = 0, x = 0,
-         wt = 0, total = 0;
+         wt = 0, relf = 0, total = 0;
   size_t staged = 0;  // host-planned part: users table, W1 pointers, item codes (sent up to the grid)
 };
 
@@ -103,6 +103,9 @@ Layout make_layout(const hstu_dims* d, int32_t B, const int32_t* uo, const int32
   // weights given in the math layout: each layer's W1 [D][4D] and W2 [3D][D], transposed
   // into [4D][D] and [D][3D] at the start of the call
   L.wt = off; off += d->weight_layout == HSTU_WEIGHTS_MATH ? align_up((size_t)d->layers * 7 * D * D * es) : 0;
+  // bfloat16 models: the current layer's relative table widened to float32 (the attention
+  // adds its entries to float32 weights; reused by every layer)
+  L.relf = off; off += d->dtype == HSTU_F32 ? 0 : align_up((size_t)d->heads * d->max_len * sizeof(float));
   L.total = L.T == 0 ? 0 : off;
   return L;
 }
@@ -499,6 +502,14 @@ hstu_status run_encode(const EncodeCall& c, const PlanSpace& ps, char* ws, hipSt
     aa.npages = npages;
     aa.aout = aout;
     aa.rel = c.w[l].rel_bias;
+    if (aa.rel && d->dtype != HSTU_F32) {
+      float* relf = reinterpret_cast<float*>(ws + lay.relf);
+      if (timed_launch(HSTU_KERNEL_NORM, s, [&] {
+            return hstu::launch_widen_bf16(c.w[l].rel_bias, relf, (int64_t)d->heads * d->max_len, s);
+          }) != hipSuccess)
+        return HSTU_ERR_HIP;
+      aa.rel = relf;
+    }
     aa.max_len = d->max_len;
     if (timed_launch(HSTU_KERNEL_ATTENTION, s,
                      [&] { return hstu::launch_attn(d->dtype, dh, aa, attn_grid, s); }) != hipSuccess)

@@ -134,7 +134,8 @@ struct AttnArgs {
   int32_t npages;        // paged cache: pages of the pool (reads outside it give zeros)
   int64_t ld;
   void* aout;            // [T_pad][3D]: writes O (float32 also reads U, writes U*O)
-  const void* rel;       // this layer's relative bias [H][max_len], or nullptr
+  const void* rel;       // this layer's relative bias [H][max_len] (float32 for both dtypes:
+                         // the bfloat16 path reads a widened copy), or nullptr
   int32_t max_len;
 };
 
@@ -185,6 +186,8 @@ hipError_t launch_uvqk(int dtype, const UvqkArgs& a, hipStream_t s);
 // grid = kXcds * (longest bin)
 hipError_t launch_attn(int dtype, int dh, const AttnArgs& a, int grid, hipStream_t s);
 hipError_t launch_transpose(int esize, const void* src, void* dst, int rows, int cols, hipStream_t s);
+// dst[i] = float(src[i]) for bfloat16 src, i < n (n < 2^31)
+hipError_t launch_widen_bf16(const void* src, float* dst, int64_t n, hipStream_t s);
 // Up to kTransposeList matrices of one shape [rows][cols], each to its own destination
 // [cols][rows], in one launch.
 constexpr int kTransposeList = 16;

@@ -82,9 +82,23 @@ __global__ __launch_bounds__(256) void transpose_kernel(TransposeList t) {
   }
 }
 
+// dst[i] = float(src[i]) for a bfloat16 src: the bits move to the upper half.
+__global__ __launch_bounds__(256) void widen_bf16_kernel(const uint16_t* __restrict__ src, float* __restrict__ dst,
+                                                         int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) dst[i] = __uint_as_float((uint32_t)src[i] << 16);
+}
+
 }  // namespace
 
-// rows * cols < 2^31 and both > 0 (checked by the caller); esize 2 or 4; 1 <= count <=
+hipError_t launch_widen_bf16(const void* src, float* dst, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (n >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  widen_bf16_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(static_cast<const uint16_t*>(src), dst, (int)n);
+  return hipGetLastError();
+}
+
+// rows * cols < 2^31 and both > 0 (checked by the caller); esize 2 or 4; 1 <=
 // kTransposeList.
 hipError_t launch_transpose_list(int esize, const TransposeList& t, hipStream_t s) {
   const dim3 grid((t.cols + 63) / 64, (t.rows + 63) / 64, t.count);

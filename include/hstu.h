@@ -139,9 +139,9 @@ typedef enum hstu_weight_layout { HSTU_WEIGHTS_PREPARED = 0, HSTU_WEIGHTS_MATH =
  *           SiLU(q_i . k_j) of head h whose relative position pos_i - pos_j is d
  *           (the original HSTU form Mask(SiLU(Q K^T) + bias) V from the DLRMv3
  *           page's "Model selection" section); NULL: no relative bias.
- * w_uvqk, w_out and any non-NULL table are 16-byte aligned. In bfloat16 a relative
- * table is read in whole 16-byte chunks, so the read can reach the end of the chunk
- * that holds its last element (the same page; those bytes are never used). */
+ * w_uvqk, w_out and any non-NULL table are 16-byte aligned. In bfloat16 each call widens
+ * a layer's relative table to float32 in its workspace (H * max_len * 4 bytes, counted in
+ * hstu_workspace_size) before that layer's attention. */
 typedef struct hstu_layer_weights {
   const void* w_uvqk;
   const void* w_out;
