@@ -49,16 +49,17 @@ def expected_bins(ul, cl, ml, heads, q):
     return [[it for _, it in sorted(enumerate(bn), key=lambda t: (-t[1][0], t[0]))] for bn in bins]
 
 
-@pytest.mark.parametrize("seed,dtype,heads", [(0, "bf16", 4), (1, "bf16", 8), (2, "f32", 2), (3, "bf16", 1),
-                                              (4, "bf16", 127)])   # the most heads an item code holds
-def test_plan_matches_the_documented_rule(seed, dtype, heads):
+@pytest.mark.parametrize("seed,dtype,heads,dh", [(0, "bf16", 4, 128), (1, "bf16", 8, 128), (2, "f32", 2, 64),
+                                                 (3, "bf16", 1, 128), (5, "bf16", 4, 64), (6, "bf16", 4, 32),
+                                                 (4, "bf16", 127, 128)])   # the most heads an item code holds
+def test_plan_matches_the_documented_rule(seed, dtype, heads, dh):
     rng = np.random.default_rng(seed)
     B = int(rng.integers(1, 24))
     ul = [int(x) for x in rng.integers(0, 1500, size=B)]
     cl = [int(x) for x in rng.integers(0, 700, size=B)]
     ml = [int(x) for x in rng.integers(0, 900, size=B)]
     ul[0], cl[0] = 0, 0                                 # an empty user
-    D = 128 * heads if dtype == "bf16" else 64 * heads
+    D = dh * heads
     d = hsa.HstuDims(2, D, heads, 4000, hsa.HSTU_BF16 if dtype == "bf16" else hsa.HSTU_F32)
     st, codes = hsa.hstu_attention_plan(d, B, workloads.lengths_to_offsets(ul), workloads.lengths_to_offsets(cl), ml)
     assert st == 0
