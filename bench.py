@@ -180,6 +180,26 @@ def cpu_baseline(wl, min_seconds: float = 10.0):
                       f"float64 with bf16-mirror rounding; {dt:.1f} s; {len(done) / dt:.4f} users/s on this host"}
 
 
+def graph_replays(torch, step, steps, alg_flops, users, warm=3):
+    """One step captured into a HIP graph (on a side stream, after the eager steps: its
+    launches, with the plan in their arguments, are recorded once), then `steps` replays
+    timed by the wall clock with a synchronize on both sides. The library records no
+    events while its timing is off, and the step has no memset or allocation to record."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(warm):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    return {"steps": steps, "ms_per_step": round(sec * 1e3, 4), "value": round(alg_flops / sec / 1e12, 3),
+            "unit": "TFLOP/s", "users_per_s": round(users / sec, 2)}
+
+
 def replay_bench(args, pages=10240, max_rows=4096, ttl=300, window=3072, batch_users=16, cand_sets=16):
     """Streaming replay: 2048 requests from 192 drawn users in time order (first visit with a
     lognormal history, then 16-128 new events per visit, 2048 candidates per request), served
@@ -253,6 +273,9 @@ def main():
     ap.add_argument("--weight-layout", choices=("prepared", "math"), default="prepared",
                     help="weights as the GEMMs read them (prepared once per model) or in the method's "
                          "layout W1 [D][4D], W2 [3D][D], transposed by every call into its workspace")
+    ap.add_argument("--graph", action="store_true",
+                    help="also capture one step into a HIP graph after the timed steps and report "
+                         "the rate of K replays of it beside the eager figures")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (to scale the HBM "
                          "byte counters of a profiler run) and exit")
@@ -323,12 +346,13 @@ def main():
     st, alg_flops, formula_flops = hsa.hstu_flops(model.dims(), wl.users, uo, co, cached if cache else None)
     assert st == 0
     alg_flops += head_flops(wl)
-    stream = torch.cuda.current_stream(dev).cuda_stream
     if wl.head:
         head = hsa.ScoringHead(wl.head, dtype=wl.dtype, device=dev)
         prob = torch.empty((int(co[-1]), head.outcomes), dtype=torch.float32, device=dev)
 
     def step():
+        # the current stream: the default one, or the capture stream of a graph
+        stream = torch.cuda.current_stream(dev).cuda_stream
         if wl.packing != "none":
             hsa.pack_uih(model, ctx, act, eo, wl.packing, out=uih, stream=stream)
         if cache is not None:
@@ -444,6 +468,8 @@ def main():
                     for k, v in kernels.items()},
         "roofline": roof,
     }
+    if args.graph:
+        result["graph"] = graph_replays(torch, step, args.steps, alg_flops, wl.users)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl)
         result["cpu_baseline"]["value"] = round(result["cpu_baseline"]["value"], 6)
